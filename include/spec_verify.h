@@ -1,0 +1,223 @@
+/*
+ * spec_verify.h -- C ABI of the MI355X (gfx950) speculative-verification kernels.
+ *
+ * Three operations make up the data-parallel hot path of one speculative
+ * decoding round:
+ *
+ *   spec_verify_attention  attention of a block of n_q query tokens (a
+ *                          gamma+1 causal chain, or an N-node candidate tree
+ *                          under an ancestor-only mask) against the full KV
+ *                          cache of every sequence;
+ *   spec_window_attention  the draft model's bounded attention: one query per
+ *                          sequence against S sink tokens plus a W-slot FIFO
+ *                          ring of the most recent tokens;
+ *   spec_sample            softmax over the vocabulary, acceptance of each
+ *                          drafted token with probability min(1, target/draft),
+ *                          and one draw from the normalised max(target-draft, 0)
+ *                          at the first rejection (or from the target row after
+ *                          the last accepted token when nothing is rejected).
+ *
+ * Conventions shared by every entry point:
+ *
+ *   Ownership   The caller allocates and frees every buffer (inputs, outputs,
+ *               workspace).  The library allocates nothing and keeps no
+ *               mutable global state; calls on different streams with
+ *               different buffers may run concurrently.
+ *   Pointers    Device pointers unless marked "host".  Tensor pointers must
+ *               be 16-byte aligned; workspaces 256-byte aligned.  All tensors
+ *               are dense, row-major, in the layouts given per argument.
+ *   Streams     All work is enqueued on `stream` (0 = the null stream); no
+ *               call synchronises the host.  Outputs are valid once the
+ *               stream reaches the end of the call.
+ *   Errors      Scalar and pointer arguments are checked on the host before
+ *               any HIP call: a bad argument returns a status and launches
+ *               nothing.  Problems that can only be seen in device-resident
+ *               data (a kv_len out of range, a bad parent entry, a token out
+ *               of the vocabulary) set bits of *dev_err (if dev_err is not
+ *               NULL) with an atomic OR; the affected sequence then gets a
+ *               defined result (zero attention output, out_count = 0) and
+ *               no memory outside the given buffers is touched.
+ *   Empty work  B == 0 returns SPEC_OK and launches nothing.
+ */
+#ifndef SPEC_VERIFY_H
+#define SPEC_VERIFY_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  SPEC_OK = 0,
+  SPEC_ERR_INVALID_ARG = 1, /* a size, count or enum is out of range */
+  SPEC_ERR_UNSUPPORTED = 2, /* a valid shape this build does not handle */
+  SPEC_ERR_BAD_TREE = 3,    /* host-side parent array is not a valid tree */
+  SPEC_ERR_MISALIGNED = 4,  /* a required pointer is NULL or misaligned */
+  SPEC_ERR_WORKSPACE = 5,   /* workspace missing or smaller than required */
+  SPEC_ERR_HIP = 6          /* a HIP launch failed (hipGetLastError) */
+} spec_status_t;
+
+typedef enum { SPEC_F32 = 0, SPEC_BF16 = 1 } spec_dtype_t;
+
+/* Bits OR-ed into *dev_err by the kernels. */
+#define SPEC_DEVERR_KV_LEN 0x1    /* kv_len[b] outside [n_q, L_cap] */
+#define SPEC_DEVERR_PARENT 0x2    /* parent[c] outside [-1, c) (sampling: a root other than 0) */
+#define SPEC_DEVERR_TOTAL_LEN 0x4 /* total_len[b] < 1 */
+#define SPEC_DEVERR_TOKEN 0x8     /* drafted token outside [0, V) */
+
+/* Largest supported query block (one 64-bit ancestor mask per node). */
+#define SPEC_MAX_NQ 64
+/* Largest supported number of nodes per sequence in spec_sample. */
+#define SPEC_MAX_SAMPLE_NODES 256
+
+/*
+ * spec_verify_attention -- verification attention of the drafted block.
+ *
+ * Defines: "Guide to MagicDec" (aifetchly blog), section 2 "Lossless Target
+ * Model Verification Across Full Context" (the target verifies the drafts with
+ * attention over the full cache); "Speculative Decoding in LLM Serving
+ * Systems" (elimelt notes), section "The algorithm", step 2 (one pass over
+ * prefix + drafts gives every drafted position its distribution) and section
+ * "Tree-based variants" (each tree token attends only to its ancestors);
+ * "Speculative Decoding & Medusa Architecture" (zyekh blog), section 4 (tree
+ * attention under a 2-D boolean mask).
+ *
+ * For sequence b, query head h and block node i:
+ *   hk = h / (Hq/Hkv);  L = kv_len[b];  p0 = L - n_q;
+ *   allowed keys: positions [0, p0) and p0 + t for every ancestor t of i
+ *   (i itself included);  out = softmax(scale * q K^T) V over the allowed
+ *   keys, lse = log(sum exp(scale * q K^T)) over the same keys (natural log).
+ *
+ *   q        [B, Hq, n_q, D]     dtype            query block (post-RoPE)
+ *   k_cache  [B, Hkv, L_cap, D]  dtype            keys; the block's own K sits at
+ *   v_cache  [B, Hkv, L_cap, D]  dtype            positions kv_len-n_q .. kv_len-1
+ *   out      [B, Hq, n_q, D]     dtype            output
+ *   lse      [B, Hq, n_q]        f32, nullable    log-sum-exp per row
+ *   kv_len   [B] int32, nullable (NULL: every sequence holds L_cap tokens)
+ *   parent   int32, nullable: NULL = chain (parent[i] = i-1); otherwise
+ *            [n_q] (parent_batch_stride 0, shared) or [B, n_q]
+ *            (parent_batch_stride n_q); parent[i] in [-1, i), -1 = root;
+ *            forests are allowed.
+ *   n_q      1 .. SPEC_MAX_NQ;  D in {64, 128};  Hq % Hkv == 0;  L_cap >= n_q.
+ *   scale    softmax scale; <= 0 selects 1/sqrt(D).
+ *   num_splits  key-range splits per (sequence, kv head); 0 = automatic.
+ *   workspace   at least spec_verify_attention_workspace(...) bytes.
+ * Returns SPEC_OK or an error status (nothing launched on error).
+ */
+spec_status_t spec_verify_attention(const void* q, const void* k_cache, const void* v_cache,
+                                    void* out, float* lse, const int32_t* kv_len,
+                                    const int32_t* parent, int32_t parent_batch_stride,
+                                    int32_t B, int32_t Hq, int32_t Hkv, int32_t n_q, int32_t D,
+                                    int32_t L_cap, spec_dtype_t dtype, float scale,
+                                    int32_t num_splits, void* workspace, size_t workspace_bytes,
+                                    int32_t* dev_err, hipStream_t stream);
+
+/* Workspace bytes spec_verify_attention needs for these sizes (0 on invalid sizes). */
+size_t spec_verify_attention_workspace(int32_t B, int32_t Hq, int32_t Hkv, int32_t n_q, int32_t D,
+                                       int32_t L_cap, spec_dtype_t dtype, int32_t num_splits);
+
+/* Split count spec_verify_attention uses when num_splits == 0 (0 on invalid sizes). */
+int32_t spec_verify_attention_auto_splits(int32_t B, int32_t Hq, int32_t Hkv, int32_t n_q,
+                                          int32_t D, int32_t L_cap, spec_dtype_t dtype);
+
+/*
+ * spec_window_attention -- bounded draft attention over sinks + a FIFO ring.
+ *
+ * Defines: "Guide to MagicDec", section 1 "Fixed-Window KV Cache Decoupling"
+ * (the draft keeps only a W-token window managed as a circular FIFO, so its
+ * attention cost is O(W) whatever the context length) and section "Best
+ * Practices", item 1 (a few dedicated slots keep the first prompt tokens as
+ * attention sinks).
+ *
+ * With T = total_len[b] tokens seen (the current one included), the keys are
+ * tokens [0, min(S,T)) (sink slot t) and tokens [max(S, T-W), T) (token t in
+ * ring slot (t-S) mod W).  One query per sequence, so no mask is applied.
+ *
+ *   q        [B, Hq, 1, D]    dtype
+ *   k_ring   [B, Hkv, W, D]   dtype   ring slots (written only by the fused append)
+ *   v_ring   [B, Hkv, W, D]   dtype
+ *   k_sink   [B, Hkv, S, D]   dtype   nullable when S == 0
+ *   v_sink   [B, Hkv, S, D]   dtype
+ *   k_new    [B, Hkv, 1, D]   dtype, nullable: K/V of token T-1; if given it is
+ *   v_new    [B, Hkv, 1, D]            written to its sink/ring slot and used
+ *                                      in this same call (fused append)
+ *   total_len [B] int32 (>= 1)
+ *   out      [B, Hq, 1, D] dtype;  lse [B, Hq, 1] f32 nullable
+ *   W >= 1, S >= 0, D in {64, 128}, Hq % Hkv == 0.
+ */
+spec_status_t spec_window_attention(const void* q, void* k_ring, void* v_ring, void* k_sink,
+                                    void* v_sink, const void* k_new, const void* v_new,
+                                    const int32_t* total_len, void* out, float* lse, int32_t B,
+                                    int32_t Hq, int32_t Hkv, int32_t D, int32_t W, int32_t S,
+                                    spec_dtype_t dtype, float scale, int32_t num_splits,
+                                    void* workspace, size_t workspace_bytes, int32_t* dev_err,
+                                    hipStream_t stream);
+
+size_t spec_window_attention_workspace(int32_t B, int32_t Hq, int32_t Hkv, int32_t D, int32_t W,
+                                       int32_t S, spec_dtype_t dtype, int32_t num_splits);
+
+/*
+ * spec_sample -- acceptance test, residual resample and bonus draw.
+ *
+ * Defines: "Guide to MagicDec", section 2 (accept x with probability
+ * min(1, p_target(x)/p_draft(x)); on rejection resample from the normalised
+ * max(0, p_target - p_draft)) and its verifier code (bonus token from the
+ * target row after the last draft when all are accepted); "Speculative
+ * Decoding & Medusa Architecture", section 2 (one speculative sampling step);
+ * "Speculative Decoding in LLM Serving Systems", section "Accepting and
+ * rejecting" (walk left to right, stop at the first rejection, 1 .. gamma+1
+ * tokens per round).
+ *
+ * Node view: node 0 is the last accepted token, nodes 1..N-1 are drafted
+ * tokens, parent[c] < c.  A chain is N = gamma+1 with parent == NULL.
+ *   target_logits [B, N, V] f32   row u: target next-token logits after node u
+ *   draft_logits  [B, N, V] f32   row u: draft logits u's children were drawn
+ *                                 from (rows of leaves are never read)
+ *   tokens        [B, N] int32    drafted token of node c (tokens[b][0] unused)
+ *   parent        int32 nullable: NULL = chain; [N] (parent_batch_stride 0)
+ *                 or [B, N] (stride N); parent[0] = -1, parent[c] in [0, c).
+ *   seed, offset  Philox4x32-10 key = seed; offset < 2^30 selects the round.
+ *                 Node c's acceptance uniform is U(ctr = (c, 0, b, 4*offset)),
+ *                 U(w) = (2*(w>>9)+1) * 2^-24 from output word 0.  Each node is
+ *                 tested; the walk takes, at every node, its first child (in
+ *                 index order) that passed.  The draw at the stop row is a
+ *                 two-level exponential race over 1024-id chunks (counters
+ *                 (chunk, row, b, 4*offset+2) and (id/4, row, b, 4*offset+3),
+ *                 word id%4); ties go to the lowest index.
+ * Outputs (all [B, ...], device):
+ *   out_tokens [B, N] int32   accepted drafted tokens then the drawn token, -1 padded
+ *   out_count  [B]    int32   emitted tokens (1 .. depth+1); 0 on a device-data error
+ *   out_path   [B, N] int32   nullable: node ids of the accepted path from 0, -1 padded
+ *   out_accept [B, N] uint8   nullable: per-node test result (node 0 reported 1)
+ * N in 1 .. SPEC_MAX_SAMPLE_NODES, V >= 1.
+ */
+spec_status_t spec_sample(const float* target_logits, const float* draft_logits,
+                          const int32_t* tokens, const int32_t* parent,
+                          int32_t parent_batch_stride, int32_t B, int32_t N, int32_t V,
+                          uint64_t seed, uint64_t offset, int32_t* out_tokens, int32_t* out_count,
+                          int32_t* out_path, uint8_t* out_accept, void* workspace,
+                          size_t workspace_bytes, int32_t* dev_err, hipStream_t stream);
+
+size_t spec_sample_workspace(int32_t B, int32_t N, int32_t V);
+
+/*
+ * spec_validate_tree -- host-side check of a parent array (host pointer).
+ * Valid: parent[c] in [-1, c) for every c; with require_single_root also
+ * parent[0] == -1 and parent[c] >= 0 for c >= 1.  Returns SPEC_OK,
+ * SPEC_ERR_BAD_TREE, or SPEC_ERR_INVALID_ARG (NULL pointer, n < 1).
+ */
+spec_status_t spec_validate_tree(const int32_t* parent_host, int32_t n,
+                                 int32_t require_single_root);
+
+/* Static, human-readable name of a status code. */
+const char* spec_status_str(spec_status_t status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SPEC_VERIFY_H */

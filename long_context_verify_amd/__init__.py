@@ -1,0 +1,36 @@
+"""MI355X-native (gfx950) kernels for the verification step of speculative decoding.
+
+The computation lives in ``libspecverify.so`` (hand-written HIP, built from
+``csrc/`` by ``build.py``) behind the C ABI of ``include/spec_verify.h``:
+
+* ``verify_attention`` -- block-of-queries attention against the full KV
+  cache, chain (causal) or candidate tree (ancestor-only) mask;
+* ``window_attention`` -- the draft's bounded attention over sink tokens and
+  a FIFO ring of the last W tokens, with an optional fused append;
+* ``spec_sample`` -- vocabulary softmax, min(1, target/draft) acceptance and
+  the residual / bonus draw.
+
+This package only marshals torch tensors into those calls.
+"""
+
+from .api import (  # noqa: F401
+    SPEC_BF16,
+    SPEC_F32,
+    SpecError,
+    lib,
+    sample_workspace_bytes,
+    spec_sample,
+    status_str,
+    validate_tree,
+    verify_attention,
+    verify_attention_auto_splits,
+    verify_attention_workspace_bytes,
+    window_attention,
+    window_attention_workspace_bytes,
+)
+
+__all__ = [
+    "SPEC_BF16", "SPEC_F32", "SpecError", "lib", "sample_workspace_bytes", "spec_sample",
+    "status_str", "validate_tree", "verify_attention", "verify_attention_auto_splits",
+    "verify_attention_workspace_bytes", "window_attention", "window_attention_workspace_bytes",
+]

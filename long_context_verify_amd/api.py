@@ -1,0 +1,230 @@
+"""ctypes binding of ``libspecverify.so`` -- argument marshalling only.
+
+Every step of the computation runs in the library's HIP kernels; this module
+checks tensor dtypes and contiguity, allocates outputs and workspaces with
+torch (device memory is the only thing torch provides), and passes raw
+pointers plus torch's current HIP stream to the C entry points declared in
+``include/spec_verify.h``.  There is no fallback: if the library is missing
+or the tensors are not on a HIP device, the call raises.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+import re
+from typing import Optional
+
+import torch
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "libspecverify.so")
+HEADER = os.path.join(os.path.dirname(HERE), "include", "spec_verify.h")
+
+SPEC_F32, SPEC_BF16 = 0, 1
+_DTYPES = {torch.float32: SPEC_F32, torch.bfloat16: SPEC_BF16}
+
+_vp, _i32, _u64, _f32, _sz = (ctypes.c_void_p, ctypes.c_int32, ctypes.c_uint64,
+                              ctypes.c_float, ctypes.c_size_t)
+
+_SIGNATURES = {
+    "spec_verify_attention": (_i32, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32,
+                                     _i32, _i32, _i32, _i32, _f32, _i32, _vp, _sz, _vp, _vp]),
+    "spec_verify_attention_workspace": (_sz, [_i32] * 8),
+    "spec_verify_attention_auto_splits": (_i32, [_i32] * 7),
+    "spec_window_attention": (_i32, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i32, _i32,
+                                     _i32, _i32, _i32, _i32, _i32, _f32, _i32, _vp, _sz, _vp, _vp]),
+    "spec_window_attention_workspace": (_sz, [_i32] * 8),
+    "spec_sample": (_i32, [_vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _u64, _u64, _vp, _vp, _vp,
+                           _vp, _vp, _sz, _vp, _vp]),
+    "spec_sample_workspace": (_sz, [_i32] * 3),
+    "spec_validate_tree": (_i32, [_vp, _i32, _i32]),
+    "spec_status_str": (ctypes.c_char_p, [_i32]),
+}
+
+_lib = None
+
+
+class SpecError(RuntimeError):
+    """A non-zero status returned by the library."""
+
+    def __init__(self, status: int, where: str):
+        self.status = status
+        super().__init__(f"{where}: {status_str(status)} ({status})")
+
+
+def declared_functions() -> list:
+    """Names of the functions declared in include/spec_verify.h."""
+    text = open(HEADER).read()
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?[a-z_0-9]+\*?\s+\*?(spec_[a-z_0-9]+)\s*\(",
+                                 text, flags=re.M)))
+
+
+def lib():
+    """Load the built library once (raises if it has not been built)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"{LIB_PATH} is missing: build it with "
+                               "`python -m long_context_verify_amd.build`")
+        handle = ctypes.CDLL(LIB_PATH)
+        for name, (res, args) in _SIGNATURES.items():
+            fn = getattr(handle, name)
+            fn.restype = res
+            fn.argtypes = args
+        _lib = handle
+    return _lib
+
+
+def status_str(status: int) -> str:
+    return lib().spec_status_str(int(status)).decode()
+
+
+def _check(status: int, where: str):
+    if status != 0:
+        raise SpecError(status, where)
+
+
+def _p(t: Optional[torch.Tensor]):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(device) -> ctypes.c_void_p:
+    return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
+
+
+def _need_gpu(*ts):
+    for t in ts:
+        if t is not None and not t.is_cuda:
+            raise ValueError("tensors must live on a HIP device")
+        if t is not None and not t.is_contiguous():
+            raise ValueError("tensors must be contiguous")
+
+
+def _workspace(nbytes: int, device, workspace: Optional[torch.Tensor]):
+    if workspace is not None:
+        if workspace.numel() * workspace.element_size() < nbytes:
+            raise ValueError("workspace too small")
+        return workspace
+    return torch.empty(max(int(nbytes), 256), dtype=torch.uint8, device=device)
+
+
+def _parent_arg(parent, B, n, device):
+    if parent is None:
+        return None, 0
+    pt = torch.as_tensor(parent, dtype=torch.int32, device=device).contiguous()
+    if pt.dim() == 1:
+        if pt.numel() != n:
+            raise ValueError("parent must have n entries")
+        return pt, 0
+    if tuple(pt.shape) != (B, n):
+        raise ValueError("parent must be [n] or [B, n]")
+    return pt, n
+
+
+def verify_attention_workspace_bytes(B, Hq, Hkv, n_q, D, L_cap, dtype, num_splits=0) -> int:
+    return int(lib().spec_verify_attention_workspace(B, Hq, Hkv, n_q, D, L_cap, _DTYPES[dtype],
+                                                     num_splits))
+
+
+def verify_attention_auto_splits(B, Hq, Hkv, n_q, D, L_cap, dtype) -> int:
+    return int(lib().spec_verify_attention_auto_splits(B, Hq, Hkv, n_q, D, L_cap, _DTYPES[dtype]))
+
+
+def verify_attention(q, k_cache, v_cache, kv_len=None, parent=None, scale: float = 0.0,
+                     num_splits: int = 0, out=None, lse=None, workspace=None, dev_err=None,
+                     want_lse: bool = True):
+    """spec_verify_attention on torch tensors.  Returns (out, lse or None)."""
+    _need_gpu(q, k_cache, v_cache, kv_len, out, lse, dev_err)
+    if q.dtype not in _DTYPES or k_cache.dtype != q.dtype or v_cache.dtype != q.dtype:
+        raise ValueError("q, k, v must share dtype float32 or bfloat16")
+    B, Hq, n_q, D = q.shape
+    _, Hkv, L_cap, _ = k_cache.shape
+    dev = q.device
+    if out is None:
+        out = torch.empty_like(q)
+    if lse is None and want_lse:
+        lse = torch.empty(B, Hq, n_q, dtype=torch.float32, device=dev)
+    if kv_len is not None:
+        kv_len = torch.as_tensor(kv_len, dtype=torch.int32, device=dev).contiguous()
+    par, pstride = _parent_arg(parent, B, n_q, dev)
+    nbytes = verify_attention_workspace_bytes(B, Hq, Hkv, n_q, D, L_cap, q.dtype, num_splits)
+    ws = _workspace(nbytes, dev, workspace)
+    st = lib().spec_verify_attention(
+        _p(q), _p(k_cache), _p(v_cache), _p(out), _p(lse), _p(kv_len), _p(par), pstride,
+        B, Hq, Hkv, n_q, D, L_cap, _DTYPES[q.dtype], float(scale), int(num_splits), _p(ws),
+        ws.numel(), _p(dev_err), _stream(dev))
+    _check(st, "spec_verify_attention")
+    return out, lse
+
+
+def window_attention_workspace_bytes(B, Hq, Hkv, D, W, S, dtype, num_splits=0) -> int:
+    return int(lib().spec_window_attention_workspace(B, Hq, Hkv, D, W, S, _DTYPES[dtype],
+                                                     num_splits))
+
+
+def window_attention(q, k_ring, v_ring, k_sink, v_sink, total_len, k_new=None, v_new=None,
+                     scale: float = 0.0, num_splits: int = 0, out=None, lse=None,
+                     workspace=None, dev_err=None, want_lse: bool = True):
+    """spec_window_attention on torch tensors.  Returns (out, lse or None)."""
+    _need_gpu(q, k_ring, v_ring, k_sink, v_sink, k_new, v_new, total_len, out, lse, dev_err)
+    B, Hq, _, D = q.shape
+    _, Hkv, W, _ = k_ring.shape
+    S = 0 if k_sink is None else k_sink.shape[2]
+    dev = q.device
+    if out is None:
+        out = torch.empty_like(q)
+    if lse is None and want_lse:
+        lse = torch.empty(B, Hq, 1, dtype=torch.float32, device=dev)
+    tl = torch.as_tensor(total_len, dtype=torch.int32, device=dev).contiguous()
+    nbytes = window_attention_workspace_bytes(B, Hq, Hkv, D, W, S, q.dtype, num_splits)
+    ws = _workspace(nbytes, dev, workspace)
+    st = lib().spec_window_attention(
+        _p(q), _p(k_ring), _p(v_ring), _p(k_sink), _p(v_sink), _p(k_new), _p(v_new), _p(tl),
+        _p(out), _p(lse), B, Hq, Hkv, D, W, S, _DTYPES[q.dtype], float(scale), int(num_splits),
+        _p(ws), ws.numel(), _p(dev_err), _stream(dev))
+    _check(st, "spec_window_attention")
+    return out, lse
+
+
+def sample_workspace_bytes(B, N, V) -> int:
+    return int(lib().spec_sample_workspace(B, N, V))
+
+
+def spec_sample(target_logits, draft_logits, tokens, parent=None, seed: int = 0, offset: int = 0,
+                out_tokens=None, out_count=None, out_path=None, out_accept=None,
+                workspace=None, dev_err=None, want_path: bool = True, want_accept: bool = True):
+    """spec_sample on torch tensors.  Returns dict(out_tokens, out_count, out_path, out_accept)."""
+    _need_gpu(target_logits, draft_logits, tokens, out_tokens, out_count, out_path, out_accept,
+              dev_err)
+    if target_logits.dtype != torch.float32 or draft_logits.dtype != torch.float32:
+        raise ValueError("logits must be float32")
+    if tokens.dtype != torch.int32:
+        raise ValueError("tokens must be int32")
+    B, N, V = target_logits.shape
+    dev = target_logits.device
+    if out_tokens is None:
+        out_tokens = torch.empty(B, N, dtype=torch.int32, device=dev)
+    if out_count is None:
+        out_count = torch.empty(B, dtype=torch.int32, device=dev)
+    if out_path is None and want_path:
+        out_path = torch.empty(B, N, dtype=torch.int32, device=dev)
+    if out_accept is None and want_accept:
+        out_accept = torch.empty(B, N, dtype=torch.uint8, device=dev)
+    par, pstride = _parent_arg(parent, B, N, dev)
+    ws = _workspace(sample_workspace_bytes(B, N, V), dev, workspace)
+    st = lib().spec_sample(
+        _p(target_logits), _p(draft_logits), _p(tokens), _p(par), pstride, B, N, V,
+        int(seed) & (2**64 - 1), int(offset), _p(out_tokens), _p(out_count), _p(out_path),
+        _p(out_accept), _p(ws), ws.numel(), _p(dev_err), _stream(dev))
+    _check(st, "spec_sample")
+    return {"out_tokens": out_tokens, "out_count": out_count, "out_path": out_path,
+            "out_accept": out_accept}
+
+
+def validate_tree(parent, require_single_root: bool = True) -> int:
+    """spec_validate_tree on a host parent array; returns the status code."""
+    import numpy as np
+    arr = np.ascontiguousarray(np.asarray(parent, dtype=np.int32))
+    return int(lib().spec_validate_tree(arr.ctypes.data_as(ctypes.c_void_p), int(arr.size),
+                                        int(bool(require_single_root))))

@@ -1,0 +1,264 @@
+// abi.cpp -- the exported C entry points: argument checks, launch plans, dispatch.
+//
+// Every check here runs on the host before any HIP call, so a bad argument
+// returns a status without touching the device (and can be exercised on a
+// machine without a GPU).
+
+#include <math.h>
+#include <string.h>
+
+#include <hip/hip_runtime_api.h>
+
+#include "spec_internal.hpp"
+#include "spec_verify.h"
+
+using namespace specv;
+
+namespace {
+
+bool aligned(const void* p, size_t a) { return p && (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+bool aligned_or_null(const void* p, size_t a) { return !p || aligned(p, a); }
+
+float resolve_scale(float scale, int32_t D) {
+  const float s = (scale > 0.f && isfinite(scale)) ? scale : 1.0f / sqrtf((float)D);
+  return s * 1.4426950408889634f;  // log2(e): the kernels run their softmax in base 2
+}
+
+spec_status_t check_attn_shape(int32_t B, int32_t Hq, int32_t Hkv, int32_t D, spec_dtype_t dtype,
+                               int32_t num_splits) {
+  if (B < 0 || Hq < 1 || Hkv < 1 || Hq % Hkv) return SPEC_ERR_INVALID_ARG;
+  if (dtype != SPEC_F32 && dtype != SPEC_BF16) return SPEC_ERR_INVALID_ARG;
+  if (D != 64 && D != 128) return SPEC_ERR_UNSUPPORTED;
+  if (num_splits < 0 || num_splits > 65536) return SPEC_ERR_INVALID_ARG;
+  return SPEC_OK;
+}
+
+spec_status_t verify_shape(int32_t B, int32_t Hq, int32_t Hkv, int32_t n_q, int32_t D,
+                           int32_t L_cap, spec_dtype_t dtype, int32_t num_splits) {
+  spec_status_t st = check_attn_shape(B, Hq, Hkv, D, dtype, num_splits);
+  if (st != SPEC_OK) return st;
+  if (n_q < 1) return SPEC_ERR_INVALID_ARG;
+  if (n_q > SPEC_MAX_NQ) return SPEC_ERR_UNSUPPORTED;
+  if (L_cap < n_q || L_cap > (1 << 30)) return SPEC_ERR_INVALID_ARG;
+  if ((long long)(Hq / Hkv) * n_q > (1 << 20)) return SPEC_ERR_UNSUPPORTED;
+  return SPEC_OK;
+}
+
+spec_status_t window_shape(int32_t B, int32_t Hq, int32_t Hkv, int32_t D, int32_t W, int32_t S,
+                           spec_dtype_t dtype, int32_t num_splits) {
+  spec_status_t st = check_attn_shape(B, Hq, Hkv, D, dtype, num_splits);
+  if (st != SPEC_OK) return st;
+  if (W < 1 || S < 0 || (long long)W + S > (1 << 30)) return SPEC_ERR_INVALID_ARG;
+  return SPEC_OK;
+}
+
+spec_status_t sample_shape(int32_t B, int32_t N, int32_t V) {
+  if (B < 0 || N < 1 || V < 1) return SPEC_ERR_INVALID_ARG;
+  if (N > SPEC_MAX_SAMPLE_NODES) return SPEC_ERR_UNSUPPORTED;
+  if (V > (1 << 27) || B > 65535) return SPEC_ERR_UNSUPPORTED;
+  return SPEC_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* spec_status_str(spec_status_t status) {
+  switch (status) {
+    case SPEC_OK: return "SPEC_OK";
+    case SPEC_ERR_INVALID_ARG: return "SPEC_ERR_INVALID_ARG";
+    case SPEC_ERR_UNSUPPORTED: return "SPEC_ERR_UNSUPPORTED";
+    case SPEC_ERR_BAD_TREE: return "SPEC_ERR_BAD_TREE";
+    case SPEC_ERR_MISALIGNED: return "SPEC_ERR_MISALIGNED";
+    case SPEC_ERR_WORKSPACE: return "SPEC_ERR_WORKSPACE";
+    case SPEC_ERR_HIP: return "SPEC_ERR_HIP";
+  }
+  return "SPEC_ERR_UNKNOWN";
+}
+
+spec_status_t spec_validate_tree(const int32_t* parent_host, int32_t n, int32_t require_single_root) {
+  if (!parent_host || n < 1) return SPEC_ERR_INVALID_ARG;
+  for (int32_t c = 0; c < n; ++c) {
+    const int32_t p = parent_host[c];
+    if (p < -1 || p >= c) return SPEC_ERR_BAD_TREE;
+    if (require_single_root && ((c == 0) != (p == -1))) return SPEC_ERR_BAD_TREE;
+  }
+  return SPEC_OK;
+}
+
+int32_t spec_verify_attention_auto_splits(int32_t B, int32_t Hq, int32_t Hkv, int32_t n_q,
+                                          int32_t D, int32_t L_cap, spec_dtype_t dtype) {
+  if (verify_shape(B, Hq, Hkv, n_q, D, L_cap, dtype, 0) != SPEC_OK || B == 0) return 0;
+  return plan_attention(B, Hkv, (Hq / Hkv) * n_q, D, L_cap, dtype, 0, false).n_splits;
+}
+
+size_t spec_verify_attention_workspace(int32_t B, int32_t Hq, int32_t Hkv, int32_t n_q, int32_t D,
+                                       int32_t L_cap, spec_dtype_t dtype, int32_t num_splits) {
+  if (verify_shape(B, Hq, Hkv, n_q, D, L_cap, dtype, num_splits) != SPEC_OK) return 0;
+  if (B == 0) return 0;
+  return plan_attention(B, Hkv, (Hq / Hkv) * n_q, D, L_cap, dtype, num_splits, false).ws_bytes;
+}
+
+spec_status_t spec_verify_attention(const void* q, const void* k_cache, const void* v_cache,
+                                    void* out, float* lse, const int32_t* kv_len,
+                                    const int32_t* parent, int32_t parent_batch_stride,
+                                    int32_t B, int32_t Hq, int32_t Hkv, int32_t n_q, int32_t D,
+                                    int32_t L_cap, spec_dtype_t dtype, float scale,
+                                    int32_t num_splits, void* workspace, size_t workspace_bytes,
+                                    int32_t* dev_err, hipStream_t stream) {
+  spec_status_t st = verify_shape(B, Hq, Hkv, n_q, D, L_cap, dtype, num_splits);
+  if (st != SPEC_OK) return st;
+  if (parent && parent_batch_stride != 0 && parent_batch_stride != n_q) return SPEC_ERR_INVALID_ARG;
+  if (B == 0) return SPEC_OK;
+  if (!aligned(q, 16) || !aligned(k_cache, 16) || !aligned(v_cache, 16) || !aligned(out, 16) ||
+      !aligned_or_null(lse, 4) || !aligned_or_null(kv_len, 4) || !aligned_or_null(parent, 4) ||
+      !aligned_or_null(dev_err, 4))
+    return SPEC_ERR_MISALIGNED;
+  const int32_t g = Hq / Hkv;
+  const AttnPlan p = plan_attention(B, Hkv, g * n_q, D, L_cap, dtype, num_splits, false);
+  if (!aligned(workspace, 256) || workspace_bytes < p.ws_bytes) return SPEC_ERR_WORKSPACE;
+
+  AttnArgs a;
+  memset(&a, 0, sizeof(a));
+  a.q = q;
+  a.k = k_cache;
+  a.v = v_cache;
+  a.lens = kv_len;
+  a.parent = parent;
+  a.parent_stride = parent ? parent_batch_stride : 0;
+  a.ws_o = static_cast<float*>(workspace);
+  a.ws_ml = reinterpret_cast<float*>(static_cast<char*>(workspace) + p.ws_o_bytes);
+  a.B = B;
+  a.Hq = Hq;
+  a.Hkv = Hkv;
+  a.g = g;
+  a.n_q = n_q;
+  a.D = D;
+  a.L_cap = L_cap;
+  a.M = g * n_q;
+  a.slice_rows = p.slice_rows;
+  a.n_qs = p.n_qs;
+  a.n_splits = p.n_splits;
+  a.n_tiles = B * Hkv * p.n_splits;
+  a.grid = p.grid;
+  a.scale_log2 = resolve_scale(scale, D);
+  a.dev_err = dev_err;
+  return launch_attention(a, false, dtype, out, lse, stream) == hipSuccess ? SPEC_OK : SPEC_ERR_HIP;
+}
+
+size_t spec_window_attention_workspace(int32_t B, int32_t Hq, int32_t Hkv, int32_t D, int32_t W,
+                                       int32_t S, spec_dtype_t dtype, int32_t num_splits) {
+  if (window_shape(B, Hq, Hkv, D, W, S, dtype, num_splits) != SPEC_OK || B == 0) return 0;
+  return plan_attention(B, Hkv, Hq / Hkv, D, W + S, dtype, num_splits, true).ws_bytes;
+}
+
+spec_status_t spec_window_attention(const void* q, void* k_ring, void* v_ring, void* k_sink,
+                                    void* v_sink, const void* k_new, const void* v_new,
+                                    const int32_t* total_len, void* out, float* lse, int32_t B,
+                                    int32_t Hq, int32_t Hkv, int32_t D, int32_t W, int32_t S,
+                                    spec_dtype_t dtype, float scale, int32_t num_splits,
+                                    void* workspace, size_t workspace_bytes, int32_t* dev_err,
+                                    hipStream_t stream) {
+  spec_status_t st = window_shape(B, Hq, Hkv, D, W, S, dtype, num_splits);
+  if (st != SPEC_OK) return st;
+  if (B == 0) return SPEC_OK;
+  if ((k_new == nullptr) != (v_new == nullptr)) return SPEC_ERR_INVALID_ARG;
+  if (!aligned(q, 16) || !aligned(k_ring, 16) || !aligned(v_ring, 16) || !aligned(out, 16) ||
+      !aligned(total_len, 4) || !aligned_or_null(lse, 4) || !aligned_or_null(k_new, 16) ||
+      !aligned_or_null(v_new, 16) || !aligned_or_null(dev_err, 4))
+    return SPEC_ERR_MISALIGNED;
+  if (S > 0 && (!aligned(k_sink, 16) || !aligned(v_sink, 16))) return SPEC_ERR_MISALIGNED;
+  const int32_t g = Hq / Hkv;
+  const AttnPlan p = plan_attention(B, Hkv, g, D, W + S, dtype, num_splits, true);
+  if (!aligned(workspace, 256) || workspace_bytes < p.ws_bytes) return SPEC_ERR_WORKSPACE;
+
+  AttnArgs a;
+  memset(&a, 0, sizeof(a));
+  a.q = q;
+  a.k = k_ring;
+  a.v = v_ring;
+  a.k_sink = k_sink;
+  a.v_sink = v_sink;
+  a.k_new = k_new;
+  a.v_new = v_new;
+  a.k_ring_w = k_ring;
+  a.v_ring_w = v_ring;
+  a.k_sink_w = k_sink;
+  a.v_sink_w = v_sink;
+  a.lens = total_len;
+  a.ws_o = static_cast<float*>(workspace);
+  a.ws_ml = reinterpret_cast<float*>(static_cast<char*>(workspace) + p.ws_o_bytes);
+  a.B = B;
+  a.Hq = Hq;
+  a.Hkv = Hkv;
+  a.g = g;
+  a.n_q = 1;
+  a.D = D;
+  a.L_cap = W + S;
+  a.M = g;
+  a.W = W;
+  a.S = S;
+  a.slice_rows = p.slice_rows;
+  a.n_qs = p.n_qs;
+  a.n_splits = p.n_splits;
+  a.n_tiles = B * Hkv * p.n_splits;
+  a.grid = p.grid;
+  a.scale_log2 = resolve_scale(scale, D);
+  a.dev_err = dev_err;
+  return launch_attention(a, true, dtype, out, lse, stream) == hipSuccess ? SPEC_OK : SPEC_ERR_HIP;
+}
+
+size_t spec_sample_workspace(int32_t B, int32_t N, int32_t V) {
+  if (sample_shape(B, N, V) != SPEC_OK || B == 0) return 0;
+  return plan_sample(B, N, V).bytes;
+}
+
+spec_status_t spec_sample(const float* target_logits, const float* draft_logits,
+                          const int32_t* tokens, const int32_t* parent,
+                          int32_t parent_batch_stride, int32_t B, int32_t N, int32_t V,
+                          uint64_t seed, uint64_t offset, int32_t* out_tokens, int32_t* out_count,
+                          int32_t* out_path, uint8_t* out_accept, void* workspace,
+                          size_t workspace_bytes, int32_t* dev_err, hipStream_t stream) {
+  spec_status_t st = sample_shape(B, N, V);
+  if (st != SPEC_OK) return st;
+  if (offset >= (1ull << 30)) return SPEC_ERR_INVALID_ARG;
+  if (parent && parent_batch_stride != 0 && parent_batch_stride != N) return SPEC_ERR_INVALID_ARG;
+  if (B == 0) return SPEC_OK;
+  if (!aligned(target_logits, 16) || !aligned(draft_logits, 16) || !aligned(tokens, 4) ||
+      !aligned(out_tokens, 4) || !aligned(out_count, 4) || !aligned_or_null(out_path, 4) ||
+      !aligned_or_null(parent, 4) || !aligned_or_null(dev_err, 4))
+    return SPEC_ERR_MISALIGNED;
+  const SamplePlan p = plan_sample(B, N, V);
+  if (!aligned(workspace, 256) || workspace_bytes < p.bytes) return SPEC_ERR_WORKSPACE;
+
+  SampleArgs a;
+  memset(&a, 0, sizeof(a));
+  a.target = target_logits;
+  a.draft = draft_logits;
+  a.tokens = tokens;
+  a.parent = parent;
+  a.parent_stride = parent ? parent_batch_stride : 0;
+  a.B = B;
+  a.N = N;
+  a.V = V;
+  a.key0 = (uint32_t)(seed & 0xffffffffu);
+  a.key1 = (uint32_t)(seed >> 32);
+  a.ctr3_base = (uint32_t)(4 * offset);
+  a.out_tokens = out_tokens;
+  a.out_count = out_count;
+  a.out_path = out_path;
+  a.out_accept = out_accept;
+  char* ws = static_cast<char*>(workspace);
+  a.part_m = reinterpret_cast<float*>(ws + p.off_m);
+  a.part_s = reinterpret_cast<double*>(ws + p.off_s);
+  a.race_w = reinterpret_cast<double*>(ws + p.off_w);
+  a.counters = reinterpret_cast<int32_t*>(ws + p.off_cnt);
+  a.n_vchunks = p.n_vchunks;
+  a.vchunk = p.vchunk;
+  a.n_race = p.n_race;
+  a.n_groups = p.n_groups;
+  a.dev_err = dev_err;
+  return launch_sample(a, stream) == hipSuccess ? SPEC_OK : SPEC_ERR_HIP;
+}
+
+}  // extern "C"

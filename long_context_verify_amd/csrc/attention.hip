@@ -1,0 +1,597 @@
+// attention.hip -- split-K attention of a query block against a long KV cache (gfx950).
+//
+// Verification attention ("Guide to MagicDec", section 2: the target verifies
+// the drafted tokens with attention over the full context; "Speculative
+// Decoding in LLM Serving Systems", sections "The algorithm" and "Tree-based
+// variants": the drafted block is causal within itself, or a tree where each
+// node sees only its ancestors) and the draft's bounded window attention
+// ("Guide to MagicDec", section 1, fixed window as a FIFO ring, and "Best
+// Practices" item 1, attention sinks) share one streaming core:
+//
+//   * a work-group owns one (sequence, kv head) unit, one slice of its query
+//     rows (the g query heads of the GQA group times the n_q block nodes, all
+//     served by the same K/V tiles) and one contiguous range of 32-key chunks;
+//   * each of its four waves walks every fourth chunk on its own, with no LDS
+//     and no barrier in the loop: K and V rows are loaded straight into MFMA
+//     operand registers (V as eight 16-byte row pieces that are transposed
+//     in-register), S^T = K Q^T and O^T = V^T P^T run on
+//     v_mfma_f32_16x16x32_bf16, and an online softmax in the log2 domain keeps
+//     every per-query quantity in the lanes of that query;
+//   * the mask is evaluated only on chunks that reach the block's own keys or
+//     the end of the sequence: a key is visible if it precedes the block or is
+//     an ancestor of the query's node (a 64-bit mask built from the parent
+//     array);
+//   * the four waves merge through LDS once at the end; the split partials
+//     (unnormalised O, running max, sum) go to the workspace and a second
+//     kernel combines them in a fixed order.
+//
+// The fp32 path is a plain VALU kernel (one wave per query row, lanes over
+// the head dimension) with the same partial format.
+
+#include <hip/hip_runtime.h>
+
+#include "spec_common.hpp"
+#include "spec_internal.hpp"
+
+namespace specv {
+
+constexpr int kChunk = 32;          // keys per wave step (two MFMA row blocks of 16)
+constexpr int kWaves = 4;           // waves per work-group
+constexpr int kThreads = kWaves * kWave;
+constexpr int kValuSlice = 4;       // query rows per work-group on the VALU path
+
+// ---------------------------------------------------------------------------
+// Key geometry of one (sequence, kv head) unit.
+// ---------------------------------------------------------------------------
+struct UnitGeom {
+  int b, hk, unit;
+  int n_keys;   // logical keys 0 .. n_keys-1
+  int p0;       // keys >= p0 are the block's own keys (masked by ancestry)
+  int key_new;  // window: logical key served from k_new/v_new (-1: none)
+  int ns;       // window: number of sink keys (keys < ns are sinks)
+};
+
+template <bool WINDOW>
+__device__ __forceinline__ UnitGeom unit_geom(const AttnArgs& a, int unit, bool report) {
+  UnitGeom u;
+  u.unit = unit;
+  u.b = unit / a.Hkv;
+  u.hk = unit - u.b * a.Hkv;
+  u.key_new = -1;
+  u.ns = 0;
+  if (!WINDOW) {
+    int L = a.lens ? a.lens[u.b] : a.L_cap;
+    if (L < a.n_q || L > a.L_cap) {
+      if (report) report_error(a.dev_err, SPEC_DEVERR_KV_LEN);
+      L = 0;
+    }
+    u.n_keys = L;
+    u.p0 = L - a.n_q;
+  } else {
+    int T = a.lens[u.b];
+    if (T < 1) {
+      if (report) report_error(a.dev_err, SPEC_DEVERR_TOTAL_LEN);
+      u.n_keys = 0;
+      u.p0 = 0;
+      return u;
+    }
+    int ns = T < a.S ? T : a.S;
+    int nr = T - a.S;
+    nr = nr < 0 ? 0 : (nr > a.W ? a.W : nr);
+    u.ns = ns;
+    u.n_keys = ns + nr;
+    u.p0 = u.n_keys;  // one query per sequence: nothing inside the window is masked
+    if (a.k_new) u.key_new = (T - 1 < a.S) ? (T - 1) : ns + (T - 1 - a.S) % a.W;
+  }
+  return u;
+}
+
+// Byte address of logical key `key` of a unit, for the K (kv=0) or V (kv=1) side.
+template <bool WINDOW>
+__device__ __forceinline__ const char* key_row(const AttnArgs& a, const UnitGeom& u, int key,
+                                               int kv, size_t row_bytes) {
+  if (!WINDOW) {
+    const char* base = static_cast<const char*>(kv ? a.v : a.k);
+    return base + ((size_t)u.unit * a.L_cap + key) * row_bytes;
+  } else {
+    if (key == u.key_new)
+      return static_cast<const char*>(kv ? a.v_new : a.k_new) + (size_t)u.unit * row_bytes;
+    if (key < u.ns)
+      return static_cast<const char*>(kv ? a.v_sink : a.k_sink) +
+             ((size_t)u.unit * a.S + key) * row_bytes;
+    return static_cast<const char*>(kv ? a.v : a.k) +
+           ((size_t)u.unit * a.W + (key - u.ns)) * row_bytes;
+  }
+}
+
+// Ancestor bitmask of block node i (bit t set: node t is i or an ancestor of i).
+__device__ __forceinline__ uint64_t ancestor_mask(const AttnArgs& a, int b, int i) {
+  if (!a.parent) return (i >= 63) ? ~0ull : ((2ull << i) - 1ull);
+  const int32_t* par = a.parent + (size_t)b * a.parent_stride;
+  uint64_t m = 0;
+  int cur = i;
+  for (int step = 0; step < 64 && cur >= 0; ++step) {
+    m |= 1ull << cur;
+    int p = par[cur];
+    if (p >= cur || p < -1) {  // not a forest with parent < child: treat as a root
+      report_error(a.dev_err, SPEC_DEVERR_PARENT);
+      break;
+    }
+    cur = p;
+  }
+  return m;
+}
+
+// Work-group -> (tile, query slice).  Tiles are (unit, split) pairs.  When a unit
+// has several query slices, all slices of a tile are placed on the same XCD
+// (work-groups are dealt round-robin over the 8 XCDs) and dispatched back to
+// back, so the K/V they share is served from that XCD's L2.
+__device__ __forceinline__ bool decode_tile(const AttnArgs& a, int& unit, int& split, int& qs) {
+  int id = blockIdx.x;
+  int tile;
+  if (a.n_qs == 1) {
+    tile = id;
+    qs = 0;
+  } else {
+    int xcd = id & 7;
+    int local = id >> 3;
+    int tix = local / a.n_qs;
+    qs = local - tix * a.n_qs;
+    tile = tix * 8 + xcd;
+  }
+  if (tile >= a.n_tiles) return false;
+  unit = tile / a.n_splits;
+  split = tile - unit * a.n_splits;
+  return true;
+}
+
+__device__ __forceinline__ void chunk_range(int n_keys, int split, int n_splits, int& c0, int& c1) {
+  long long nch = (n_keys + kChunk - 1) / kChunk;
+  c0 = (int)(nch * split / n_splits);
+  c1 = (int)(nch * (split + 1) / n_splits);
+}
+
+// Fused append of the window kernel: the current token's K/V go to its slot.
+// Only the (split 0, slice 0) work-group of a unit writes; every reader of that
+// key takes it from k_new/v_new instead, so no reader sees the slot mid-write.
+template <bool WINDOW>
+__device__ __forceinline__ void window_append(const AttnArgs& a, const UnitGeom& u, int split,
+                                              int qs, size_t row_bytes) {
+  if (!WINDOW) return;
+  if (u.key_new < 0 || split != 0 || qs != 0) return;
+  const int n16 = (int)(row_bytes / 16);
+  for (int t = threadIdx.x; t < 2 * n16; t += blockDim.x) {
+    int kv = t / n16, piece = t - kv * n16;
+    const u32x4* src = reinterpret_cast<const u32x4*>(
+        static_cast<const char*>(kv ? a.v_new : a.k_new) + (size_t)u.unit * row_bytes);
+    char* dst;
+    if (u.key_new < u.ns)
+      dst = static_cast<char*>(kv ? a.v_sink_w : a.k_sink_w) +
+            ((size_t)u.unit * a.S + u.key_new) * row_bytes;
+    else
+      dst = static_cast<char*>(kv ? a.v_ring_w : a.k_ring_w) +
+            ((size_t)u.unit * a.W + (u.key_new - u.ns)) * row_bytes;
+    reinterpret_cast<u32x4*>(dst)[piece] = src[piece];
+  }
+}
+
+// ---------------------------------------------------------------------------
+// bf16 MFMA split kernel.  QB = MFMA query blocks (16 rows each) per slice.
+// ---------------------------------------------------------------------------
+template <int D, int QB, bool WINDOW>
+__global__ __launch_bounds__(kThreads, 2) void attn_split_mfma(AttnArgs a) {
+  constexpr int DS = D / 32;             // MFMA k-steps over the head dim for S
+  constexpr int SR = 16 * QB;            // query rows per slice
+  constexpr int LDS_STRIDE = D + 1;
+  __shared__ float lds_o[kWaves][SR][LDS_STRIDE];
+  __shared__ float lds_ml[kWaves][SR][2];
+
+  int unit, split, qs;
+  if (!decode_tile(a, unit, split, qs)) return;
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  const int r = lane & 15;   // MFMA column: query within a block; also V row piece
+  const int h = lane >> 4;   // MFMA k-group
+  const size_t row_bytes = (size_t)D * 2;
+
+  const UnitGeom u = unit_geom<WINDOW>(a, unit, split == 0 && qs == 0 && threadIdx.x == 0);
+  window_append<WINDOW>(a, u, split, qs, row_bytes);
+
+  // Query operands (B side of S^T = K Q^T): lane holds Q[row][32 s + 8 h .. +8].
+  const char* qbase = static_cast<const char*>(a.q) +
+                      ((size_t)(u.b * a.Hq + u.hk * a.g) * a.n_q) * row_bytes;
+  bf16x8 qop[QB][DS];
+  uint64_t anc[QB];
+#pragma unroll
+  for (int qb = 0; qb < QB; ++qb) {
+    const int row = qs * SR + qb * 16 + r;
+    const bool live = row < a.M;
+#pragma unroll
+    for (int s = 0; s < DS; ++s) {
+      if (live)
+        qop[qb][s] = *reinterpret_cast<const bf16x8*>(qbase + (size_t)row * row_bytes +
+                                                      (32 * s + 8 * h) * 2);
+      else
+        qop[qb][s] = bf16x8{};
+    }
+    anc[qb] = (!WINDOW && live) ? ancestor_mask(a, u.b, row % a.n_q) : 1ull;
+  }
+
+  int c0, c1;
+  chunk_range(u.n_keys, split, a.n_splits, c0, c1);
+
+  float m[QB], lsum[QB];
+  f32x4 oacc[QB][8];
+#pragma unroll
+  for (int qb = 0; qb < QB; ++qb) {
+    m[qb] = -INFINITY;
+    lsum[qb] = 0.f;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) oacc[qb][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+  }
+
+  const int last = u.n_keys - 1;
+  for (int c = c0 + wave; c < c1; c += kWaves) {
+    const int kbase = c * kChunk;
+    // K operands (A side): lane holds K[kbase + 16 kb + r][32 s + 8 h .. +8].
+    bf16x8 kop[2][DS];
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) {
+      int key = kbase + 16 * kb + r;
+      key = key < last ? key : last;
+      const char* p = key_row<WINDOW>(a, u, key, 0, row_bytes);
+#pragma unroll
+      for (int s = 0; s < DS; ++s)
+        kop[kb][s] = *reinterpret_cast<const bf16x8*>(p + (32 * s + 8 * h) * 2);
+    }
+    // V row pieces: lane holds V[key(h,t)][8 r .. 8 r + 7] for its eight keys
+    // key(h,t) = kbase + 16 (t/4) + 4 h + t%4 -- the keys whose scores the
+    // S^T accumulators leave in this lane.
+    u32x4 vraw[8];
+#pragma unroll
+    for (int t = 0; t < 8; ++t) {
+      int key = kbase + 16 * (t >> 2) + 4 * h + (t & 3);
+      key = key < last ? key : last;
+      if (8 * r < D)
+        vraw[t] = *reinterpret_cast<const u32x4*>(key_row<WINDOW>(a, u, key, 1, row_bytes) +
+                                                  r * 16);
+      else
+        vraw[t] = u32x4{0u, 0u, 0u, 0u};
+    }
+
+    // S^T blocks: sacc[qb][kb][e] = score(key kbase + 16 kb + 4 h + e, query qb*16 + r).
+    f32x4 sacc[QB][2];
+#pragma unroll
+    for (int qb = 0; qb < QB; ++qb)
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb) {
+        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int s = 0; s < DS; ++s)
+          acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kop[kb][s], qop[qb][s], acc, 0, 0, 0);
+        sacc[qb][kb] = acc;
+      }
+
+    const bool need_mask = kbase + kChunk > u.p0;
+    bf16x8 pop[QB];
+#pragma unroll
+    for (int qb = 0; qb < QB; ++qb) {
+      float sv[8];
+#pragma unroll
+      for (int t = 0; t < 8; ++t) sv[t] = sacc[qb][t >> 2][t & 3] * a.scale_log2;
+      if (need_mask) {
+#pragma unroll
+        for (int t = 0; t < 8; ++t) {
+          const int key = kbase + 16 * (t >> 2) + 4 * h + (t & 3);
+          bool ok = key < u.n_keys;
+          if (ok && key >= u.p0) ok = (anc[qb] >> (key - u.p0)) & 1ull;
+          if (!ok) sv[t] = -INFINITY;
+        }
+      }
+      float cm = sv[0];
+#pragma unroll
+      for (int t = 1; t < 8; ++t) cm = fmaxf(cm, sv[t]);
+      cm = xgroup_max(cm);
+      const float mn = fmaxf(m[qb], cm);
+      const float mu = (mn == -INFINITY) ? 0.f : mn;
+      const float alpha = fast_exp2(m[qb] - mu);
+      m[qb] = mn;
+      float p[8];
+      float ps = 0.f;
+#pragma unroll
+      for (int t = 0; t < 8; ++t) {
+        p[t] = fast_exp2(sv[t] - mu);
+        ps += p[t];
+      }
+      lsum[qb] = lsum[qb] * alpha + ps;
+#pragma unroll
+      for (int j = 0; j < 8; ++j) oacc[qb][j] *= alpha;
+      u32x4 pk = {pack_bf16x2(p[0], p[1]), pack_bf16x2(p[2], p[3]), pack_bf16x2(p[4], p[5]),
+                  pack_bf16x2(p[6], p[7])};
+      pop[qb] = __builtin_bit_cast(bf16x8, pk);
+    }
+
+    // In-register 8x8 transpose: vop[j] holds V[key(h,t)][8 r + j] for t = 0..7,
+    // the A operand of O^T = V^T P^T whose row r stands for head-dim index 8 r + j.
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      u32x4 w;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const uint32_t lo = vraw[2 * e][j >> 1];
+        const uint32_t hi = vraw[2 * e + 1][j >> 1];
+        w[e] = (j & 1) ? ((lo >> 16) | (hi & 0xffff0000u)) : ((lo & 0xffffu) | (hi << 16));
+      }
+      const bf16x8 vop = __builtin_bit_cast(bf16x8, w);
+#pragma unroll
+      for (int qb = 0; qb < QB; ++qb)
+        oacc[qb][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vop, pop[qb], oacc[qb][j], 0, 0, 0);
+    }
+  }
+
+  // Wave partial -> LDS.  oacc[qb][j][e] is O(row qb*16 + r, head-dim 8 (4 h + e) + j).
+#pragma unroll
+  for (int qb = 0; qb < QB; ++qb) {
+    const float l = xgroup_sum(lsum[qb]);
+    const int row = qb * 16 + r;
+#pragma unroll
+    for (int j = 0; j < 8; ++j)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int d = 8 * (4 * h + e) + j;
+        if (d < D) lds_o[wave][row][d] = oacc[qb][j][e];
+      }
+    if (h == 0) {
+      lds_ml[wave][row][0] = m[qb];
+      lds_ml[wave][row][1] = l;
+    }
+  }
+  __syncthreads();
+
+  // Merge the four waves and store the work-group partial.
+  const size_t part = ((size_t)unit * a.n_qs + qs) * a.n_splits + split;
+  float* wo = a.ws_o + part * SR * D;
+  float* wml = a.ws_ml + part * SR * 2;
+  for (int idx = threadIdx.x; idx < SR * D; idx += kThreads) {
+    const int row = idx / D, d = idx - row * D;
+    float mx = -INFINITY;
+#pragma unroll
+    for (int w = 0; w < kWaves; ++w) mx = fmaxf(mx, lds_ml[w][row][0]);
+    const float mu = (mx == -INFINITY) ? 0.f : mx;
+    float o = 0.f, l = 0.f;
+#pragma unroll
+    for (int w = 0; w < kWaves; ++w) {
+      const float sc = fast_exp2(lds_ml[w][row][0] - mu);
+      o += sc * lds_o[w][row][d];
+      l += sc * lds_ml[w][row][1];
+    }
+    wo[idx] = o;
+    if (d == 0) {
+      wml[row * 2 + 0] = mx;
+      wml[row * 2 + 1] = l;
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// fp32 VALU split kernel: one wave per query row, lanes over the head dim.
+// ---------------------------------------------------------------------------
+template <int D, bool WINDOW>
+__global__ __launch_bounds__(kThreads) void attn_split_valu(AttnArgs a) {
+  constexpr int DPL = D / 64;  // head-dim entries per lane
+  int unit, split, qs;
+  if (!decode_tile(a, unit, split, qs)) return;
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  const size_t row_bytes = (size_t)D * 4;
+  const UnitGeom u = unit_geom<WINDOW>(a, unit, split == 0 && qs == 0 && threadIdx.x == 0);
+  window_append<WINDOW>(a, u, split, qs, row_bytes);
+
+  const int row = qs * kValuSlice + wave;
+  if (row >= a.M) return;   // no barrier follows
+  const float* qrow = reinterpret_cast<const float*>(
+      static_cast<const char*>(a.q) +
+      ((size_t)(u.b * a.Hq + u.hk * a.g) * a.n_q + row) * row_bytes);
+  float qv[DPL];
+#pragma unroll
+  for (int e = 0; e < DPL; ++e) qv[e] = qrow[lane + 64 * e];
+  const uint64_t anc = WINDOW ? 1ull : ancestor_mask(a, u.b, row % a.n_q);
+
+  int c0, c1;
+  chunk_range(u.n_keys, split, a.n_splits, c0, c1);
+  const int k0 = c0 * kChunk;
+  const int k1 = min(c1 * kChunk, u.n_keys);
+
+  float m = -INFINITY, l = 0.f;
+  float o[DPL];
+#pragma unroll
+  for (int e = 0; e < DPL; ++e) o[e] = 0.f;
+
+  constexpr int KB = 4;  // keys per step
+  for (int kk = k0; kk < k1; kk += KB) {
+    float s[KB];
+    float vv[KB][DPL];
+#pragma unroll
+    for (int t = 0; t < KB; ++t) {
+      int key = kk + t;
+      const bool ok_key = key < k1;
+      key = ok_key ? key : k1 - 1;
+      const float* kr = reinterpret_cast<const float*>(key_row<WINDOW>(a, u, key, 0, row_bytes));
+      const float* vr = reinterpret_cast<const float*>(key_row<WINDOW>(a, u, key, 1, row_bytes));
+      float part = 0.f;
+#pragma unroll
+      for (int e = 0; e < DPL; ++e) {
+        part = fmaf(qv[e], kr[lane + 64 * e], part);
+        vv[t][e] = vr[lane + 64 * e];
+      }
+#pragma unroll
+      for (int off = 32; off >= 1; off >>= 1) part += __shfl_xor(part, off);
+      bool ok = ok_key;
+      if (ok && key >= u.p0) ok = (anc >> (key - u.p0)) & 1ull;
+      s[t] = ok ? part * a.scale_log2 : -INFINITY;
+    }
+    float cm = s[0];
+#pragma unroll
+    for (int t = 1; t < KB; ++t) cm = fmaxf(cm, s[t]);
+    const float mn = fmaxf(m, cm);
+    const float mu = (mn == -INFINITY) ? 0.f : mn;
+    const float alpha = fast_exp2(m - mu);
+    m = mn;
+    l *= alpha;
+#pragma unroll
+    for (int e = 0; e < DPL; ++e) o[e] *= alpha;
+#pragma unroll
+    for (int t = 0; t < KB; ++t) {
+      const float p = fast_exp2(s[t] - mu);
+      l += p;
+#pragma unroll
+      for (int e = 0; e < DPL; ++e) o[e] = fmaf(p, vv[t][e], o[e]);
+    }
+  }
+
+  const size_t part = ((size_t)unit * a.n_qs + qs) * a.n_splits + split;
+  float* wo = a.ws_o + (part * kValuSlice + wave) * D;
+#pragma unroll
+  for (int e = 0; e < DPL; ++e) wo[lane + 64 * e] = o[e];
+  if (lane == 0) {
+    float* wml = a.ws_ml + (part * kValuSlice + wave) * 2;
+    wml[0] = m;
+    wml[1] = l;
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Split merge: one wave per output row, fixed split order (deterministic).
+// ---------------------------------------------------------------------------
+template <int D, typename OutT>
+__global__ __launch_bounds__(256) void attn_merge(MergeArgs a) {
+  constexpr int DPL = D / 64;
+  const int lane = threadIdx.x & 63;
+  const long long grow = (long long)blockIdx.x * 4 + (threadIdx.x >> 6);
+  const long long total = (long long)a.B * a.Hkv * a.M;
+  if (grow >= total) return;
+  const int unit = (int)(grow / a.M);
+  const int row = (int)(grow - (long long)unit * a.M);
+  const int qs = row / a.slice_rows;
+  const int rr = row - qs * a.slice_rows;
+  const size_t part0 = ((size_t)unit * a.n_qs + qs) * a.n_splits;
+
+  float mx = -INFINITY;
+  for (int s = 0; s < a.n_splits; ++s)
+    mx = fmaxf(mx, a.ws_ml[((part0 + s) * a.slice_rows + rr) * 2]);
+  const float mu = (mx == -INFINITY) ? 0.f : mx;
+  float acc[DPL];
+#pragma unroll
+  for (int e = 0; e < DPL; ++e) acc[e] = 0.f;
+  float l = 0.f;
+  for (int s = 0; s < a.n_splits; ++s) {
+    const size_t pr = (part0 + s) * a.slice_rows + rr;
+    const float sc = fast_exp2(a.ws_ml[pr * 2] - mu);
+    l += sc * a.ws_ml[pr * 2 + 1];
+    const float* src = a.ws_o + pr * D;
+#pragma unroll
+    for (int e = 0; e < DPL; ++e) acc[e] = fmaf(sc, src[lane + 64 * e], acc[e]);
+  }
+  const float inv = l > 0.f ? 1.f / l : 0.f;
+  const int b = unit / a.Hkv, hk = unit - (unit / a.Hkv) * a.Hkv;
+  const size_t orow = (size_t)(b * a.Hq + hk * a.g) * a.n_q + row;
+  OutT* out = static_cast<OutT*>(a.out) + orow * D;
+#pragma unroll
+  for (int e = 0; e < DPL; ++e) out[lane + 64 * e] = (OutT)(acc[e] * inv);
+  if (a.lse && lane == 0) a.lse[orow] = l > 0.f ? (mx + __log2f(l)) * kLn2 : -INFINITY;
+}
+
+// ---------------------------------------------------------------------------
+// Host-side planning and launch.
+// ---------------------------------------------------------------------------
+static int ceil_div(long long a, long long b) { return (int)((a + b - 1) / b); }
+
+AttnPlan plan_attention(int32_t B, int32_t Hkv, int32_t M, int32_t D, int32_t n_keys_max,
+                        spec_dtype_t dtype, int32_t num_splits, bool window) {
+  AttnPlan p{};
+  const bool mfma = dtype == SPEC_BF16;
+  p.slice_rows = mfma ? (M <= 16 ? 16 : 32) : kValuSlice;
+  p.n_qs = ceil_div(M, p.slice_rows);
+  const long long units = (long long)B * Hkv;
+  const int chunks = ceil_div(n_keys_max, kChunk);
+  if (num_splits > 0) {
+    p.n_splits = num_splits;
+  } else {
+    // Aim for about four work-groups per CU (256 CUs) so the HBM stream has
+    // enough waves in flight, but give every wave at least one chunk.
+    const long long target = window ? 512 : 1024;
+    long long s = (target + units * p.n_qs - 1) / (units * p.n_qs);
+    long long smax = mfma ? (chunks + kWaves - 1) / kWaves : chunks;
+    if (s > smax) s = smax;
+    if (s < 1) s = 1;
+    p.n_splits = (int)s;
+  }
+  const long long tiles = units * p.n_splits;
+  p.grid = (int)(p.n_qs == 1 ? tiles : ((tiles + 7) / 8) * 8 * p.n_qs);
+  const size_t parts = (size_t)tiles * p.n_qs;
+  p.ws_o_bytes = ((parts * p.slice_rows * D * sizeof(float)) + 255) & ~(size_t)255;
+  p.ws_ml_bytes = ((parts * p.slice_rows * 2 * sizeof(float)) + 255) & ~(size_t)255;
+  p.ws_bytes = p.ws_o_bytes + p.ws_ml_bytes;
+  return p;
+}
+
+template <bool WINDOW>
+static hipError_t launch_split(const AttnArgs& a, spec_dtype_t dtype, hipStream_t stream) {
+  dim3 grid(a.grid), block(kThreads);
+  if (dtype == SPEC_BF16) {
+    if (a.D == 128) {
+      if (a.slice_rows == 16)
+        hipLaunchKernelGGL((attn_split_mfma<128, 1, WINDOW>), grid, block, 0, stream, a);
+      else
+        hipLaunchKernelGGL((attn_split_mfma<128, 2, WINDOW>), grid, block, 0, stream, a);
+    } else {
+      if (a.slice_rows == 16)
+        hipLaunchKernelGGL((attn_split_mfma<64, 1, WINDOW>), grid, block, 0, stream, a);
+      else
+        hipLaunchKernelGGL((attn_split_mfma<64, 2, WINDOW>), grid, block, 0, stream, a);
+    }
+  } else {
+    if (a.D == 128)
+      hipLaunchKernelGGL((attn_split_valu<128, WINDOW>), grid, block, 0, stream, a);
+    else
+      hipLaunchKernelGGL((attn_split_valu<64, WINDOW>), grid, block, 0, stream, a);
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_attention(const AttnArgs& a, bool window, spec_dtype_t dtype, void* out,
+                            float* lse, hipStream_t stream) {
+  hipError_t e = window ? launch_split<true>(a, dtype, stream) : launch_split<false>(a, dtype, stream);
+  if (e != hipSuccess) return e;
+  MergeArgs m;
+  m.ws_o = a.ws_o;
+  m.ws_ml = a.ws_ml;
+  m.out = out;
+  m.lse = lse;
+  m.B = a.B;
+  m.Hq = a.Hq;
+  m.Hkv = a.Hkv;
+  m.g = a.g;
+  m.n_q = a.n_q;
+  m.D = a.D;
+  m.M = a.M;
+  m.slice_rows = a.slice_rows;
+  m.n_qs = a.n_qs;
+  m.n_splits = a.n_splits;
+  const long long rows = (long long)a.B * a.Hkv * a.M;
+  dim3 grid((unsigned)((rows + 3) / 4)), block(256);
+  if (dtype == SPEC_BF16) {
+    if (a.D == 128)
+      hipLaunchKernelGGL((attn_merge<128, __bf16>), grid, block, 0, stream, m);
+    else
+      hipLaunchKernelGGL((attn_merge<64, __bf16>), grid, block, 0, stream, m);
+  } else {
+    if (a.D == 128)
+      hipLaunchKernelGGL((attn_merge<128, float>), grid, block, 0, stream, m);
+    else
+      hipLaunchKernelGGL((attn_merge<64, float>), grid, block, 0, stream, m);
+  }
+  return hipGetLastError();
+}
+
+}  // namespace specv

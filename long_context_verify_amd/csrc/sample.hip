@@ -1,0 +1,485 @@
+// sample.hip -- the speculative-sampling tail on gfx950.
+//
+// What is computed ("Guide to MagicDec", section 2 and its verifier code;
+// "Speculative Decoding & Medusa Architecture", section 2; "Speculative
+// Decoding in LLM Serving Systems", section "Accepting and rejecting"):
+// per sequence, each drafted token x at node c is tested against
+// min(1, p_target(x) / p_draft(x)) taken at c's parent; the walk from the
+// root keeps the accepted prefix; at the stop node one token is drawn from
+// the normalised max(p_target - p_draft, 0) (after a rejection) or from
+// p_target (when the walk ends at a leaf: the bonus token).
+//
+// Two kernels:
+//
+//   sample_stats      grid (vocab chunks, 2N rows, B).  Streams the logits
+//                     once (every target row and the draft rows of nodes that
+//                     have children) and writes per-chunk (max, sum of
+//                     exp(x - max)); fp32 inside a thread, fp64 across.
+//   sample_resolve    grid (groups, B).  Every work-group of a sequence first
+//                     re-derives the same decision (fp64 log-normalisers, one
+//                     Philox uniform per node, the walk) -- a few hundred
+//                     scalars -- then computes the residual (or target) mass
+//                     of its share of 1024-id race chunks of the stop row.  The
+//                     last work-group of the sequence to finish (device-scope
+//                     counter) runs the two-level exponential race in fp64 and
+//                     writes the outputs.
+//
+// Randomness: Philox4x32-10 (Salmon, Moraes, Dror, Shaw, SC'11: four 32-bit
+// counter words, two key words, ten rounds of two 32x32->64 multiplies with
+// the published multipliers and Weyl key bumps), uniform
+// U = (2 (w >> 9) + 1) 2^-24.  Counters:
+//   accept test of node c:      (c, 0, b, 4*offset + 0), word 0
+//   race over chunks at row r:  (chunk, r, b, 4*offset + 2), word 0
+//   race over ids in a chunk:   (id / 4, r, b, 4*offset + 3), word id % 4
+
+#include <hip/hip_runtime.h>
+
+#include "spec_common.hpp"
+#include "spec_internal.hpp"
+
+namespace specv {
+
+constexpr int kSampleThreads = 256;
+constexpr int kRaceChunk = 1024;
+constexpr int kStatsChunk = 8192;   // ids per stats work-group (32 per thread)
+
+__device__ __forceinline__ void philox4x32_10(uint32_t& c0, uint32_t& c1, uint32_t& c2,
+                                              uint32_t& c3, uint32_t k0, uint32_t k1) {
+#pragma unroll
+  for (int round = 0; round < 10; ++round) {
+    if (round) {
+      k0 += 0x9E3779B9u;
+      k1 += 0xBB67AE85u;
+    }
+    const uint64_t p0 = (uint64_t)0xD2511F53u * c0;
+    const uint64_t p1 = (uint64_t)0xCD9E8D57u * c2;
+    const uint32_t n0 = (uint32_t)(p1 >> 32) ^ c1 ^ k0;
+    const uint32_t n2 = (uint32_t)(p0 >> 32) ^ c3 ^ k1;
+    c1 = (uint32_t)p1;
+    c3 = (uint32_t)p0;
+    c0 = n0;
+    c2 = n2;
+  }
+}
+
+__device__ __forceinline__ double uniform24(uint32_t w) {
+  return ((double)(w >> 9) * 2.0 + 1.0) * 5.9604644775390625e-08;  // 2^-24
+}
+
+__device__ __forceinline__ int parent_of(const SampleArgs& a, int b, int c) {
+  if (!a.parent) return c - 1;
+  return a.parent[(size_t)b * a.parent_stride + c];
+}
+
+// Block-wide reductions (256 threads = 4 waves) through a small LDS scratch.
+__device__ __forceinline__ float block_max(float v, float* red) {
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) v = fmaxf(v, __shfl_xor(v, off));
+  const int w = threadIdx.x >> 6;
+  __syncthreads();
+  if ((threadIdx.x & 63) == 0) red[w] = v;
+  __syncthreads();
+  return fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
+}
+
+__device__ __forceinline__ double block_sum(double v, double* red) {
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) v += __shfl_xor(v, off);
+  const int w = threadIdx.x >> 6;
+  __syncthreads();
+  if ((threadIdx.x & 63) == 0) red[w] = v;
+  __syncthreads();
+  return (red[0] + red[1]) + (red[2] + red[3]);
+}
+
+// Arg-max of (score, index) with ties to the lowest index.
+__device__ __forceinline__ void better(double& s, int& i, double s2, int i2) {
+  if (s2 > s || (s2 == s && i2 < i)) {
+    s = s2;
+    i = i2;
+  }
+}
+__device__ __forceinline__ void block_argmax(double& s, int& i, double* reds, int* redi) {
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) {
+    const double s2 = __shfl_xor(s, off);
+    const int i2 = __shfl_xor(i, off);
+    better(s, i, s2, i2);
+  }
+  const int w = threadIdx.x >> 6;
+  __syncthreads();
+  if ((threadIdx.x & 63) == 0) {
+    reds[w] = s;
+    redi[w] = i;
+  }
+  __syncthreads();
+  s = reds[0];
+  i = redi[0];
+#pragma unroll
+  for (int k = 1; k < 4; ++k) better(s, i, reds[k], redi[k]);
+}
+
+// ---------------------------------------------------------------------------
+// Row statistics.
+// ---------------------------------------------------------------------------
+template <bool VEC4>
+__global__ __launch_bounds__(kSampleThreads) void sample_stats(SampleArgs a) {
+  __shared__ float redf[4];
+  __shared__ double redd[4];
+  const int chunk = blockIdx.x, rowsel = blockIdx.y, b = blockIdx.z;
+  if (chunk == 0 && rowsel == 0 && threadIdx.x == 0) a.counters[b] = 0;
+  const int kind = rowsel >= a.N;  // 0: target row, 1: draft row
+  const int u = rowsel - kind * a.N;
+  if (kind) {
+    // Draft rows are needed only at nodes that have children.
+    int has = 0;
+    for (int c = 1 + threadIdx.x; c < a.N; c += kSampleThreads) has |= parent_of(a, b, c) == u;
+    if (!__syncthreads_or(has)) return;
+  }
+  const float* row = (kind ? a.draft : a.target) + ((size_t)b * a.N + u) * a.V;
+  const int x0 = chunk * a.vchunk;
+  constexpr int PER = kStatsChunk / kSampleThreads;  // 32
+  float x[PER];
+  if (VEC4) {
+    const f32x4* row4 = reinterpret_cast<const f32x4*>(row);
+#pragma unroll
+    for (int i = 0; i < PER / 4; ++i) {
+      const int e = x0 + 4 * (threadIdx.x + kSampleThreads * i);
+      f32x4 v = {-INFINITY, -INFINITY, -INFINITY, -INFINITY};
+      if (e < a.V) v = row4[e >> 2];   // V % 4 == 0: a vector is wholly in or out
+#pragma unroll
+      for (int k = 0; k < 4; ++k) x[4 * i + k] = v[k];
+    }
+  } else {
+#pragma unroll
+    for (int i = 0; i < PER; ++i) {
+      const int e = x0 + threadIdx.x + kSampleThreads * i;
+      x[i] = e < a.V ? row[e] : -INFINITY;
+    }
+  }
+  float mx = x[0];
+#pragma unroll
+  for (int i = 1; i < PER; ++i) mx = fmaxf(mx, x[i]);
+  mx = block_max(mx, redf);
+  float s = 0.f;
+  if (mx != -INFINITY) {
+#pragma unroll
+    for (int i = 0; i < PER; ++i) s += fast_exp2((x[i] - mx) * kLog2e);
+  }
+  const double tot = block_sum((double)s, redd);
+  if (threadIdx.x == 0) {
+    const size_t o = ((size_t)b * 2 * a.N + rowsel) * a.n_vchunks + chunk;
+    a.part_m[o] = mx;
+    a.part_s[o] = tot;
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Decision, residual masses and the race.
+// ---------------------------------------------------------------------------
+struct RowStat {
+  float m;     // row max
+  double s;    // sum exp(x - m)
+};
+
+__device__ __forceinline__ RowStat combine_row(const SampleArgs& a, int b, int rowsel) {
+  const size_t o = ((size_t)b * 2 * a.N + rowsel) * a.n_vchunks;
+  float m = -INFINITY;
+  for (int k = 0; k < a.n_vchunks; ++k) m = fmaxf(m, a.part_m[o + k]);
+  double s = 0.0;
+  if (m != -INFINITY)
+    for (int k = 0; k < a.n_vchunks; ++k) {
+      const float mk = a.part_m[o + k];
+      if (mk != -INFINITY) s += a.part_s[o + k] * exp((double)mk - (double)m);
+    }
+  return RowStat{m, s};
+}
+
+template <bool VEC4>
+__global__ __launch_bounds__(kSampleThreads) void sample_resolve(SampleArgs a) {
+  __shared__ float st_m[2][SPEC_MAX_SAMPLE_NODES];
+  __shared__ double st_lz[2][SPEC_MAX_SAMPLE_NODES];   // log normaliser per row
+  __shared__ double st_s[2][SPEC_MAX_SAMPLE_NODES];
+  __shared__ uint8_t has_child[SPEC_MAX_SAMPLE_NODES];
+  __shared__ uint8_t acc[SPEC_MAX_SAMPLE_NODES];
+  __shared__ int path[SPEC_MAX_SAMPLE_NODES];
+  __shared__ int s_len, s_bad, s_last, s_fallback;
+  __shared__ double redd[4];
+  __shared__ int redi[4];
+
+  const int grp = blockIdx.x, b = blockIdx.y;
+  const int N = a.N, V = a.V;
+  const int tid = threadIdx.x;
+
+  // ---- decision (identical in every work-group of the sequence) ----
+  if (tid == 0) {
+    s_bad = 0;
+    s_fallback = 0;
+  }
+  for (int u = tid; u < N; u += kSampleThreads) has_child[u] = 0;
+  __syncthreads();
+  for (int c = 1 + tid; c < N; c += kSampleThreads) {
+    const int p = parent_of(a, b, c);
+    if (p < 0 || p >= c) {
+      s_bad = 1;
+    } else {
+      has_child[p] = 1;
+    }
+  }
+  if (tid == 0 && a.parent && parent_of(a, b, 0) != -1) s_bad = 1;
+  __syncthreads();
+  const bool bad_tree = s_bad != 0;
+  for (int u = tid; u < N; u += kSampleThreads) {
+    const RowStat t = combine_row(a, b, u);
+    st_m[0][u] = t.m;
+    st_s[0][u] = t.s;
+    st_lz[0][u] = (double)t.m + log(t.s);
+    if (!bad_tree && has_child[u]) {
+      const RowStat d = combine_row(a, b, N + u);
+      st_m[1][u] = d.m;
+      st_s[1][u] = d.s;
+      st_lz[1][u] = (double)d.m + log(d.s);
+    }
+  }
+  __syncthreads();
+  if (tid == 0) acc[0] = 1;
+  for (int c = 1 + tid; c < N; c += kSampleThreads) {
+    acc[c] = 0;
+    if (bad_tree) continue;
+    const int p = parent_of(a, b, c);
+    const int x = a.tokens[(size_t)b * N + c];
+    if (x < 0 || x >= V) {
+      s_bad = 2;
+      continue;
+    }
+    const float tl = a.target[((size_t)b * N + p) * V + x];
+    const float dl = a.draft[((size_t)b * N + p) * V + x];
+    double ratio;
+    if (dl == -INFINITY)
+      ratio = (tl == -INFINITY) ? 0.0 : INFINITY;
+    else
+      ratio = exp(((double)tl - st_lz[0][p]) - ((double)dl - st_lz[1][p]));
+    uint32_t c0 = (uint32_t)c, c1 = 0u, c2 = (uint32_t)b, c3 = a.ctr3_base + 0u;
+    philox4x32_10(c0, c1, c2, c3, a.key0, a.key1);
+    acc[c] = uniform24(c0) < ratio;
+  }
+  __syncthreads();
+  const bool bad = s_bad != 0;
+  // Walk from the root: at each node take the first child, in index order,
+  // that passed its test.  Children have larger indices than their parent.
+  if (tid < kWave) {
+    int cur = 0, len = 1;
+    if (tid == 0) path[0] = 0;
+    if (!bad) {
+      while (true) {
+        int nxt = -1;
+        for (int base = cur + 1; base < N && nxt < 0; base += kWave) {
+          const int c = base + tid;
+          const bool hit = c < N && acc[c] && parent_of(a, b, c) == cur;
+          const unsigned long long ball = __ballot(hit);
+          if (ball) nxt = base + __ffsll((long long)ball) - 1;
+        }
+        if (nxt < 0) break;
+        if (tid == 0) path[len] = nxt;
+        ++len;
+        cur = nxt;
+      }
+    }
+    if (tid == 0) s_len = len;
+  }
+  __syncthreads();
+  const int len = s_len;
+  const int r = path[len - 1];               // stop row
+  const bool residual = has_child[r] != 0;   // rejection happened at r's children
+
+  // ---- residual (or target) mass of this group's race chunks ----
+  const float* trow = a.target + ((size_t)b * N + r) * V;
+  const float* drow = a.draft + ((size_t)b * N + r) * V;
+  const float tm = st_m[0][r];
+  const float tinv = (float)(1.0 / st_s[0][r]);
+  const float dm = residual ? st_m[1][r] : 0.f;
+  const float dinv = residual ? (float)(1.0 / st_s[1][r]) : 0.f;
+  const int q0 = (int)((long long)a.n_race * grp / a.n_groups);
+  const int q1 = (int)((long long)a.n_race * (grp + 1) / a.n_groups);
+  for (int q = q0; q < q1; ++q) {
+    float sw = 0.f, spt = 0.f;
+    if (!bad) {
+      const int e0 = q * kRaceChunk + 4 * tid;
+      float tv[4], dv[4];
+      if (VEC4) {
+        f32x4 t4 = {-INFINITY, -INFINITY, -INFINITY, -INFINITY}, d4 = t4;
+        if (e0 < V) {
+          t4 = reinterpret_cast<const f32x4*>(trow)[e0 >> 2];
+          if (residual) d4 = reinterpret_cast<const f32x4*>(drow)[e0 >> 2];
+        }
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+          tv[k] = t4[k];
+          dv[k] = d4[k];
+        }
+      } else {
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+          const int e = e0 + k;
+          tv[k] = e < V ? trow[e] : -INFINITY;
+          dv[k] = (e < V && residual) ? drow[e] : -INFINITY;
+        }
+      }
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        const float pt = fast_exp2((tv[k] - tm) * kLog2e) * tinv;
+        const float pd = residual ? fast_exp2((dv[k] - dm) * kLog2e) * dinv : 0.f;
+        spt += pt;
+        sw += fmaxf(pt - pd, 0.f);
+      }
+    }
+    const double tw = block_sum((double)sw, redd);
+    const double tp = block_sum((double)spt, redd);
+    if (tid == 0) {
+      double* o = a.race_w + ((size_t)b * a.n_race + q) * 2;
+      o[0] = tw;
+      o[1] = tp;
+    }
+  }
+
+  // ---- last work-group of the sequence finishes the draw ----
+  __threadfence();
+  __syncthreads();
+  if (tid == 0) s_last = atomicAdd(&a.counters[b], 1) == a.n_groups - 1;
+  __syncthreads();
+  if (!s_last) return;
+  __threadfence();
+
+  int* out_tok = a.out_tokens + (size_t)b * N;
+  if (bad) {
+    for (int c = tid; c < N; c += kSampleThreads) {
+      out_tok[c] = -1;
+      if (a.out_path) a.out_path[(size_t)b * N + c] = -1;
+      if (a.out_accept) a.out_accept[(size_t)b * N + c] = 0;
+    }
+    if (tid == 0) {
+      a.out_count[b] = 0;
+      report_error(a.dev_err, s_bad == 2 ? SPEC_DEVERR_TOKEN : SPEC_DEVERR_PARENT);
+    }
+    return;
+  }
+
+  // Level 1: chunks race with score W_c / E1_c.
+  const volatile double* rw = a.race_w + (size_t)b * a.n_race * 2;
+  double tot = 0.0;
+  for (int q = tid; q < a.n_race; q += kSampleThreads) tot += rw[2 * q];
+  tot = block_sum(tot, redd);
+  const int col = (residual && tot <= 0.0) ? 1 : (residual ? 0 : 1);
+  if (tid == 0) s_fallback = residual && tot <= 0.0;
+  double best = -1.0;
+  int bidx = 0x7fffffff;
+  for (int q = tid; q < a.n_race; q += kSampleThreads) {
+    const double W = rw[2 * q + col];
+    if (W > 0.0) {
+      uint32_t c0 = (uint32_t)q, c1 = (uint32_t)r, c2 = (uint32_t)b, c3 = a.ctr3_base + 2u;
+      philox4x32_10(c0, c1, c2, c3, a.key0, a.key1);
+      better(best, bidx, W / -log(uniform24(c0)), q);
+    }
+  }
+  block_argmax(best, bidx, redd, redi);
+  const int cstar = bidx < a.n_race ? bidx : 0;
+  __syncthreads();
+  const bool use_resid = residual && !s_fallback;
+
+  // Level 2: ids of the winning chunk race with score w_x / E2_x (fp64 weights).
+  double best2 = -1.0;
+  int bidx2 = 0x7fffffff;
+  {
+    const int e0 = cstar * kRaceChunk + 4 * tid;
+    uint32_t c0 = (uint32_t)(e0 >> 2), c1 = (uint32_t)r, c2 = (uint32_t)b, c3 = a.ctr3_base + 3u;
+    philox4x32_10(c0, c1, c2, c3, a.key0, a.key1);
+    const uint32_t words[4] = {c0, c1, c2, c3};
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      const int e = e0 + k;
+      if (e < V) {
+        const double pt = exp((double)trow[e] - st_lz[0][r]);
+        double w = pt;
+        if (use_resid) {
+          const double pd = exp((double)drow[e] - st_lz[1][r]);
+          w = pt - pd > 0.0 ? pt - pd : 0.0;
+        }
+        if (w > 0.0) better(best2, bidx2, w / -log(uniform24(words[k])), e);
+      }
+    }
+  }
+  block_argmax(best2, bidx2, redd, redi);
+  if (bidx2 >= V) {
+    // The fp32 chunk mass was positive but no id of the chunk has a positive
+    // fp64 residual (a cancellation at the 1e-7 level): draw from the target.
+    best2 = -1.0;
+    bidx2 = 0x7fffffff;
+    const int e0 = cstar * kRaceChunk + 4 * tid;
+    uint32_t c0 = (uint32_t)(e0 >> 2), c1 = (uint32_t)r, c2 = (uint32_t)b, c3 = a.ctr3_base + 3u;
+    philox4x32_10(c0, c1, c2, c3, a.key0, a.key1);
+    const uint32_t words[4] = {c0, c1, c2, c3};
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      const int e = e0 + k;
+      if (e < V) {
+        const double pt = exp((double)trow[e] - st_lz[0][r]);
+        if (pt > 0.0) better(best2, bidx2, pt / -log(uniform24(words[k])), e);
+      }
+    }
+    block_argmax(best2, bidx2, redd, redi);
+  }
+  const int y = bidx2 < V ? bidx2 : 0;
+
+  for (int c = tid; c < N; c += kSampleThreads) {
+    int tokv = -1, pv = -1;
+    if (c < len - 1) tokv = a.tokens[(size_t)b * N + path[c + 1]];
+    else if (c == len - 1) tokv = y;
+    if (c < len) pv = path[c];
+    out_tok[c] = tokv;
+    if (a.out_path) a.out_path[(size_t)b * N + c] = pv;
+    if (a.out_accept) a.out_accept[(size_t)b * N + c] = acc[c];
+  }
+  if (tid == 0) a.out_count[b] = len;
+}
+
+// ---------------------------------------------------------------------------
+// Host-side planning and launch.
+// ---------------------------------------------------------------------------
+static size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+SamplePlan plan_sample(int32_t B, int32_t N, int32_t V) {
+  SamplePlan p{};
+  p.vchunk = kStatsChunk;
+  p.n_vchunks = (V + kStatsChunk - 1) / kStatsChunk;
+  p.n_race = (V + kRaceChunk - 1) / kRaceChunk;
+  long long groups = (1024 + (long long)B - 1) / (B > 0 ? B : 1);
+  if (groups > p.n_race) groups = p.n_race;
+  if (groups < 1) groups = 1;
+  p.n_groups = (int)groups;
+  const size_t rows = (size_t)B * 2 * N * p.n_vchunks;
+  p.off_m = 0;
+  p.off_s = align256(p.off_m + rows * sizeof(float));
+  p.off_w = align256(p.off_s + rows * sizeof(double));
+  p.off_cnt = align256(p.off_w + (size_t)B * p.n_race * 2 * sizeof(double));
+  p.bytes = align256(p.off_cnt + (size_t)B * sizeof(int32_t));
+  return p;
+}
+
+hipError_t launch_sample(const SampleArgs& a, hipStream_t stream) {
+  const bool vec4 = (a.V % 4) == 0;
+  dim3 g1(a.n_vchunks, 2 * a.N, a.B), blk(kSampleThreads);
+  if (vec4)
+    hipLaunchKernelGGL(sample_stats<true>, g1, blk, 0, stream, a);
+  else
+    hipLaunchKernelGGL(sample_stats<false>, g1, blk, 0, stream, a);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  dim3 g2(a.n_groups, a.B);
+  if (vec4)
+    hipLaunchKernelGGL(sample_resolve<true>, g2, blk, 0, stream, a);
+  else
+    hipLaunchKernelGGL(sample_resolve<false>, g2, blk, 0, stream, a);
+  return hipGetLastError();
+}
+
+}  // namespace specv

@@ -1,0 +1,96 @@
+// spec_internal.hpp -- host-side launch plans shared by the C ABI and the kernel files.
+#pragma once
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include <hip/hip_runtime_api.h>
+
+#include "spec_verify.h"
+
+namespace specv {
+
+// Everything one split-K attention launch needs.  Built and checked on the
+// host by the ABI layer; the kernels only read it.
+struct AttnArgs {
+  const void* q;          // [B, Hq, n_q, D]
+  const void* k;          // verify: K cache [B, Hkv, L_cap, D]; window: ring [B, Hkv, W, D]
+  const void* v;
+  const void* k_sink;     // window only: [B, Hkv, S, D]
+  const void* v_sink;
+  const void* k_new;      // window only, nullable: [B, Hkv, 1, D]
+  const void* v_new;
+  void* k_ring_w;         // window fused append destinations (same buffers as k/v, k_sink/v_sink)
+  void* v_ring_w;
+  void* k_sink_w;
+  void* v_sink_w;
+  const int32_t* lens;    // verify: kv_len (nullable); window: total_len
+  const int32_t* parent;  // verify: nullable parent array
+  int32_t parent_stride;
+  float* ws_o;            // [n_partials][slice_rows][D]
+  float* ws_ml;           // [n_partials][slice_rows][2]  (running max in log2 units, sum)
+  int32_t B, Hq, Hkv, g, n_q, D, L_cap, M;
+  int32_t W, S;           // window geometry
+  int32_t slice_rows;     // query rows per work-group slice
+  int32_t n_qs;           // slices per (sequence, kv head)
+  int32_t n_splits;       // key-range splits per (sequence, kv head)
+  int32_t n_tiles;        // B * Hkv * n_splits
+  int32_t grid;           // work-groups launched
+  float scale_log2;       // softmax scale * log2(e)
+  int32_t* dev_err;
+};
+
+struct MergeArgs {
+  const float* ws_o;
+  const float* ws_ml;
+  void* out;
+  float* lse;
+  int32_t B, Hq, Hkv, g, n_q, D, M;
+  int32_t slice_rows, n_qs, n_splits;
+};
+
+struct AttnPlan {
+  int32_t slice_rows, n_qs, n_splits, grid;
+  size_t ws_o_bytes, ws_ml_bytes, ws_bytes;
+};
+
+AttnPlan plan_attention(int32_t B, int32_t Hkv, int32_t M, int32_t D, int32_t n_keys_max,
+                        spec_dtype_t dtype, int32_t num_splits, bool window);
+
+hipError_t launch_attention(const AttnArgs& a, bool window, spec_dtype_t dtype, void* out,
+                            float* lse, hipStream_t stream);
+
+struct SampleArgs {
+  const float* target;
+  const float* draft;
+  const int32_t* tokens;
+  const int32_t* parent;
+  int32_t parent_stride;
+  int32_t B, N, V;
+  uint32_t key0, key1;
+  uint32_t ctr3_base;      // 4 * offset
+  int32_t* out_tokens;
+  int32_t* out_count;
+  int32_t* out_path;
+  uint8_t* out_accept;
+  // workspace views
+  float* part_m;           // [B][2N][n_vchunks]
+  double* part_s;          // [B][2N][n_vchunks]
+  double* race_w;          // [B][n_race][2]  (residual mass, target mass) per race chunk
+  int32_t* counters;       // [B]
+  int32_t n_vchunks;       // stats chunks per row
+  int32_t vchunk;          // ids per stats chunk
+  int32_t n_race;          // race chunks per row (1024 ids each)
+  int32_t n_groups;        // resample work-groups per sequence
+  int32_t* dev_err;
+};
+
+struct SamplePlan {
+  int32_t n_vchunks, vchunk, n_race, n_groups;
+  size_t off_m, off_s, off_w, off_cnt, bytes;
+};
+
+SamplePlan plan_sample(int32_t B, int32_t N, int32_t V);
+hipError_t launch_sample(const SampleArgs& a, hipStream_t stream);
+
+}  // namespace specv

@@ -1,0 +1,127 @@
+"""Host-side checks of the C-ABI library (no GPU needed).
+
+The library must load, export every function include/spec_verify.h declares,
+and reject bad arguments on the host before any HIP call (so these run on a
+machine without a device).  Fake but aligned pointer values are used where a
+call is expected to fail validation; no call here reaches a launch.
+"""
+
+import ctypes
+import os
+
+import numpy as np
+import pytest
+
+import long_context_verify_amd as L
+from long_context_verify_amd import api
+
+OK, INVALID, UNSUPPORTED, BAD_TREE, MISALIGNED, WORKSPACE = 0, 1, 2, 3, 4, 5
+P = ctypes.c_void_p(0x10000)          # aligned fake device pointer (never dereferenced)
+P_ODD = ctypes.c_void_p(0x10004)      # 4-byte aligned only
+NULL = None
+
+
+def test_library_file_exists_and_loads():
+    assert os.path.exists(api.LIB_PATH), "run __graft_entry__.build() first"
+    assert L.lib() is not None
+
+
+def test_every_declared_function_is_exported():
+    names = api.declared_functions()
+    assert {"spec_verify_attention", "spec_window_attention", "spec_sample"} <= set(names)
+    handle = ctypes.CDLL(api.LIB_PATH)
+    for n in names:
+        assert hasattr(handle, n), n
+    assert set(names) == set(api._SIGNATURES)
+
+
+def test_status_strings():
+    assert L.status_str(0) == "SPEC_OK"
+    assert L.status_str(4) == "SPEC_ERR_MISALIGNED"
+    assert L.status_str(99) == "SPEC_ERR_UNKNOWN"
+
+
+def _verify(q=P, k=P, v=P, out=P, lse=NULL, kv_len=NULL, parent=NULL, pstride=0, B=2, Hq=8,
+            Hkv=2, n_q=5, D=128, L_cap=1000, dtype=1, scale=0.0, splits=0, ws=P, ws_bytes=0,
+            err=NULL):
+    return L.lib().spec_verify_attention(q, k, v, out, lse, kv_len, parent, pstride, B, Hq, Hkv,
+                                         n_q, D, L_cap, dtype, scale, splits, ws, ws_bytes, err,
+                                         NULL)
+
+
+def test_verify_attention_argument_checks():
+    assert _verify(B=0) == OK                      # empty batch: nothing to do
+    assert _verify(Hq=7) == INVALID                # Hq % Hkv != 0
+    assert _verify(D=96) == UNSUPPORTED
+    assert _verify(n_q=65) == UNSUPPORTED
+    assert _verify(n_q=0) == INVALID
+    assert _verify(L_cap=4) == INVALID             # L_cap < n_q
+    assert _verify(dtype=5) == INVALID
+    assert _verify(splits=-1) == INVALID
+    assert _verify(parent=P, pstride=3) == INVALID
+    assert _verify(q=P_ODD) == MISALIGNED
+    assert _verify(k=NULL) == MISALIGNED
+    assert _verify(ws_bytes=16) == WORKSPACE       # far below the planned workspace
+    assert _verify(ws=P_ODD, ws_bytes=1 << 40) == WORKSPACE
+
+
+def test_workspace_queries():
+    import torch
+    bf16 = torch.bfloat16
+    a = L.verify_attention_workspace_bytes(8, 32, 8, 5, 128, 32768, bf16)
+    b = L.verify_attention_workspace_bytes(8, 32, 8, 5, 128, 32768, bf16, num_splits=1)
+    assert a > b > 0 and a % 256 == 0
+    assert L.verify_attention_workspace_bytes(8, 32, 8, 5, 96, 32768, bf16) == 0
+    assert L.verify_attention_auto_splits(8, 32, 8, 5, 128, 32768, bf16) >= 1
+    assert L.window_attention_workspace_bytes(8, 32, 8, 128, 512, 4, bf16) > 0
+    assert L.sample_workspace_bytes(8, 5, 128256) > 0
+    assert L.sample_workspace_bytes(8, 0, 128256) == 0
+
+
+def _window(B=2, Hq=8, Hkv=2, D=128, W=64, S=4, k_new=NULL, v_new=NULL, k_sink=P, ws_bytes=0,
+            total_len=P, dtype=1):
+    return L.lib().spec_window_attention(P, P, P, k_sink, P, k_new, v_new, total_len, P, NULL, B,
+                                         Hq, Hkv, D, W, S, dtype, 0.0, 0, P, ws_bytes, NULL, NULL)
+
+
+def test_window_attention_argument_checks():
+    assert _window(B=0) == OK
+    assert _window(W=0) == INVALID
+    assert _window(S=-1) == INVALID
+    assert _window(D=32) == UNSUPPORTED
+    assert _window(k_new=P) == INVALID             # k_new without v_new
+    assert _window(k_sink=NULL) == MISALIGNED      # sinks needed when S > 0
+    assert _window(total_len=NULL) == MISALIGNED
+    assert _window() == WORKSPACE
+
+
+def _sample(B=2, N=5, V=1000, offset=0, parent=NULL, pstride=0, tgt=P, ws_bytes=0):
+    return L.lib().spec_sample(tgt, P, P, parent, pstride, B, N, V, 1, offset, P, P, NULL, NULL, P,
+                               ws_bytes, NULL, NULL)
+
+
+def test_sample_argument_checks():
+    assert _sample(B=0) == OK
+    assert _sample(N=0) == INVALID
+    assert _sample(N=257) == UNSUPPORTED
+    assert _sample(V=0) == INVALID
+    assert _sample(offset=1 << 30) == INVALID
+    assert _sample(parent=P, pstride=4) == INVALID
+    assert _sample(tgt=P_ODD) == MISALIGNED
+    assert _sample() == WORKSPACE
+
+
+@pytest.mark.parametrize("parent,single,expect", [
+    ([-1, 0, 0, 1, 3], True, OK),
+    ([-1, 0, 2], True, BAD_TREE),          # parent not before child
+    ([-1, -1, 0], True, BAD_TREE),         # second root
+    ([-1, -1, 0], False, OK),              # forests are fine for attention
+    ([0, 0], False, BAD_TREE),             # node 0 cannot have a parent
+    ([-1, -2], False, BAD_TREE),
+])
+def test_validate_tree(parent, single, expect):
+    assert L.validate_tree(np.array(parent), single) == expect
+
+
+def test_validate_tree_null():
+    assert L.lib().spec_validate_tree(NULL, 3, 1) == INVALID

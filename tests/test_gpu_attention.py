@@ -1,0 +1,169 @@
+"""GPU parity of spec_verify_attention against the fp64 oracle (MI355X).
+
+Tolerances (max abs): 1e-5 for fp32 inputs, 2e-2 for bf16 inputs on the
+outputs; lse 1e-5 / 1e-2; bf16 also holds a 1e-2 relative Frobenius error.
+"""
+
+import numpy as np
+import pytest
+import torch
+
+from oracle.attention import verify_attention as oracle_verify
+from tests.gpu_util import assert_attention_close, oracle_unit, say
+from workloads import CONFIGS, make_attention_inputs, random_tree
+
+pytestmark = pytest.mark.gpu
+
+DEV = "cuda"
+
+
+def _lib():
+    import long_context_verify_amd as L
+    return L
+
+
+def _gpu_and_oracle(x, parent=None, num_splits=0, scale=0.0):
+    L = _lib()
+    out, lse = L.verify_attention(x["q"], x["k"], x["v"], x["kv_len"], parent=parent,
+                                  num_splits=num_splits, scale=scale)
+    torch.cuda.synchronize()
+    o_ref, l_ref = oracle_verify(x["q"], x["k"], x["v"], x["kv_len"],
+                                 None if parent is None else np.asarray(parent),
+                                 scale=scale if scale > 0 else None)
+    return out, lse, o_ref, l_ref
+
+
+CASES = [
+    # name, B, Hq, Hkv, n_q, D, L, dtype, L_cap, kv_len
+    ("tiny_chain_fp32", 1, 8, 2, 5, 64, 1024, "f32", None, None),
+    ("fp32_d128_ragged", 3, 4, 2, 5, 128, 700, "f32", 777, [700, 5, 777]),
+    ("bf16_chain_g4", 2, 32, 8, 5, 128, 4133, "bf16", None, None),
+    ("bf16_chain_g1_M6", 2, 8, 8, 6, 128, 1000, "bf16", None, None),
+    ("bf16_d64", 2, 16, 4, 4, 64, 2000, "bf16", 2100, [2000, 1999]),
+    ("bf16_g8_M32", 1, 64, 8, 4, 128, 3000, "bf16", None, None),
+    ("bf16_nq1", 2, 8, 2, 1, 128, 513, "bf16", None, None),
+    ("bf16_only_block", 2, 8, 2, 5, 128, 5, "bf16", None, None),
+    ("fp32_only_block", 1, 4, 1, 3, 64, 3, "f32", None, None),
+]
+
+
+@pytest.mark.parametrize("case", CASES, ids=[c[0] for c in CASES])
+def test_chain_parity(case):
+    name, B, Hq, Hkv, n_q, D, L, dt, L_cap, kv_len = case
+    say(f"verify chain {name}")
+    x = make_attention_inputs(B, Hq, Hkv, n_q, D, L, dtype=dt, seed=sum(map(ord, name)),
+                              device=DEV, L_cap=L_cap, kv_len=kv_len)
+    out, lse, o_ref, l_ref = _gpu_and_oracle(x)
+    assert_attention_close(out, lse, o_ref, l_ref, x["q"].dtype, name)
+
+
+@pytest.mark.parametrize("splits", [1, 3, 7, 64, 1000])
+def test_split_count_independence(splits):
+    say(f"verify splits={splits}")
+    x = make_attention_inputs(2, 16, 4, 5, 128, 3000, dtype="bf16", seed=splits, device=DEV)
+    out, lse, o_ref, l_ref = _gpu_and_oracle(x, num_splits=splits)
+    assert_attention_close(out, lse, o_ref, l_ref, torch.bfloat16, f"splits={splits}")
+
+
+@pytest.mark.parametrize("dt", ["f32", "bf16"])
+def test_tree_parity(dt):
+    say(f"verify tree 64 nodes {dt}")
+    parent = random_tree(64, seed=4321)
+    x = make_attention_inputs(2, 32, 8, 64, 128, 1024 + 64, dtype=dt, seed=77, device=DEV)
+    out, lse, o_ref, l_ref = _gpu_and_oracle(x, parent=parent)
+    assert_attention_close(out, lse, o_ref, l_ref, x["q"].dtype, f"tree {dt}")
+
+
+def test_tree_per_sequence_parent_and_forest():
+    say("verify per-sequence parents incl. forest")
+    n = 17
+    parents = np.stack([random_tree(n, max_depth=3, max_children=3, seed=5),
+                        np.full(n, -1, dtype=np.int32),
+                        np.arange(-1, n - 1, dtype=np.int32)])
+    x = make_attention_inputs(3, 8, 2, n, 128, 600, dtype="bf16", seed=8, device=DEV,
+                              kv_len=[600, 300, 17])
+    L = _lib()
+    out, lse = L.verify_attention(x["q"], x["k"], x["v"], x["kv_len"], parent=parents)
+    torch.cuda.synchronize()
+    o_ref, l_ref = oracle_verify(x["q"], x["k"], x["v"], x["kv_len"], parents)
+    assert_attention_close(out, lse, o_ref, l_ref, torch.bfloat16, "per-seq parents")
+
+
+def test_chain_parent_array_matches_null_parent():
+    say("verify explicit chain parent == NULL parent")
+    x = make_attention_inputs(2, 32, 8, 5, 128, 2048, dtype="bf16", seed=3, device=DEV)
+    L = _lib()
+    o1, l1 = L.verify_attention(x["q"], x["k"], x["v"], x["kv_len"])
+    o2, l2 = L.verify_attention(x["q"], x["k"], x["v"], x["kv_len"],
+                                parent=np.arange(-1, 4, dtype=np.int32))
+    torch.cuda.synchronize()
+    assert torch.equal(o1, o2) and torch.equal(l1, l2)
+
+
+def test_needle_keys_move_the_running_max():
+    """Keys equal to 4*q at a few positions shift the max between splits."""
+    say("verify needle stress")
+    B, Hq, Hkv, n_q, D, L = 1, 8, 2, 5, 128, 8192
+    x = make_attention_inputs(B, Hq, Hkv, n_q, D, L, dtype="bf16", seed=12, device=DEV)
+    for pos in (17, 2500, 6000, L - n_q - 1):
+        x["k"][0, :, pos] = (4.0 * x["q"][0, ::Hq // Hkv, 0].float()).to(torch.bfloat16)
+    out, lse, o_ref, l_ref = _gpu_and_oracle(x, num_splits=9)
+    assert_attention_close(out, lse, o_ref, l_ref, torch.bfloat16, "needle")
+
+
+def test_custom_scale():
+    say("verify custom scale")
+    x = make_attention_inputs(1, 8, 2, 5, 128, 999, dtype="bf16", seed=4, device=DEV)
+    out, lse, o_ref, l_ref = _gpu_and_oracle(x, scale=0.05)
+    assert_attention_close(out, lse, o_ref, l_ref, torch.bfloat16, "scale")
+
+
+def test_deterministic_bits():
+    say("verify determinism")
+    x = make_attention_inputs(4, 32, 8, 5, 128, 5000, dtype="bf16", seed=6, device=DEV)
+    L = _lib()
+    o1, l1 = L.verify_attention(x["q"], x["k"], x["v"], x["kv_len"])
+    o2, l2 = L.verify_attention(x["q"], x["k"], x["v"], x["kv_len"])
+    torch.cuda.synchronize()
+    assert torch.equal(o1, o2) and torch.equal(l1, l2)
+
+
+def test_bad_kv_len_sets_error_and_zero_output():
+    say("verify bad kv_len")
+    x = make_attention_inputs(2, 8, 2, 5, 64, 100, dtype="bf16", seed=1, device=DEV,
+                              kv_len=[100, 3])
+    err = torch.zeros(1, dtype=torch.int32, device=DEV)
+    L = _lib()
+    out, lse = L.verify_attention(x["q"], x["k"], x["v"], x["kv_len"], dev_err=err)
+    torch.cuda.synchronize()
+    assert int(err.item()) & 0x1
+    assert torch.all(out[1] == 0)
+    assert torch.all(torch.isneginf(lse[1]))
+    o_ref, l_ref = oracle_verify(x["q"][:1], x["k"][:1], x["v"][:1], [100])
+    assert_attention_close(out[:1], lse[:1], o_ref, l_ref, torch.bfloat16, "good sequence")
+
+
+FULL = ["llama8b_32k_chain", "magicdec_128k_chain", "medusa_tree64_8k", "llama70b_16k_chain_b64"]
+
+
+@pytest.mark.parametrize("name", FULL)
+def test_full_size_sampled_units(name):
+    """Whole workload on the GPU in the benchmarked launch shape; oracle on sampled units."""
+    cfg = CONFIGS[name]
+    say(f"verify full-size {name}")
+    x = make_attention_inputs(cfg.batch, cfg.hq, cfg.hkv, cfg.n_q, cfg.head_dim, cfg.kv_len,
+                              dtype=cfg.dtype, seed=cfg.seed, device=DEV)
+    parent = random_tree(cfg.n_q) if cfg.tree else None
+    L = _lib()
+    out, lse = L.verify_attention(x["q"], x["k"], x["v"], x["kv_len"], parent=parent)
+    torch.cuda.synchronize()
+    g = cfg.hq // cfg.hkv
+    rng = np.random.default_rng(cfg.seed)
+    units = {(0, 0), (cfg.batch - 1, cfg.hkv - 1)}
+    while len(units) < 4:
+        units.add((int(rng.integers(cfg.batch)), int(rng.integers(cfg.hkv))))
+    for b, hk in sorted(units):
+        o_ref, l_ref = oracle_unit(x["q"], x["k"], x["v"], x["kv_len"], parent, b, hk, g)
+        assert_attention_close(out[b:b + 1, hk * g:(hk + 1) * g], lse[b:b + 1, hk * g:(hk + 1) * g],
+                               o_ref, l_ref, torch.bfloat16, f"{name} unit {(b, hk)}")
+    assert torch.isfinite(out.float()).all()

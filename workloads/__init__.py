@@ -219,8 +219,8 @@ def make_window_inputs(B: int, Hq: int, Hkv: int, D: int, W: int, S: int,
 
     k_ring = stale_k.clone()
     v_ring = stale_v.clone()
-    k_sink = stale_sk[:, :, :S].clone() if S > 0 else stale_sk[:, :, :1].clone()
-    v_sink = stale_sv[:, :, :S].clone() if S > 0 else stale_sv[:, :, :1].clone()
+    k_sink = stale_sk[:, :, :S].clone() if S > 0 else None
+    v_sink = stale_sv[:, :, :S].clone() if S > 0 else None
     k_new = v_new = None
     if fused_append:
         k_new = torch.empty((B, Hkv, 1, D), dtype=q.dtype, device=device)

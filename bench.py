@@ -1,0 +1,357 @@
+#!/usr/bin/env python3
+"""Benchmark of one speculative verification step on one MI355X.
+
+A step is one pass of the whole hot path over one batch of synthetic input,
+shaped like an 8B-class GQA layer at 32K context (batch 8, 32 query heads,
+8 KV heads, head dim 128, bf16, gamma = 4):
+
+  1. spec_verify_attention  the gamma+1 = 5 block queries of every sequence
+                            against its 32768-token KV cache (causal chain);
+  2. spec_window_attention  one draft-step query against 4 sink tokens and a
+                            512-slot ring (the MagicDec bounded draft cache);
+  3. spec_sample            acceptance test + residual/bonus draw over a
+                            128256-token vocabulary (5 target rows, 4 draft rows
+                            per sequence).
+
+All inputs are resident in HBM before the timed region.  The printed value
+is verified draft tokens per second (batch * gamma per step).  Per-op times
+come from HIP events recorded on the stream the library launches on (torch's
+current stream).  The oracle (fp64 numpy) is timed on a bounded sample of the
+same workload on the host cores and reported as ``cpu_baseline``.
+
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
+"""
+
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+HBM_PEAK_GBPS = 8000.0      # MI355X HBM3E, vendor figure
+METRIC = "verify-attn KV GB/s (% HBM peak) + verified draft tokens/sec, 1 MI355X"
+
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+KERNEL_SOURCES = ["long_context_verify_amd/csrc/attention.hip",
+                  "long_context_verify_amd/csrc/spec_common.hpp",
+                  "long_context_verify_amd/csrc/spec_internal.hpp"]
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "verify_attn_llama8b_32k_hbm_counters.txt")
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def kernel_source_sha256() -> str:
+    import hashlib
+    h = hashlib.sha256()
+    for rel in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, rel), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()
+
+
+def recorded_traffic(workload: str):
+    """HBM bytes per launch of the verify kernel from the committed counter summary.
+
+    The summary records the counter-derived bytes and the hash of the kernel
+    sources they were taken with; if the sources changed since, the figure no
+    longer describes this kernel and None is returned.
+    """
+    try:
+        fields = {}
+        with open(TRAFFIC_FILE) as f:
+            for line in f:
+                if ":" in line and not line.startswith("#"):
+                    k, v = line.split(":", 1)
+                    fields[k.strip()] = v.strip()
+        if fields.get("workload") != workload or fields.get("source_sha256") != kernel_source_sha256():
+            return None
+        return int(fields["traffic_bytes_per_launch"])
+    except (OSError, KeyError, ValueError):
+        return None
+
+
+def parse():
+    p = argparse.ArgumentParser()
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=50)
+    p.add_argument("--warmup", type=int, default=10)
+    p.add_argument("--workload", default="llama8b_32k_chain")
+    p.add_argument("--cpu-budget", type=float, default=12.0,
+                   help="seconds of oracle work for the CPU baseline (0 disables it)")
+    p.add_argument("--copy-probe-mib", type=int, default=0,
+                   help="also run plain device copies of this many MiB (calibrates HBM "
+                        "byte counters: the copy reads and writes exactly this much)")
+    return p.parse_args()
+
+
+def build_inputs(cfg, dev):
+    from workloads import (chain_parent, make_attention_inputs, make_sample_inputs,
+                           make_window_inputs, random_tree)
+    att = make_attention_inputs(cfg.batch, cfg.hq, cfg.hkv, cfg.n_q, cfg.head_dim, cfg.kv_len,
+                                dtype=cfg.dtype, seed=cfg.seed, device=dev)
+    parent = random_tree(cfg.n_q) if cfg.tree else None
+    win = None
+    if cfg.window is not None:
+        win = make_window_inputs(cfg.batch, cfg.hq, cfg.hkv, cfg.head_dim, cfg.window, cfg.sinks,
+                                 [cfg.kv_len] * cfg.batch, dtype=cfg.dtype, seed=cfg.seed + 1,
+                                 device=dev)
+    sparent = parent if cfg.tree else None
+    smp = make_sample_inputs(cfg.batch, cfg.n_nodes, cfg.vocab, sparent, cfg.target_std,
+                             draft_noise_std=cfg.draft_noise_std, draft_std=cfg.draft_std,
+                             seed=cfg.seed + 2, device=dev)
+    return att, parent, win, smp
+
+
+def sample_rows_read(n_nodes, parent):
+    """Logit rows one sequence's sampling reads once: every target row + draft rows of internal nodes."""
+    if parent is None:
+        n_int = n_nodes - 1
+    else:
+        n_int = len(set(int(p) for p in parent[1:]))
+    return n_nodes + n_int
+
+
+def cpu_baseline(cfg, att, parent, win, smp, budget_s):
+    """Time the fp64 oracle on a bounded sample of the step and scale it to the whole step."""
+    import torch
+    from oracle.attention import verify_attention, window_attention
+    from oracle.sample import spec_sample
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:  # pragma: no cover
+        threads = 1
+    g = cfg.hq // cfg.hkv
+    units = cfg.batch * cfg.hkv
+    share = budget_s / 3.0
+    # (1) verify attention: whole (sequence, kv head) units
+    t_unit, n_unit = 0.0, 0
+    while t_unit < share and n_unit < units:
+        b, hk = divmod(n_unit, cfg.hkv)
+        q = att["q"][b:b + 1, hk * g:(hk + 1) * g].cpu()
+        k = att["k"][b:b + 1, hk:hk + 1].cpu()
+        v = att["v"][b:b + 1, hk:hk + 1].cpu()
+        t0 = time.perf_counter()
+        verify_attention(q, k, v, [cfg.kv_len], parent)
+        t_unit += time.perf_counter() - t0
+        n_unit += 1
+    t_verify = t_unit / n_unit * units
+    # (2) window attention: whole sequences
+    t_window, n_win = 0.0, 0
+    if win is not None:
+        t_w = 0.0
+        while t_w < share / 2 and n_win < cfg.batch:
+            b = n_win
+            sl = slice(b, b + 1)
+            args = [win[k][sl].cpu() for k in ("q", "hist_sink_k", "hist_sink_v",
+                                               "hist_recent_k", "hist_recent_v")]
+            t0 = time.perf_counter()
+            window_attention(*args, [cfg.kv_len], cfg.window, cfg.sinks)
+            t_w += time.perf_counter() - t0
+            n_win += 1
+        t_window = t_w / n_win * cfg.batch
+    # (3) sampling: whole sequences
+    t_s, n_seq = 0.0, 0
+    while t_s < share and n_seq < cfg.batch:
+        b = n_seq
+        tl, dl, tk = (smp[k][b:b + 1].cpu() for k in ("target", "draft", "tokens"))
+        t0 = time.perf_counter()
+        spec_sample(tl, dl, tk, parent if cfg.tree else None, seed=1, offset=0)
+        t_s += time.perf_counter() - t0
+        n_seq += 1
+    t_sample = t_s / n_seq * cfg.batch
+    t_step = t_verify + t_window + t_sample
+    drafts = cfg.batch * (cfg.n_nodes - 1)
+    return {
+        "value": drafts / t_step, "unit": "verified draft tokens/s", "cores": int(threads),
+        "kind": "oracle",
+        "sample": (f"{n_unit}/{units} verify units (sequence x kv head), {n_win}/{cfg.batch} "
+                   f"window sequences, {n_seq}/{cfg.batch} sampling sequences; fp64 numpy, "
+                   f"scaled to the whole step ({t_step:.2f} s/step)"),
+        "ms_per_step": t_step * 1e3,
+    }
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); the verification "
+              "path is measured on a single MI355X and multi-GPU runs are not part of it.",
+              file=sys.stderr)
+        sys.exit(2)
+    import torch
+    import long_context_verify_amd as L
+    from workloads import CONFIGS
+
+    if not torch.cuda.is_available():
+        print("no HIP device visible", file=sys.stderr)
+        sys.exit(1)
+    cfg = CONFIGS[args.workload]
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    L.lib()  # fail loudly if the library is missing
+    log(f"[bench] building inputs for {cfg.name}")
+    att, parent, win, smp = build_inputs(cfg, dev)
+    B, Hq, Hkv, D, Lk, nq = cfg.batch, cfg.hq, cfg.hkv, cfg.head_dim, cfg.kv_len, cfg.n_q
+    dt = att["q"].dtype
+    esz = att["q"].element_size()
+
+    # Preallocated outputs and workspaces: the timed loop allocates nothing.
+    out = torch.empty_like(att["q"])
+    lse = torch.empty(B, Hq, nq, dtype=torch.float32, device=dev)
+    ws_v = torch.zeros(max(L.verify_attention_workspace_bytes(B, Hq, Hkv, nq, D, Lk, dt), 256),
+                       dtype=torch.uint8, device=dev)
+    par_t = None if parent is None else torch.as_tensor(parent, dtype=torch.int32, device=dev)
+    if win is not None:
+        wout = torch.empty_like(win["q"])
+        wlse = torch.empty(B, Hq, 1, dtype=torch.float32, device=dev)
+        ws_w = torch.zeros(max(L.window_attention_workspace_bytes(B, Hq, Hkv, D, cfg.window,
+                                                                  cfg.sinks, dt), 256),
+                           dtype=torch.uint8, device=dev)
+    N, V = cfg.n_nodes, cfg.vocab
+    s_out = {"out_tokens": torch.empty(B, N, dtype=torch.int32, device=dev),
+             "out_count": torch.empty(B, dtype=torch.int32, device=dev),
+             "out_path": torch.empty(B, N, dtype=torch.int32, device=dev),
+             "out_accept": torch.empty(B, N, dtype=torch.uint8, device=dev)}
+    ws_s = torch.zeros(max(L.sample_workspace_bytes(B, N, V), 256), dtype=torch.uint8, device=dev)
+    seed = 0x5EED0000 + cfg.seed
+
+    def op_verify():
+        L.verify_attention(att["q"], att["k"], att["v"], att["kv_len"], parent=par_t, out=out,
+                           lse=lse, workspace=ws_v)
+
+    def op_window():
+        L.window_attention(win["q"], win["k_ring"], win["v_ring"], win["k_sink"], win["v_sink"],
+                           win["total_len"], out=wout, lse=wlse, workspace=ws_w)
+
+    def op_sample(i):
+        L.spec_sample(smp["target"], smp["draft"], smp["tokens"], parent=par_t if cfg.tree else None,
+                      seed=seed, offset=i, workspace=ws_s, **s_out)
+
+    ops = [("verify_attn", lambda i: op_verify())]
+    if win is not None:
+        ops.append(("window_attn", lambda i: op_window()))
+    ops.append(("sample", op_sample))
+
+    if args.copy_probe_mib > 0:
+        n = args.copy_probe_mib << 20
+        src_b = torch.ones(n, dtype=torch.uint8, device=dev)
+        dst_b = torch.empty_like(src_b)
+        for _ in range(3):
+            dst_b.copy_(src_b)
+        torch.cuda.synchronize()
+        log(f"[bench] copy probe: 3 x {args.copy_probe_mib} MiB device-to-device copies")
+        del src_b, dst_b
+
+    log(f"[bench] warmup {args.warmup}")
+    for i in range(args.warmup):
+        for _, f in ops:
+            f(i)
+    torch.cuda.synchronize()
+
+    # (A) Headline: K whole steps back to back, host clock around a device sync.
+    log(f"[bench] timing {args.steps} steps")
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        for _, f in ops:
+            f(args.warmup + i)
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    ms_step = (t1 - t0) * 1e3 / args.steps
+
+    # (B) Per-op device time: HIP events on the stream the library launches on
+    # (torch's current stream), one pair per call.  All calls are queued behind
+    # a GPU sleep so host launch latency cannot leak into the bracketed time;
+    # ops whose inputs fit in the 256 MB Infinity Cache get a 512 MB read of an
+    # unrelated buffer between calls (outside the brackets), so every call
+    # reads its inputs from HBM and no dirty lines are left to write back.
+    stream = torch.cuda.current_stream(dev)
+    flush = torch.ones(128 << 20, dtype=torch.float32, device=dev)
+    op_bytes_in = {"verify_attn": att["k"].numel() * esz * 2,
+                   "window_attn": 0 if win is None else
+                   (win["k_ring"].numel() + win["k_sink"].numel()) * esz * 2,
+                   "sample": smp["target"].numel() * 8}
+    op_us = {}
+    for name, f in ops:
+        pairs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+                 for _ in range(args.steps)]
+        need_flush = op_bytes_in[name] < (768 << 20)
+        torch.cuda.synchronize()
+        torch.cuda._sleep(int(2.4e9 * 0.05))           # ~50 ms of GPU spin while we enqueue
+        for i, (e0, e1) in enumerate(pairs):
+            if need_flush:
+                flush.amax()
+            e0.record(stream)
+            f(args.warmup + args.steps + i)
+            e1.record(stream)
+        torch.cuda.synchronize()
+        op_us[name] = float(np.mean([a.elapsed_time(b) for a, b in pairs]) * 1e3)
+    log(f"[bench] per-op mean us: {op_us}")
+
+    # Algorithmic bytes per call.
+    kv_bytes = 2 * B * Hkv * Lk * D * esz
+    qo_bytes = 2 * B * Hq * nq * D * esz
+    verify_bytes = kv_bytes + qo_bytes
+    ops_report = {"verify_attn": {
+        "us": op_us["verify_attn"], "bytes": verify_bytes,
+        "GBps": verify_bytes / op_us["verify_attn"] / 1e3,
+    }}
+    ops_report["verify_attn"]["hbm_frac"] = ops_report["verify_attn"]["GBps"] / HBM_PEAK_GBPS
+    if win is not None:
+        keys = cfg.sinks + cfg.window
+        wbytes = 2 * B * Hkv * keys * D * esz + 2 * B * Hq * D * esz
+        ops_report["window_attn"] = {"us": op_us["window_attn"], "bytes": wbytes,
+                                     "GBps": wbytes / op_us["window_attn"] / 1e3}
+    srows = sample_rows_read(N, parent if cfg.tree else None)
+    sbytes = B * srows * V * 4
+    ops_report["sample"] = {"us": op_us["sample"], "bytes": sbytes,
+                            "GBps": sbytes / op_us["sample"] / 1e3}
+    ops_report["sample"]["hbm_frac"] = ops_report["sample"]["GBps"] / HBM_PEAK_GBPS
+
+    drafts = B * (N - 1)
+    value = drafts / (ms_step / 1e3)
+    res = {
+        "metric": METRIC,
+        "value": value,
+        "unit": "verified draft tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16" if dt != torch.float32 else "f32",
+        "data": "synthetic",
+        "config": {"workload": cfg.name, "batch": B, "q_heads": Hq, "kv_heads": Hkv,
+                   "head_dim": D, "kv_len": Lk, "block": "tree" if cfg.tree else "chain",
+                   "gamma": nq - 1, "draft_window": cfg.window, "sinks": cfg.sinks,
+                   "vocab": V, "parallelism": "single-gpu"},
+        "verify_attn_GBps": ops_report["verify_attn"]["GBps"],
+        "verify_attn_hbm_frac": ops_report["verify_attn"]["hbm_frac"],
+        "roofline": {
+            "kernel": "spec_verify_attention",
+            "bound": "hbm",
+            "achieved": ops_report["verify_attn"]["GBps"],
+            "peak": HBM_PEAK_GBPS,
+            "unit": "GB/s",
+            "frac": ops_report["verify_attn"]["hbm_frac"],
+            "traffic": recorded_traffic(cfg.name),
+        },
+        "ops": ops_report,
+    }
+    if args.cpu_budget > 0:
+        log("[bench] timing the oracle on a bounded sample (CPU)")
+        res["cpu_baseline"] = cpu_baseline(cfg, att, parent, win, smp, args.cpu_budget)
+    print(json.dumps(res), flush=True)
+
+
+if __name__ == "__main__":
+    main()

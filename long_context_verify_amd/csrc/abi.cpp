@@ -143,6 +143,8 @@ spec_status_t spec_verify_attention(const void* q, const void* k_cache, const vo
   a.grid = p.grid;
   a.scale_log2 = resolve_scale(scale, D);
   a.dev_err = dev_err;
+  a.out = out;
+  a.lse = lse;
   return launch_attention(a, false, dtype, out, lse, stream) == hipSuccess ? SPEC_OK : SPEC_ERR_HIP;
 }
 
@@ -205,6 +207,8 @@ spec_status_t spec_window_attention(const void* q, void* k_ring, void* v_ring, v
   a.grid = p.grid;
   a.scale_log2 = resolve_scale(scale, D);
   a.dev_err = dev_err;
+  a.out = out;
+  a.lse = lse;
   return launch_attention(a, true, dtype, out, lse, stream) == hipSuccess ? SPEC_OK : SPEC_ERR_HIP;
 }
 
@@ -252,7 +256,9 @@ spec_status_t spec_sample(const float* target_logits, const float* draft_logits,
   a.part_m = reinterpret_cast<float*>(ws + p.off_m);
   a.part_s = reinterpret_cast<double*>(ws + p.off_s);
   a.race_w = reinterpret_cast<double*>(ws + p.off_w);
-  a.counters = reinterpret_cast<int32_t*>(ws + p.off_cnt);
+  a.decision = reinterpret_cast<int32_t*>(ws + p.off_dec);
+  a.decision_lz = reinterpret_cast<double*>(ws + p.off_lz);
+  a.dec_stride = p.dec_stride;
   a.n_vchunks = p.n_vchunks;
   a.vchunk = p.vchunk;
   a.n_race = p.n_race;

@@ -11,10 +11,12 @@
 //   * a work-group owns one (sequence, kv head) unit, one slice of its query
 //     rows (the g query heads of the GQA group times the n_q block nodes, all
 //     served by the same K/V tiles) and one contiguous range of 32-key chunks;
-//   * each of its four waves walks every fourth chunk on its own, with no LDS
-//     and no barrier in the loop: K and V rows are loaded straight into MFMA
-//     operand registers (V as eight 16-byte row pieces that are transposed
-//     in-register), S^T = K Q^T and O^T = V^T P^T run on
+//   * each of its four waves walks every fourth chunk on its own, with no
+//     barrier in the loop: K and V rows are streamed with non-temporal
+//     16-byte loads (the wave's next chunk in flight while it computes the
+//     current one) straight into MFMA operand registers (V as eight 16-byte
+//     row pieces transposed in-register; the loop-invariant Q operands sit in
+//     LDS), S^T = K Q^T and O^T = V^T P^T run on
 //     v_mfma_f32_16x16x32_bf16, and an online softmax in the log2 domain keeps
 //     every per-query quantity in the lanes of that query;
 //   * the mask is evaluated only on chunks that reach the block's own keys or
@@ -29,6 +31,8 @@
 // the head dimension) with the same partial format.
 
 #include <hip/hip_runtime.h>
+
+#include <type_traits>
 
 #include "spec_common.hpp"
 #include "spec_internal.hpp"
@@ -185,6 +189,7 @@ __global__ __launch_bounds__(kThreads, 2) void attn_split_mfma(AttnArgs a) {
   constexpr int LDS_STRIDE = D + 1;
   __shared__ float lds_o[kWaves][SR][LDS_STRIDE];
   __shared__ float lds_ml[kWaves][SR][2];
+  __shared__ bf16x8 lds_q[QB][DS][kWave];
 
   int unit, split, qs;
   if (!decode_tile(a, unit, split, qs)) return;
@@ -198,24 +203,26 @@ __global__ __launch_bounds__(kThreads, 2) void attn_split_mfma(AttnArgs a) {
   window_append<WINDOW>(a, u, split, qs, row_bytes);
 
   // Query operands (B side of S^T = K Q^T): lane holds Q[row][32 s + 8 h .. +8].
+  // They are loop-invariant; wave 0 stages them in LDS in operand order and
+  // every wave re-reads them per chunk (conflict-free 16-byte reads), which
+  // keeps 32 VGPRs free for the in-flight K/V of the next chunk.
   const char* qbase = static_cast<const char*>(a.q) +
                       ((size_t)(u.b * a.Hq + u.hk * a.g) * a.n_q) * row_bytes;
-  bf16x8 qop[QB][DS];
   uint64_t anc[QB];
 #pragma unroll
   for (int qb = 0; qb < QB; ++qb) {
     const int row = qs * SR + qb * 16 + r;
     const bool live = row < a.M;
+    if (wave == 0) {
 #pragma unroll
-    for (int s = 0; s < DS; ++s) {
-      if (live)
-        qop[qb][s] = *reinterpret_cast<const bf16x8*>(qbase + (size_t)row * row_bytes +
-                                                      (32 * s + 8 * h) * 2);
-      else
-        qop[qb][s] = bf16x8{};
+      for (int s = 0; s < DS; ++s)
+        lds_q[qb][s][lane] = live ? *reinterpret_cast<const bf16x8*>(
+                                        qbase + (size_t)row * row_bytes + (32 * s + 8 * h) * 2)
+                                  : bf16x8{};
     }
     anc[qb] = (!WINDOW && live) ? ancestor_mask(a, u.b, row % a.n_q) : 1ull;
   }
+  __syncthreads();
 
   int c0, c1;
   chunk_range(u.n_keys, split, a.n_splits, c0, c1);
@@ -231,10 +238,8 @@ __global__ __launch_bounds__(kThreads, 2) void attn_split_mfma(AttnArgs a) {
   }
 
   const int last = u.n_keys - 1;
-  for (int c = c0 + wave; c < c1; c += kWaves) {
-    const int kbase = c * kChunk;
-    // K operands (A side): lane holds K[kbase + 16 kb + r][32 s + 8 h .. +8].
-    bf16x8 kop[2][DS];
+  // K operands (A side): lane holds K[kbase + 16 kb + r][32 s + 8 h .. +8].
+  auto load_k = [&](int kbase, bf16x8 (&kop)[2][DS]) {
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb) {
       int key = kbase + 16 * kb + r;
@@ -242,35 +247,52 @@ __global__ __launch_bounds__(kThreads, 2) void attn_split_mfma(AttnArgs a) {
       const char* p = key_row<WINDOW>(a, u, key, 0, row_bytes);
 #pragma unroll
       for (int s = 0; s < DS; ++s)
-        kop[kb][s] = *reinterpret_cast<const bf16x8*>(p + (32 * s + 8 * h) * 2);
+        kop[kb][s] = __builtin_nontemporal_load(reinterpret_cast<const bf16x8*>(p + (32 * s + 8 * h) * 2));
     }
-    // V row pieces: lane holds V[key(h,t)][8 r .. 8 r + 7] for its eight keys
-    // key(h,t) = kbase + 16 (t/4) + 4 h + t%4 -- the keys whose scores the
-    // S^T accumulators leave in this lane.
-    u32x4 vraw[8];
+  };
+  // V row pieces: lane holds V[key(h,t)][8 r .. 8 r + 7] for its eight keys
+  // key(h,t) = kbase + 16 (t/4) + 4 h + t%4 -- the keys whose scores the
+  // S^T accumulators leave in this lane.
+  auto load_v = [&](int kbase, u32x4 (&vraw)[8]) {
 #pragma unroll
     for (int t = 0; t < 8; ++t) {
       int key = kbase + 16 * (t >> 2) + 4 * h + (t & 3);
       key = key < last ? key : last;
       if (8 * r < D)
-        vraw[t] = *reinterpret_cast<const u32x4*>(key_row<WINDOW>(a, u, key, 1, row_bytes) +
-                                                  r * 16);
+        vraw[t] = __builtin_nontemporal_load(
+            reinterpret_cast<const u32x4*>(key_row<WINDOW>(a, u, key, 1, row_bytes) + r * 16));
       else
         vraw[t] = u32x4{0u, 0u, 0u, 0u};
     }
+  };
+
+  // Software pipeline: the loads of the wave's next chunk are issued as soon
+  // as the current chunk has consumed the registers they land in (K after the
+  // S^T products, V after its transpose), so HBM traffic stays in flight
+  // while the wave computes.  The prefetch is never behind a branch, which
+  // keeps the compiler's wait counts exact.
+  bf16x8 kop[2][DS];
+  u32x4 vraw[8];
+  auto chunk_step = [&](auto prefetch, int kbase, int nbase) {
+    constexpr bool kPrefetch = decltype(prefetch)::value;
 
     // S^T blocks: sacc[qb][kb][e] = score(key kbase + 16 kb + 4 h + e, query qb*16 + r).
     f32x4 sacc[QB][2];
+    int qlane = lane;
+    asm volatile("" : "+v"(qlane));  // keep the LDS reads of Q inside the loop
 #pragma unroll
-    for (int qb = 0; qb < QB; ++qb)
+    for (int qb = 0; qb < QB; ++qb) {
+      f32x4 acc0 = {0.f, 0.f, 0.f, 0.f}, acc1 = acc0;
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb) {
-        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int s = 0; s < DS; ++s)
-          acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kop[kb][s], qop[qb][s], acc, 0, 0, 0);
-        sacc[qb][kb] = acc;
+      for (int s = 0; s < DS; ++s) {
+        const bf16x8 qv = lds_q[qb][s][qlane];
+        acc0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kop[0][s], qv, acc0, 0, 0, 0);
+        acc1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kop[1][s], qv, acc1, 0, 0, 0);
       }
+      sacc[qb][0] = acc0;
+      sacc[qb][1] = acc1;
+    }
+    if constexpr (kPrefetch) load_k(nbase, kop);
 
     const bool need_mask = kbase + kChunk > u.p0;
     bf16x8 pop[QB];
@@ -283,9 +305,11 @@ __global__ __launch_bounds__(kThreads, 2) void attn_split_mfma(AttnArgs a) {
 #pragma unroll
         for (int t = 0; t < 8; ++t) {
           const int key = kbase + 16 * (t >> 2) + 4 * h + (t & 3);
-          bool ok = key < u.n_keys;
-          if (ok && key >= u.p0) ok = (anc[qb] >> (key - u.p0)) & 1ull;
-          if (!ok) sv[t] = -INFINITY;
+          const int rel = key - u.p0;   // block node index when 0 <= rel < n_q
+          const bool in_block = rel >= 0;
+          const bool anc_ok = ((anc[qb] >> (rel & 63)) & 1ull) != 0;
+          const bool ok = key < u.n_keys && (!in_block || anc_ok);
+          sv[t] = ok ? sv[t] : -INFINITY;
         }
       }
       float cm = sv[0];
@@ -313,6 +337,7 @@ __global__ __launch_bounds__(kThreads, 2) void attn_split_mfma(AttnArgs a) {
 
     // In-register 8x8 transpose: vop[j] holds V[key(h,t)][8 r + j] for t = 0..7,
     // the A operand of O^T = V^T P^T whose row r stands for head-dim index 8 r + j.
+    bf16x8 vop[8];
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
       u32x4 w;
@@ -322,10 +347,30 @@ __global__ __launch_bounds__(kThreads, 2) void attn_split_mfma(AttnArgs a) {
         const uint32_t hi = vraw[2 * e + 1][j >> 1];
         w[e] = (j & 1) ? ((lo >> 16) | (hi & 0xffff0000u)) : ((lo & 0xffffu) | (hi << 16));
       }
-      const bf16x8 vop = __builtin_bit_cast(bf16x8, w);
+      vop[j] = __builtin_bit_cast(bf16x8, w);
+    }
+    if constexpr (kPrefetch) load_v(nbase, vraw);
+#pragma unroll
+    for (int j = 0; j < 8; ++j)
 #pragma unroll
       for (int qb = 0; qb < QB; ++qb)
-        oacc[qb][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vop, pop[qb], oacc[qb][j], 0, 0, 0);
+        oacc[qb][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vop[j], pop[qb], oacc[qb][j], 0, 0, 0);
+  };
+
+  int c = c0 + wave;
+  if (c < c1) {
+    load_k(c * kChunk, kop);
+    load_v(c * kChunk, vraw);
+    if constexpr (WINDOW) {
+      // A few chunks per wave: peel the last one so nothing is read twice.
+      for (; c + kWaves < c1; c += kWaves)
+        chunk_step(std::true_type{}, c * kChunk, (c + kWaves) * kChunk);
+      chunk_step(std::false_type{}, c * kChunk, 0);
+    } else {
+      // Tens of chunks per wave: a branch-free loop whose last iteration
+      // re-reads its own chunk schedules better than the peeled form.
+      for (; c < c1; c += kWaves)
+        chunk_step(std::true_type{}, c * kChunk, (c + kWaves < c1 ? c + kWaves : c) * kChunk);
     }
   }
 
@@ -348,10 +393,14 @@ __global__ __launch_bounds__(kThreads, 2) void attn_split_mfma(AttnArgs a) {
   }
   __syncthreads();
 
-  // Merge the four waves and store the work-group partial.
+  // Merge the four waves.  With a single split per unit this is the final
+  // result (normalised and stored straight to the output); otherwise the
+  // work-group partial goes to the workspace for the split merge.
   const size_t part = ((size_t)unit * a.n_qs + qs) * a.n_splits + split;
   float* wo = a.ws_o + part * SR * D;
   float* wml = a.ws_ml + part * SR * 2;
+  const bool direct = a.n_splits == 1;
+  const size_t orow0 = (size_t)(u.b * a.Hq + u.hk * a.g) * a.n_q + (size_t)qs * SR;
   for (int idx = threadIdx.x; idx < SR * D; idx += kThreads) {
     const int row = idx / D, d = idx - row * D;
     float mx = -INFINITY;
@@ -365,10 +414,18 @@ __global__ __launch_bounds__(kThreads, 2) void attn_split_mfma(AttnArgs a) {
       o += sc * lds_o[w][row][d];
       l += sc * lds_ml[w][row][1];
     }
-    wo[idx] = o;
-    if (d == 0) {
-      wml[row * 2 + 0] = mx;
-      wml[row * 2 + 1] = l;
+    if (direct) {
+      if (qs * SR + row < a.M) {
+        static_cast<__bf16*>(a.out)[(orow0 + row) * D + d] = (__bf16)(l > 0.f ? o / l : 0.f);
+        if (d == 0 && a.lse)
+          a.lse[orow0 + row] = l > 0.f ? (mx + __log2f(l)) * kLn2 : -INFINITY;
+      }
+    } else {
+      wo[idx] = o;
+      if (d == 0) {
+        wml[row * 2 + 0] = mx;
+        wml[row * 2 + 1] = l;
+      }
     }
   }
 }
@@ -449,6 +506,14 @@ __global__ __launch_bounds__(kThreads) void attn_split_valu(AttnArgs a) {
     }
   }
 
+  if (a.n_splits == 1) {
+    const size_t orow = (size_t)(u.b * a.Hq + u.hk * a.g) * a.n_q + row;
+    const float inv = l > 0.f ? 1.f / l : 0.f;
+#pragma unroll
+    for (int e = 0; e < DPL; ++e) static_cast<float*>(a.out)[orow * D + lane + 64 * e] = o[e] * inv;
+    if (lane == 0 && a.lse) a.lse[orow] = l > 0.f ? (m + __log2f(l)) * kLn2 : -INFINITY;
+    return;
+  }
   const size_t part = ((size_t)unit * a.n_qs + qs) * a.n_splits + split;
   float* wo = a.ws_o + (part * kValuSlice + wave) * D;
 #pragma unroll
@@ -461,44 +526,49 @@ __global__ __launch_bounds__(kThreads) void attn_split_valu(AttnArgs a) {
 }
 
 // ---------------------------------------------------------------------------
-// Split merge: one wave per output row, fixed split order (deterministic).
+// Split merge: one thread per (output row, 4 head-dim entries).  Splits are
+// combined in a fixed order, so the result is deterministic.
 // ---------------------------------------------------------------------------
 template <int D, typename OutT>
 __global__ __launch_bounds__(256) void attn_merge(MergeArgs a) {
-  constexpr int DPL = D / 64;
-  const int lane = threadIdx.x & 63;
-  const long long grow = (long long)blockIdx.x * 4 + (threadIdx.x >> 6);
-  const long long total = (long long)a.B * a.Hkv * a.M;
-  if (grow >= total) return;
+  constexpr int TPR = D / 4;  // threads per row
+  const long long gid = (long long)blockIdx.x * 256 + threadIdx.x;
+  const long long total = (long long)a.B * a.Hkv * a.M * TPR;
+  if (gid >= total) return;
+  const long long grow = gid / TPR;
+  const int d0 = (int)(gid - grow * TPR) * 4;
   const int unit = (int)(grow / a.M);
   const int row = (int)(grow - (long long)unit * a.M);
   const int qs = row / a.slice_rows;
   const int rr = row - qs * a.slice_rows;
   const size_t part0 = ((size_t)unit * a.n_qs + qs) * a.n_splits;
+  const size_t pstride = (size_t)a.slice_rows;   // rows between consecutive splits
 
-  float mx = -INFINITY;
-  for (int s = 0; s < a.n_splits; ++s)
-    mx = fmaxf(mx, a.ws_ml[((part0 + s) * a.slice_rows + rr) * 2]);
-  const float mu = (mx == -INFINITY) ? 0.f : mx;
-  float acc[DPL];
-#pragma unroll
-  for (int e = 0; e < DPL; ++e) acc[e] = 0.f;
-  float l = 0.f;
+  // Single pass with a running max: every split's loads are independent, so
+  // they are all in flight together.
+  const float* ml = a.ws_ml + (part0 * a.slice_rows + rr) * 2;
+  const float* src = a.ws_o + (part0 * a.slice_rows + rr) * D + d0;
+  float mx = -INFINITY, l = 0.f;
+  f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll 8
   for (int s = 0; s < a.n_splits; ++s) {
-    const size_t pr = (part0 + s) * a.slice_rows + rr;
-    const float sc = fast_exp2(a.ws_ml[pr * 2] - mu);
-    l += sc * a.ws_ml[pr * 2 + 1];
-    const float* src = a.ws_o + pr * D;
-#pragma unroll
-    for (int e = 0; e < DPL; ++e) acc[e] = fmaf(sc, src[lane + 64 * e], acc[e]);
+    const float ms = ml[s * pstride * 2];
+    const float ls = ml[s * pstride * 2 + 1];
+    const f32x4 v = *reinterpret_cast<const f32x4*>(src + s * pstride * D);
+    const float mn = fmaxf(mx, ms);
+    const float mu = (mn == -INFINITY) ? 0.f : mn;
+    const float s_old = fast_exp2(mx - mu), s_new = fast_exp2(ms - mu);
+    acc = acc * s_old + v * s_new;
+    l = l * s_old + ls * s_new;
+    mx = mn;
   }
   const float inv = l > 0.f ? 1.f / l : 0.f;
-  const int b = unit / a.Hkv, hk = unit - (unit / a.Hkv) * a.Hkv;
+  const int b = unit / a.Hkv, hk = unit - b * a.Hkv;
   const size_t orow = (size_t)(b * a.Hq + hk * a.g) * a.n_q + row;
-  OutT* out = static_cast<OutT*>(a.out) + orow * D;
+  OutT* out = static_cast<OutT*>(a.out) + orow * D + d0;
 #pragma unroll
-  for (int e = 0; e < DPL; ++e) out[lane + 64 * e] = (OutT)(acc[e] * inv);
-  if (a.lse && lane == 0) a.lse[orow] = l > 0.f ? (mx + __log2f(l)) * kLn2 : -INFINITY;
+  for (int e = 0; e < 4; ++e) out[e] = (OutT)(acc[e] * inv);
+  if (a.lse && d0 == 0) a.lse[orow] = l > 0.f ? (mx + __log2f(l)) * kLn2 : -INFINITY;
 }
 
 // ---------------------------------------------------------------------------
@@ -516,10 +586,17 @@ AttnPlan plan_attention(int32_t B, int32_t Hkv, int32_t M, int32_t D, int32_t n_
   const int chunks = ceil_div(n_keys_max, kChunk);
   if (num_splits > 0) {
     p.n_splits = num_splits;
+  } else if (window) {
+    // The draft window is a few hundred keys and latency-bound: spread it so
+    // that every wave gets one chunk.
+    p.n_splits = (int)(mfma ? (chunks + kWaves - 1) / kWaves : (chunks + 7) / 8);
+    if (p.n_splits < 1) p.n_splits = 1;
   } else {
-    // Aim for about four work-groups per CU (256 CUs) so the HBM stream has
-    // enough waves in flight, but give every wave at least one chunk.
-    const long long target = window ? 512 : 1024;
+    // Aim for about one work-group per CU (256 CUs): on the 8B / 32K, 128K
+    // and 70B / 16K workloads fewer, longer key ranges streamed faster than
+    // more, shorter ones (and need less merge traffic).  Every wave gets at
+    // least one chunk.
+    const long long target = 256;
     long long s = (target + units * p.n_qs - 1) / (units * p.n_qs);
     long long smax = mfma ? (chunks + kWaves - 1) / kWaves : chunks;
     if (s > smax) s = smax;
@@ -562,7 +639,7 @@ static hipError_t launch_split(const AttnArgs& a, spec_dtype_t dtype, hipStream_
 hipError_t launch_attention(const AttnArgs& a, bool window, spec_dtype_t dtype, void* out,
                             float* lse, hipStream_t stream) {
   hipError_t e = window ? launch_split<true>(a, dtype, stream) : launch_split<false>(a, dtype, stream);
-  if (e != hipSuccess) return e;
+  if (e != hipSuccess || a.n_splits == 1) return e;
   MergeArgs m;
   m.ws_o = a.ws_o;
   m.ws_ml = a.ws_ml;
@@ -578,8 +655,8 @@ hipError_t launch_attention(const AttnArgs& a, bool window, spec_dtype_t dtype, 
   m.slice_rows = a.slice_rows;
   m.n_qs = a.n_qs;
   m.n_splits = a.n_splits;
-  const long long rows = (long long)a.B * a.Hkv * a.M;
-  dim3 grid((unsigned)((rows + 3) / 4)), block(256);
+  const long long threads = (long long)a.B * a.Hkv * a.M * (a.D / 4);
+  dim3 grid((unsigned)((threads + 255) / 256)), block(256);
   if (dtype == SPEC_BF16) {
     if (a.D == 128)
       hipLaunchKernelGGL((attn_merge<128, __bf16>), grid, block, 0, stream, m);

@@ -9,20 +9,20 @@
 // the normalised max(p_target - p_draft, 0) (after a rejection) or from
 // p_target (when the walk ends at a leaf: the bonus token).
 //
-// Two kernels:
+// Three kernels, back to back on the caller's stream (the kernel boundaries
+// order the phases; no work-group waits on another):
 //
-//   sample_stats      grid (vocab chunks, 2N rows, B).  Streams the logits
-//                     once (every target row and the draft rows of nodes that
-//                     have children) and writes per-chunk (max, sum of
-//                     exp(x - max)); fp32 inside a thread, fp64 across.
-//   sample_resolve    grid (groups, B).  Every work-group of a sequence first
-//                     re-derives the same decision (fp64 log-normalisers, one
-//                     Philox uniform per node, the walk) -- a few hundred
-//                     scalars -- then computes the residual (or target) mass
-//                     of its share of 1024-id race chunks of the stop row.  The
-//                     last work-group of the sequence to finish (device-scope
-//                     counter) runs the two-level exponential race in fp64 and
-//                     writes the outputs.
+//   sample_stats   grid (vocab chunks, 2N rows, B).  Streams the logits once
+//                  (every target row and the draft rows of nodes that have
+//                  children) and writes per-chunk (max, sum of exp(x - max));
+//                  fp32 inside a thread, fp64 across threads.
+//   sample_resid   grid (groups, B).  Every work-group of a sequence derives
+//                  the same decision (fp64 log-normalisers, one Philox uniform
+//                  per node, the walk) -- a few hundred scalars -- then sums
+//                  the residual (or target) mass of its share of the 1024-id
+//                  race chunks of the stop row.  Group 0 stores the decision.
+//   sample_race    grid (B).  The two-level exponential race in fp64 at the
+//                  stop row, and the outputs.
 //
 // Randomness: Philox4x32-10 (Salmon, Moraes, Dror, Shaw, SC'11: four 32-bit
 // counter words, two key words, ten rounds of two 32x32->64 multiplies with
@@ -127,7 +127,6 @@ __global__ __launch_bounds__(kSampleThreads) void sample_stats(SampleArgs a) {
   __shared__ float redf[4];
   __shared__ double redd[4];
   const int chunk = blockIdx.x, rowsel = blockIdx.y, b = blockIdx.z;
-  if (chunk == 0 && rowsel == 0 && threadIdx.x == 0) a.counters[b] = 0;
   const int kind = rowsel >= a.N;  // 0: target row, 1: draft row
   const int u = rowsel - kind * a.N;
   if (kind) {
@@ -175,70 +174,72 @@ __global__ __launch_bounds__(kSampleThreads) void sample_stats(SampleArgs a) {
 }
 
 // ---------------------------------------------------------------------------
-// Decision, residual masses and the race.
+// Decision and residual masses.
 // ---------------------------------------------------------------------------
-struct RowStat {
-  float m;     // row max
-  double s;    // sum exp(x - m)
-};
-
-__device__ __forceinline__ RowStat combine_row(const SampleArgs& a, int b, int rowsel) {
-  const size_t o = ((size_t)b * 2 * a.N + rowsel) * a.n_vchunks;
-  float m = -INFINITY;
-  for (int k = 0; k < a.n_vchunks; ++k) m = fmaxf(m, a.part_m[o + k]);
-  double s = 0.0;
-  if (m != -INFINITY)
-    for (int k = 0; k < a.n_vchunks; ++k) {
-      const float mk = a.part_m[o + k];
-      if (mk != -INFINITY) s += a.part_s[o + k] * exp((double)mk - (double)m);
-    }
-  return RowStat{m, s};
+__device__ __forceinline__ float wave_max(float v) {
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) v = fmaxf(v, __shfl_xor(v, off));
+  return v;
+}
+__device__ __forceinline__ double wave_sum(double v) {
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) v += __shfl_xor(v, off);
+  return v;
 }
 
 template <bool VEC4>
-__global__ __launch_bounds__(kSampleThreads) void sample_resolve(SampleArgs a) {
+__global__ __launch_bounds__(kSampleThreads) void sample_resid(SampleArgs a) {
   __shared__ float st_m[2][SPEC_MAX_SAMPLE_NODES];
   __shared__ double st_lz[2][SPEC_MAX_SAMPLE_NODES];   // log normaliser per row
   __shared__ double st_s[2][SPEC_MAX_SAMPLE_NODES];
   __shared__ uint8_t has_child[SPEC_MAX_SAMPLE_NODES];
   __shared__ uint8_t acc[SPEC_MAX_SAMPLE_NODES];
   __shared__ int path[SPEC_MAX_SAMPLE_NODES];
-  __shared__ int s_len, s_bad, s_last, s_fallback;
+  __shared__ int s_len, s_bad;
   __shared__ double redd[4];
-  __shared__ int redi[4];
 
   const int grp = blockIdx.x, b = blockIdx.y;
   const int N = a.N, V = a.V;
   const int tid = threadIdx.x;
 
   // ---- decision (identical in every work-group of the sequence) ----
-  if (tid == 0) {
-    s_bad = 0;
-    s_fallback = 0;
-  }
+  if (tid == 0) s_bad = 0;
   for (int u = tid; u < N; u += kSampleThreads) has_child[u] = 0;
   __syncthreads();
   for (int c = 1 + tid; c < N; c += kSampleThreads) {
     const int p = parent_of(a, b, c);
-    if (p < 0 || p >= c) {
+    if (p < 0 || p >= c)
       s_bad = 1;
-    } else {
+    else
       has_child[p] = 1;
-    }
   }
   if (tid == 0 && a.parent && parent_of(a, b, 0) != -1) s_bad = 1;
   __syncthreads();
   const bool bad_tree = s_bad != 0;
-  for (int u = tid; u < N; u += kSampleThreads) {
-    const RowStat t = combine_row(a, b, u);
-    st_m[0][u] = t.m;
-    st_s[0][u] = t.s;
-    st_lz[0][u] = (double)t.m + log(t.s);
-    if (!bad_tree && has_child[u]) {
-      const RowStat d = combine_row(a, b, N + u);
-      st_m[1][u] = d.m;
-      st_s[1][u] = d.s;
-      st_lz[1][u] = (double)d.m + log(d.s);
+  // Per-row log normaliser from the per-chunk (max, sum) partials: one wave
+  // per row, lanes over chunks, so every partial is fetched in one round.
+  {
+    const int wave = tid >> 6, lane = tid & 63;
+    for (int rs = wave; rs < 2 * N; rs += kSampleThreads / kWave) {
+      const int kind = rs >= N;
+      const int u = rs - kind * N;
+      if (kind && (bad_tree || !has_child[u])) continue;   // uniform across the wave
+      const size_t o = ((size_t)b * 2 * N + rs) * a.n_vchunks;
+      float m = -INFINITY;
+      for (int k = lane; k < a.n_vchunks; k += kWave) m = fmaxf(m, a.part_m[o + k]);
+      m = wave_max(m);
+      double sum = 0.0;
+      if (m != -INFINITY)
+        for (int k = lane; k < a.n_vchunks; k += kWave) {
+          const float mk = a.part_m[o + k];
+          if (mk != -INFINITY) sum += a.part_s[o + k] * exp((double)mk - (double)m);
+        }
+      sum = wave_sum(sum);
+      if (lane == 0) {
+        st_m[kind][u] = m;
+        st_s[kind][u] = sum;
+        st_lz[kind][u] = (double)m + log(sum);
+      }
     }
   }
   __syncthreads();
@@ -290,7 +291,23 @@ __global__ __launch_bounds__(kSampleThreads) void sample_resolve(SampleArgs a) {
   __syncthreads();
   const int len = s_len;
   const int r = path[len - 1];               // stop row
-  const bool residual = has_child[r] != 0;   // rejection happened at r's children
+  const bool residual = has_child[r] != 0;   // rejection happened among r's children
+
+  if (grp == 0) {
+    int32_t* dec = a.decision + (size_t)b * a.dec_stride;
+    for (int c = tid; c < N; c += kSampleThreads) {
+      dec[4 + c] = c < len ? path[c] : -1;
+      dec[4 + N + c] = acc[c];
+    }
+    if (tid == 0) {
+      dec[0] = len;
+      dec[1] = bad ? s_bad : 0;
+      dec[2] = residual;
+      double* lz = reinterpret_cast<double*>(a.decision_lz) + (size_t)b * 2;
+      lz[0] = st_lz[0][r];
+      lz[1] = residual ? st_lz[1][r] : 0.0;
+    }
+  }
 
   // ---- residual (or target) mass of this group's race chunks ----
   const float* trow = a.target + ((size_t)b * N + r) * V;
@@ -341,15 +358,22 @@ __global__ __launch_bounds__(kSampleThreads) void sample_resolve(SampleArgs a) {
       o[1] = tp;
     }
   }
+}
 
-  // ---- last work-group of the sequence finishes the draw ----
-  __threadfence();
-  __syncthreads();
-  if (tid == 0) s_last = atomicAdd(&a.counters[b], 1) == a.n_groups - 1;
-  __syncthreads();
-  if (!s_last) return;
-  __threadfence();
-
+// ---------------------------------------------------------------------------
+// The draw at the stop row and the outputs: one work-group per sequence.
+// ---------------------------------------------------------------------------
+template <bool VEC4>
+__global__ __launch_bounds__(kSampleThreads) void sample_race(SampleArgs a) {
+  __shared__ double redd[4];
+  __shared__ int redi[4];
+  const int b = blockIdx.x;
+  const int N = a.N, V = a.V;
+  const int tid = threadIdx.x;
+  const int32_t* dec = a.decision + (size_t)b * a.dec_stride;
+  const int len = dec[0];
+  const int bad = dec[1];
+  const bool residual = dec[2] != 0;
   int* out_tok = a.out_tokens + (size_t)b * N;
   if (bad) {
     for (int c = tid; c < N; c += kSampleThreads) {
@@ -359,18 +383,24 @@ __global__ __launch_bounds__(kSampleThreads) void sample_resolve(SampleArgs a) {
     }
     if (tid == 0) {
       a.out_count[b] = 0;
-      report_error(a.dev_err, s_bad == 2 ? SPEC_DEVERR_TOKEN : SPEC_DEVERR_PARENT);
+      report_error(a.dev_err, bad == 2 ? SPEC_DEVERR_TOKEN : SPEC_DEVERR_PARENT);
     }
     return;
   }
+  const int r = dec[4 + len - 1];
+  const double* lz = reinterpret_cast<const double*>(a.decision_lz) + (size_t)b * 2;
+  const double lzt = lz[0], lzd = lz[1];
+  const float* trow = a.target + ((size_t)b * N + r) * V;
+  const float* drow = a.draft + ((size_t)b * N + r) * V;
 
-  // Level 1: chunks race with score W_c / E1_c.
-  const volatile double* rw = a.race_w + (size_t)b * a.n_race * 2;
+  // Level 1: chunks race with score W_c / E1_c.  After a rejection the
+  // weights are the residual masses; if they all vanish, the target's.
+  const double* rw = a.race_w + (size_t)b * a.n_race * 2;
   double tot = 0.0;
   for (int q = tid; q < a.n_race; q += kSampleThreads) tot += rw[2 * q];
   tot = block_sum(tot, redd);
-  const int col = (residual && tot <= 0.0) ? 1 : (residual ? 0 : 1);
-  if (tid == 0) s_fallback = residual && tot <= 0.0;
+  const bool fallback = residual && !(tot > 0.0);
+  const int col = (residual && !fallback) ? 0 : 1;
   double best = -1.0;
   int bidx = 0x7fffffff;
   for (int q = tid; q < a.n_race; q += kSampleThreads) {
@@ -383,61 +413,56 @@ __global__ __launch_bounds__(kSampleThreads) void sample_resolve(SampleArgs a) {
   }
   block_argmax(best, bidx, redd, redi);
   const int cstar = bidx < a.n_race ? bidx : 0;
-  __syncthreads();
-  const bool use_resid = residual && !s_fallback;
+  const bool use_resid = residual && !fallback;
 
   // Level 2: ids of the winning chunk race with score w_x / E2_x (fp64 weights).
-  double best2 = -1.0;
-  int bidx2 = 0x7fffffff;
-  {
-    const int e0 = cstar * kRaceChunk + 4 * tid;
-    uint32_t c0 = (uint32_t)(e0 >> 2), c1 = (uint32_t)r, c2 = (uint32_t)b, c3 = a.ctr3_base + 3u;
-    philox4x32_10(c0, c1, c2, c3, a.key0, a.key1);
-    const uint32_t words[4] = {c0, c1, c2, c3};
+  const int e0 = cstar * kRaceChunk + 4 * tid;
+  uint32_t w0 = (uint32_t)(e0 >> 2), w1 = (uint32_t)r, w2 = (uint32_t)b, w3 = a.ctr3_base + 3u;
+  philox4x32_10(w0, w1, w2, w3, a.key0, a.key1);
+  const uint32_t words[4] = {w0, w1, w2, w3};
+  double pt[4], wx[4];
 #pragma unroll
-    for (int k = 0; k < 4; ++k) {
-      const int e = e0 + k;
-      if (e < V) {
-        const double pt = exp((double)trow[e] - st_lz[0][r]);
-        double w = pt;
-        if (use_resid) {
-          const double pd = exp((double)drow[e] - st_lz[1][r]);
-          w = pt - pd > 0.0 ? pt - pd : 0.0;
-        }
-        if (w > 0.0) better(best2, bidx2, w / -log(uniform24(words[k])), e);
+  for (int k = 0; k < 4; ++k) {
+    const int e = e0 + k;
+    pt[k] = 0.0;
+    wx[k] = 0.0;
+    if (e < V) {
+      pt[k] = exp((double)trow[e] - lzt);
+      wx[k] = pt[k];
+      if (use_resid) {
+        const double pd = exp((double)drow[e] - lzd);
+        wx[k] = pt[k] - pd > 0.0 ? pt[k] - pd : 0.0;
       }
     }
   }
+  double best2 = -1.0;
+  int bidx2 = 0x7fffffff;
+#pragma unroll
+  for (int k = 0; k < 4; ++k)
+    if (wx[k] > 0.0) better(best2, bidx2, wx[k] / -log(uniform24(words[k])), e0 + k);
   block_argmax(best2, bidx2, redd, redi);
   if (bidx2 >= V) {
     // The fp32 chunk mass was positive but no id of the chunk has a positive
     // fp64 residual (a cancellation at the 1e-7 level): draw from the target.
     best2 = -1.0;
     bidx2 = 0x7fffffff;
-    const int e0 = cstar * kRaceChunk + 4 * tid;
-    uint32_t c0 = (uint32_t)(e0 >> 2), c1 = (uint32_t)r, c2 = (uint32_t)b, c3 = a.ctr3_base + 3u;
-    philox4x32_10(c0, c1, c2, c3, a.key0, a.key1);
-    const uint32_t words[4] = {c0, c1, c2, c3};
 #pragma unroll
-    for (int k = 0; k < 4; ++k) {
-      const int e = e0 + k;
-      if (e < V) {
-        const double pt = exp((double)trow[e] - st_lz[0][r]);
-        if (pt > 0.0) better(best2, bidx2, pt / -log(uniform24(words[k])), e);
-      }
-    }
+    for (int k = 0; k < 4; ++k)
+      if (pt[k] > 0.0) better(best2, bidx2, pt[k] / -log(uniform24(words[k])), e0 + k);
     block_argmax(best2, bidx2, redd, redi);
   }
   const int y = bidx2 < V ? bidx2 : 0;
 
   for (int c = tid; c < N; c += kSampleThreads) {
-    int tokv = -1, pv = -1;
-    if (c < len - 1) tokv = a.tokens[(size_t)b * N + path[c + 1]];
-    else if (c == len - 1) tokv = y;
-    if (c < len) pv = path[c];
+    int tokv = -1;
+    const int pv = dec[4 + c];
+    if (c < len - 1)
+      tokv = a.tokens[(size_t)b * N + dec[4 + c + 1]];
+    else if (c == len - 1)
+      tokv = y;
     out_tok[c] = tokv;
     if (a.out_path) a.out_path[(size_t)b * N + c] = pv;
-    if (a.out_accept) a.out_accept[(size_t)b * N + c] = acc[c];
+    if (a.out_accept) a.out_accept[(size_t)b * N + c] = (uint8_t)dec[4 + N + c];
   }
   if (tid == 0) a.out_count[b] = len;
 }
@@ -452,33 +477,33 @@ SamplePlan plan_sample(int32_t B, int32_t N, int32_t V) {
   p.vchunk = kStatsChunk;
   p.n_vchunks = (V + kStatsChunk - 1) / kStatsChunk;
   p.n_race = (V + kRaceChunk - 1) / kRaceChunk;
-  long long groups = (1024 + (long long)B - 1) / (B > 0 ? B : 1);
+  long long groups = (512 + (long long)B - 1) / (B > 0 ? B : 1);
   if (groups > p.n_race) groups = p.n_race;
   if (groups < 1) groups = 1;
   p.n_groups = (int)groups;
+  p.dec_stride = 4 + 2 * N;
   const size_t rows = (size_t)B * 2 * N * p.n_vchunks;
   p.off_m = 0;
   p.off_s = align256(p.off_m + rows * sizeof(float));
   p.off_w = align256(p.off_s + rows * sizeof(double));
-  p.off_cnt = align256(p.off_w + (size_t)B * p.n_race * 2 * sizeof(double));
-  p.bytes = align256(p.off_cnt + (size_t)B * sizeof(int32_t));
+  p.off_dec = align256(p.off_w + (size_t)B * p.n_race * 2 * sizeof(double));
+  p.off_lz = align256(p.off_dec + (size_t)B * p.dec_stride * sizeof(int32_t));
+  p.bytes = align256(p.off_lz + (size_t)B * 2 * sizeof(double));
   return p;
 }
 
 hipError_t launch_sample(const SampleArgs& a, hipStream_t stream) {
   const bool vec4 = (a.V % 4) == 0;
-  dim3 g1(a.n_vchunks, 2 * a.N, a.B), blk(kSampleThreads);
-  if (vec4)
+  dim3 g1(a.n_vchunks, 2 * a.N, a.B), g2(a.n_groups, a.B), g3(a.B), blk(kSampleThreads);
+  if (vec4) {
     hipLaunchKernelGGL(sample_stats<true>, g1, blk, 0, stream, a);
-  else
+    hipLaunchKernelGGL(sample_resid<true>, g2, blk, 0, stream, a);
+    hipLaunchKernelGGL(sample_race<true>, g3, blk, 0, stream, a);
+  } else {
     hipLaunchKernelGGL(sample_stats<false>, g1, blk, 0, stream, a);
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
-  dim3 g2(a.n_groups, a.B);
-  if (vec4)
-    hipLaunchKernelGGL(sample_resolve<true>, g2, blk, 0, stream, a);
-  else
-    hipLaunchKernelGGL(sample_resolve<false>, g2, blk, 0, stream, a);
+    hipLaunchKernelGGL(sample_resid<false>, g2, blk, 0, stream, a);
+    hipLaunchKernelGGL(sample_race<false>, g3, blk, 0, stream, a);
+  }
   return hipGetLastError();
 }
 

@@ -29,6 +29,8 @@ struct AttnArgs {
   int32_t parent_stride;
   float* ws_o;            // [n_partials][slice_rows][D]
   float* ws_ml;           // [n_partials][slice_rows][2]  (running max in log2 units, sum)
+  void* out;              // [B, Hq, n_q, D]: written directly when n_splits == 1
+  float* lse;             // nullable
   int32_t B, Hq, Hkv, g, n_q, D, L_cap, M;
   int32_t W, S;           // window geometry
   int32_t slice_rows;     // query rows per work-group slice
@@ -77,7 +79,9 @@ struct SampleArgs {
   float* part_m;           // [B][2N][n_vchunks]
   double* part_s;          // [B][2N][n_vchunks]
   double* race_w;          // [B][n_race][2]  (residual mass, target mass) per race chunk
-  int32_t* counters;       // [B]
+  int32_t* decision;       // [B][dec_stride]: len, error, residual flag, -, path[N], accept[N]
+  double* decision_lz;     // [B][2]: log normalisers of the stop row (target, draft)
+  int32_t dec_stride;
   int32_t n_vchunks;       // stats chunks per row
   int32_t vchunk;          // ids per stats chunk
   int32_t n_race;          // race chunks per row (1024 ids each)
@@ -86,8 +90,8 @@ struct SampleArgs {
 };
 
 struct SamplePlan {
-  int32_t n_vchunks, vchunk, n_race, n_groups;
-  size_t off_m, off_s, off_w, off_cnt, bytes;
+  int32_t n_vchunks, vchunk, n_race, n_groups, dec_stride;
+  size_t off_m, off_s, off_w, off_dec, off_lz, bytes;
 };
 
 SamplePlan plan_sample(int32_t B, int32_t N, int32_t V);

@@ -136,6 +136,7 @@ spec_status_t spec_verify_attention(const void* q, const void* k_cache, const vo
   a.D = D;
   a.L_cap = L_cap;
   a.M = g * n_q;
+  a.tree_waves = p.tree_waves;
   a.slice_rows = p.slice_rows;
   a.n_qs = p.n_qs;
   a.n_splits = p.n_splits;

@@ -431,6 +431,250 @@ __global__ __launch_bounds__(kThreads, 2) void attn_split_mfma(AttnArgs a) {
 }
 
 // ---------------------------------------------------------------------------
+// bf16 MFMA kernel for wide query blocks (candidate trees): all waves of a
+// work-group share every K/V chunk through LDS.
+//
+// Each wave owns 32 query rows (two MFMA blocks, Q in registers); the
+// work-group covers WAVES*32 rows of one (sequence, kv head) unit, so one
+// pass over the keys serves them all.  Chunks of 32 keys (16 KB) are copied
+// HBM -> LDS with direct-to-LDS loads (global_load_lds_dwordx4: lane l's 16
+// bytes land at base + 16 l), NBUF-1 chunks ahead of the one being computed,
+// into a ring of NBUF tiles; one barrier per chunk.  A tile holds
+//   K: 8 operand units of 1 KB in MFMA A-operand order (unit kb*4+s, lane
+//      (h,r) = K[16 kb + r][32 s + 8 h .. +8]) -- read back conflict-free;
+//   V: 32 rows x 256 B, row-major -- each wave reads its eight 16-byte row
+//      pieces and transposes them in registers as in the streaming kernel.
+// The running max is only moved (and O rescaled) when a row's chunk max
+// exceeds it by more than 2^8 (log2 domain); otherwise the exponentials are
+// taken against the old max and stay below 256, which keeps the rescale off
+// the VALU in the common case.
+// ---------------------------------------------------------------------------
+constexpr int kTreeNBuf = 4;
+constexpr float kRescaleTau = 8.0f;   // log2 units
+
+__device__ __forceinline__ void lds_dma16(const void* src, void* lds_base) {
+  __builtin_amdgcn_global_load_lds(src, (__attribute__((address_space(3))) void*)lds_base, 16, 0,
+                                   0);
+}
+
+// Wait until at most n of this wave's vector-memory operations are pending
+// (expcnt / lgkmcnt left unconstrained).
+__device__ __forceinline__ void wait_vmcnt(int n) {
+  switch (n) {
+    case 0: __builtin_amdgcn_s_waitcnt(0x0F70); break;
+    case 4: __builtin_amdgcn_s_waitcnt(0x0F74); break;
+    case 8: __builtin_amdgcn_s_waitcnt(0x0F78); break;
+    default: __builtin_amdgcn_s_waitcnt(0x0F70); break;
+  }
+}
+
+template <int WAVES>
+__global__ __launch_bounds__(WAVES * kWave, 8 / WAVES) void attn_tree_mfma(AttnArgs a) {
+  constexpr int D = 128, DS = 4, QB = 2;
+  constexpr int SR = WAVES * 32;              // query rows per work-group
+  constexpr int TILE = 16384;                 // bytes per chunk (K 8 KB + V 8 KB)
+  constexpr int UPW = 16 / WAVES;             // 1 KB load units per wave per chunk
+  __shared__ __attribute__((aligned(16))) char tiles[kTreeNBuf][TILE];
+
+  int unit, split, qs;
+  if (!decode_tile(a, unit, split, qs)) return;
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  const int r = lane & 15;
+  const int h = lane >> 4;
+  const size_t row_bytes = (size_t)D * 2;
+  const UnitGeom u = unit_geom<false>(a, unit, split == 0 && qs == 0 && threadIdx.x == 0);
+
+  const char* qbase = static_cast<const char*>(a.q) +
+                      ((size_t)(u.b * a.Hq + u.hk * a.g) * a.n_q) * row_bytes;
+  const int row0 = qs * SR + wave * 32;       // first row of this wave
+  const bool wave_live = row0 < a.M;
+  bf16x8 qop[QB][DS];
+  uint64_t anc[QB];
+#pragma unroll
+  for (int qb = 0; qb < QB; ++qb) {
+    const int row = row0 + qb * 16 + r;
+    const bool live = row < a.M;
+#pragma unroll
+    for (int s = 0; s < DS; ++s)
+      qop[qb][s] = live ? *reinterpret_cast<const bf16x8*>(qbase + (size_t)row * row_bytes +
+                                                           (32 * s + 8 * h) * 2)
+                        : bf16x8{};
+    anc[qb] = live ? ancestor_mask(a, u.b, row % a.n_q) : 1ull;
+  }
+
+  int c0, c1;
+  chunk_range(u.n_keys, split, a.n_splits, c0, c1);
+  const int last = u.n_keys - 1;
+  const char* kbase_p = static_cast<const char*>(a.k) + (size_t)u.unit * a.L_cap * row_bytes;
+  const char* vbase_p = static_cast<const char*>(a.v) + (size_t)u.unit * a.L_cap * row_bytes;
+
+  // This wave's share of one chunk: UPW 1 KB units out of 16 (8 K + 8 V).
+  auto issue = [&](int c, int buf) {
+    const int kbase = c * kChunk;
+    char* tile = tiles[buf];
+#pragma unroll
+    for (int i = 0; i < UPW; ++i) {
+      const int unit_id = wave * UPW + i;
+      if (unit_id < 8) {      // K operand unit (kb, s)
+        const int kb = unit_id >> 2, s = unit_id & 3;
+        int key = kbase + 16 * kb + r;
+        key = key < last ? key : last;
+        lds_dma16(kbase_p + (size_t)key * row_bytes + (32 * s + 8 * h) * 2, tile + unit_id * 1024);
+      } else {                // V rows 4 (unit_id - 8) .. +3, 16 lanes per row
+        int key = kbase + 4 * (unit_id - 8) + (lane >> 4);
+        key = key < last ? key : last;
+        lds_dma16(vbase_p + (size_t)key * row_bytes + (lane & 15) * 16, tile + unit_id * 1024);
+      }
+    }
+  };
+
+  float m[QB], lsum[QB];
+  f32x4 oacc[QB][8];
+#pragma unroll
+  for (int qb = 0; qb < QB; ++qb) {
+    m[qb] = -INFINITY;
+    lsum[qb] = 0.f;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) oacc[qb][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+  }
+
+#pragma unroll
+  for (int i = 0; i < kTreeNBuf - 1; ++i)
+    if (c0 + i < c1) issue(c0 + i, (c0 + i) % kTreeNBuf);
+
+  for (int c = c0; c < c1; ++c) {
+    // Chunks issued after c by this wave so far: min(NBUF-2, c1-1-c), UPW loads each.
+    const int ahead = min(kTreeNBuf - 2, c1 - 1 - c);
+    wait_vmcnt(ahead * UPW);
+    __syncthreads();   // chunk c is in LDS for every wave; all waves are past chunk c-1
+    if (c + kTreeNBuf - 1 < c1) issue(c + kTreeNBuf - 1, (c + kTreeNBuf - 1) % kTreeNBuf);
+    if (!wave_live) continue;
+
+    const char* tile = tiles[c % kTreeNBuf];
+    const int kbase = c * kChunk;
+    bf16x8 kop[2][DS];
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int s = 0; s < DS; ++s)
+        kop[kb][s] = *reinterpret_cast<const bf16x8*>(tile + (kb * 4 + s) * 1024 + lane * 16);
+
+    f32x4 sacc[QB][2];
+#pragma unroll
+    for (int qb = 0; qb < QB; ++qb) {
+      f32x4 acc0 = {0.f, 0.f, 0.f, 0.f}, acc1 = acc0;
+#pragma unroll
+      for (int s = 0; s < DS; ++s) {
+        acc0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kop[0][s], qop[qb][s], acc0, 0, 0, 0);
+        acc1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kop[1][s], qop[qb][s], acc1, 0, 0, 0);
+      }
+      sacc[qb][0] = acc0;
+      sacc[qb][1] = acc1;
+    }
+
+    const bool need_mask = kbase + kChunk > u.p0;
+    bf16x8 pop[QB];
+#pragma unroll
+    for (int qb = 0; qb < QB; ++qb) {
+      float sv[8];
+#pragma unroll
+      for (int t = 0; t < 8; ++t) sv[t] = sacc[qb][t >> 2][t & 3] * a.scale_log2;
+      if (need_mask) {
+#pragma unroll
+        for (int t = 0; t < 8; ++t) {
+          const int key = kbase + 16 * (t >> 2) + 4 * h + (t & 3);
+          const int rel = key - u.p0;
+          const bool anc_ok = ((anc[qb] >> (rel & 63)) & 1ull) != 0;
+          const bool ok = key < u.n_keys && (rel < 0 || anc_ok);
+          sv[t] = ok ? sv[t] : -INFINITY;
+        }
+      }
+      float cm = sv[0];
+#pragma unroll
+      for (int t = 1; t < 8; ++t) cm = fmaxf(cm, sv[t]);
+      cm = xgroup_max(cm);
+      const bool grow = cm > m[qb] + kRescaleTau;
+      if (__any(grow)) {
+        const float mn = grow ? cm : m[qb];
+        const float alpha = grow ? fast_exp2(m[qb] - mn) : 1.f;
+        m[qb] = mn;
+        lsum[qb] *= alpha;
+#pragma unroll
+        for (int j = 0; j < 8; ++j) oacc[qb][j] *= alpha;
+      }
+      const float mu = (m[qb] == -INFINITY) ? 0.f : m[qb];
+      float p[8];
+      float ps = 0.f;
+#pragma unroll
+      for (int t = 0; t < 8; ++t) {
+        p[t] = fast_exp2(sv[t] - mu);
+        ps += p[t];
+      }
+      lsum[qb] += ps;
+      u32x4 pk = {pack_bf16x2(p[0], p[1]), pack_bf16x2(p[2], p[3]), pack_bf16x2(p[4], p[5]),
+                  pack_bf16x2(p[6], p[7])};
+      pop[qb] = __builtin_bit_cast(bf16x8, pk);
+    }
+
+    u32x4 vraw[8];
+#pragma unroll
+    for (int t = 0; t < 8; ++t) {
+      const int krow = 16 * (t >> 2) + 4 * h + (t & 3);
+      vraw[t] = *reinterpret_cast<const u32x4*>(tile + 8192 + krow * 256 + r * 16);
+    }
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      u32x4 w;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const uint32_t lo = vraw[2 * e][j >> 1];
+        const uint32_t hi = vraw[2 * e + 1][j >> 1];
+        w[e] = (j & 1) ? ((lo >> 16) | (hi & 0xffff0000u)) : ((lo & 0xffffu) | (hi << 16));
+      }
+      const bf16x8 vop = __builtin_bit_cast(bf16x8, w);
+#pragma unroll
+      for (int qb = 0; qb < QB; ++qb)
+        oacc[qb][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vop, pop[qb], oacc[qb][j], 0, 0, 0);
+    }
+  }
+
+  if (!wave_live) return;
+  // Each wave owns its rows: write them straight to the output (one split) or
+  // to the workspace partial of this (unit, slice, split).
+  const bool direct = a.n_splits == 1;
+  const size_t orow0 = (size_t)(u.b * a.Hq + u.hk * a.g) * a.n_q;
+  const size_t part = ((size_t)unit * a.n_qs + qs) * a.n_splits + split;
+#pragma unroll
+  for (int qb = 0; qb < QB; ++qb) {
+    const float l = xgroup_sum(lsum[qb]);
+    const int srow = wave * 32 + qb * 16 + r;      // row within the slice
+    const int row = qs * SR + srow;
+    if (row >= a.M) continue;
+    if (direct) {
+      const float inv = l > 0.f ? 1.f / l : 0.f;
+      __bf16* o = static_cast<__bf16*>(a.out) + (orow0 + row) * D;
+#pragma unroll
+      for (int j = 0; j < 8; ++j)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) o[8 * (4 * h + e) + j] = (__bf16)(oacc[qb][j][e] * inv);
+      if (h == 0 && a.lse) a.lse[orow0 + row] = l > 0.f ? (m[qb] + __log2f(l)) * kLn2 : -INFINITY;
+    } else {
+      float* wo = a.ws_o + (part * SR + srow) * D;
+#pragma unroll
+      for (int j = 0; j < 8; ++j)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) wo[8 * (4 * h + e) + j] = oacc[qb][j][e];
+      if (h == 0) {
+        float* wml = a.ws_ml + (part * SR + srow) * 2;
+        wml[0] = m[qb];
+        wml[1] = l;
+      }
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
 // fp32 VALU split kernel: one wave per query row, lanes over the head dim.
 // ---------------------------------------------------------------------------
 template <int D, bool WINDOW>
@@ -580,10 +824,13 @@ AttnPlan plan_attention(int32_t B, int32_t Hkv, int32_t M, int32_t D, int32_t n_
                         spec_dtype_t dtype, int32_t num_splits, bool window) {
   AttnPlan p{};
   const bool mfma = dtype == SPEC_BF16;
-  p.slice_rows = mfma ? (M <= 16 ? 16 : 32) : kValuSlice;
-  p.n_qs = ceil_div(M, p.slice_rows);
   const long long units = (long long)B * Hkv;
   const int chunks = ceil_div(n_keys_max, kChunk);
+  // Query blocks wider than one streaming slice (candidate trees) go to the
+  // LDS-shared kernel, so the K/V of a unit is read once for all its rows.
+  p.tree_waves = (mfma && !window && D == 128 && M > 32) ? (M > 128 ? 8 : 4) : 0;
+  p.slice_rows = p.tree_waves ? 32 * p.tree_waves : (mfma ? (M <= 16 ? 16 : 32) : kValuSlice);
+  p.n_qs = ceil_div(M, p.slice_rows);
   if (num_splits > 0) {
     p.n_splits = num_splits;
   } else if (window) {
@@ -615,7 +862,11 @@ AttnPlan plan_attention(int32_t B, int32_t Hkv, int32_t M, int32_t D, int32_t n_
 template <bool WINDOW>
 static hipError_t launch_split(const AttnArgs& a, spec_dtype_t dtype, hipStream_t stream) {
   dim3 grid(a.grid), block(kThreads);
-  if (dtype == SPEC_BF16) {
+  if (!WINDOW && a.tree_waves == 8) {
+    hipLaunchKernelGGL(attn_tree_mfma<8>, grid, dim3(512), 0, stream, a);
+  } else if (!WINDOW && a.tree_waves == 4) {
+    hipLaunchKernelGGL(attn_tree_mfma<4>, grid, dim3(256), 0, stream, a);
+  } else if (dtype == SPEC_BF16) {
     if (a.D == 128) {
       if (a.slice_rows == 16)
         hipLaunchKernelGGL((attn_split_mfma<128, 1, WINDOW>), grid, block, 0, stream, a);

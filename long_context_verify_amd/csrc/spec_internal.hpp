@@ -33,6 +33,7 @@ struct AttnArgs {
   float* lse;             // nullable
   int32_t B, Hq, Hkv, g, n_q, D, L_cap, M;
   int32_t W, S;           // window geometry
+  int32_t tree_waves;     // 0: streaming kernel; 4 or 8: LDS-shared wide-block kernel
   int32_t slice_rows;     // query rows per work-group slice
   int32_t n_qs;           // slices per (sequence, kv head)
   int32_t n_splits;       // key-range splits per (sequence, kv head)
@@ -52,7 +53,7 @@ struct MergeArgs {
 };
 
 struct AttnPlan {
-  int32_t slice_rows, n_qs, n_splits, grid;
+  int32_t tree_waves, slice_rows, n_qs, n_splits, grid;
   size_t ws_o_bytes, ws_ml_bytes, ws_bytes;
 };
 

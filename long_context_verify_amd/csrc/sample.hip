@@ -16,11 +16,12 @@
 //                  (every target row and the draft rows of nodes that have
 //                  children) and writes per-chunk (max, sum of exp(x - max));
 //                  fp32 inside a thread, fp64 across threads.
-//   sample_resid   grid (groups, B).  Every work-group of a sequence derives
-//                  the same decision (fp64 log-normalisers, one Philox uniform
-//                  per node, the walk) -- a few hundred scalars -- then sums
-//                  the residual (or target) mass of its share of the 1024-id
-//                  race chunks of the stop row.  Group 0 stores the decision.
+//   sample_resid   grid (race chunks, B).  Every work-group of a sequence
+//                  derives the same decision (fp64 log-normalisers, one Philox
+//                  uniform and acceptance test per node, the walk from the
+//                  root: a few hundred scalars, two memory round trips), then
+//                  the residual (or target) mass of one 1024-id chunk of the
+//                  stop row.  Group 0 stores the decision.
 //   sample_race    grid (B).  The two-level exponential race in fp64 at the
 //                  stop row, and the outputs.
 //
@@ -187,176 +188,206 @@ __device__ __forceinline__ double wave_sum(double v) {
   return v;
 }
 
-template <bool VEC4>
-__global__ __launch_bounds__(kSampleThreads) void sample_resid(SampleArgs a) {
-  __shared__ float st_m[2][SPEC_MAX_SAMPLE_NODES];
-  __shared__ double st_lz[2][SPEC_MAX_SAMPLE_NODES];   // log normaliser per row
-  __shared__ double st_s[2][SPEC_MAX_SAMPLE_NODES];
-  __shared__ uint8_t has_child[SPEC_MAX_SAMPLE_NODES];
-  __shared__ uint8_t acc[SPEC_MAX_SAMPLE_NODES];
-  __shared__ int path[SPEC_MAX_SAMPLE_NODES];
-  __shared__ int s_len, s_bad;
-  __shared__ double redd[4];
+// The decision of one sequence, computed by a whole work-group: fp64
+// log-normalisers from the per-chunk partials, one Philox uniform and
+// acceptance test per drafted node, and the walk from the root.  Every global
+// load it needs is issued up front, so it costs about two memory round trips.
+struct Decision {
+  float m[2][SPEC_MAX_SAMPLE_NODES];      // row max (target, draft)
+  double lz[2][SPEC_MAX_SAMPLE_NODES];    // row log normaliser
+  double s[2][SPEC_MAX_SAMPLE_NODES];     // row sum of exp(x - max)
+  uint8_t has_child[SPEC_MAX_SAMPLE_NODES];
+  uint8_t acc[SPEC_MAX_SAMPLE_NODES];
+  int path[SPEC_MAX_SAMPLE_NODES];
+  int len, bad, stop;
+  bool residual;
+};
 
-  const int grp = blockIdx.x, b = blockIdx.y;
+__device__ void decide_sequence(const SampleArgs& a, int b, Decision& d) {
   const int N = a.N, V = a.V;
   const int tid = threadIdx.x;
 
-  // ---- decision (identical in every work-group of the sequence) ----
-  if (tid == 0) s_bad = 0;
-  for (int u = tid; u < N; u += kSampleThreads) has_child[u] = 0;
+  // Drafted-token logits at each node's parent: issue these loads first.
+  float tl = 0.f, dl = 0.f;
+  int x = 0, p = -1;
+  const int c_tok = 1 + tid;
+  if (c_tok < N) {
+    p = parent_of(a, b, c_tok);
+    x = a.tokens[(size_t)b * N + c_tok];
+    if (p >= 0 && p < c_tok && x >= 0 && x < V) {
+      tl = a.target[((size_t)b * N + p) * V + x];
+      dl = a.draft[((size_t)b * N + p) * V + x];
+    }
+  }
+  if (tid == 0) d.bad = 0;
+  for (int u = tid; u < N; u += kSampleThreads) d.has_child[u] = 0;
   __syncthreads();
   for (int c = 1 + tid; c < N; c += kSampleThreads) {
-    const int p = parent_of(a, b, c);
-    if (p < 0 || p >= c)
-      s_bad = 1;
+    const int pc = parent_of(a, b, c);
+    if (pc < 0 || pc >= c)
+      d.bad = 1;
     else
-      has_child[p] = 1;
+      d.has_child[pc] = 1;
   }
-  if (tid == 0 && a.parent && parent_of(a, b, 0) != -1) s_bad = 1;
+  if (tid == 0 && a.parent && parent_of(a, b, 0) != -1) d.bad = 1;
   __syncthreads();
-  const bool bad_tree = s_bad != 0;
-  // Per-row log normaliser from the per-chunk (max, sum) partials: one wave
-  // per row, lanes over chunks, so every partial is fetched in one round.
-  {
-    const int wave = tid >> 6, lane = tid & 63;
-    for (int rs = wave; rs < 2 * N; rs += kSampleThreads / kWave) {
-      const int kind = rs >= N;
-      const int u = rs - kind * N;
-      if (kind && (bad_tree || !has_child[u])) continue;   // uniform across the wave
-      const size_t o = ((size_t)b * 2 * N + rs) * a.n_vchunks;
-      float m = -INFINITY;
-      for (int k = lane; k < a.n_vchunks; k += kWave) m = fmaxf(m, a.part_m[o + k]);
-      m = wave_max(m);
-      double sum = 0.0;
-      if (m != -INFINITY)
-        for (int k = lane; k < a.n_vchunks; k += kWave) {
-          const float mk = a.part_m[o + k];
-          if (mk != -INFINITY) sum += a.part_s[o + k] * exp((double)mk - (double)m);
-        }
-      sum = wave_sum(sum);
-      if (lane == 0) {
-        st_m[kind][u] = m;
-        st_s[kind][u] = sum;
-        st_lz[kind][u] = (double)m + log(sum);
+  const bool bad_tree = d.bad != 0;
+
+  // Fold the per-chunk partials of every needed row: GL lanes per row, all
+  // rows side by side, so the partials arrive in one round.
+  const int nv = a.n_vchunks;
+  const int GL = nv >= 64 ? 64 : (nv > 32 ? 64 : nv > 16 ? 32 : nv > 8 ? 16 : nv > 4 ? 8 : 4);
+  const int rows_per_pass = kSampleThreads / GL;
+  for (int base = 0; base < 2 * N; base += rows_per_pass) {
+    const int rs = base + tid / GL;
+    const int k0 = tid % GL;
+    const int kind = rs >= N;
+    const int u = rs - kind * N;
+    const bool need = rs < 2 * N && (!kind || (!bad_tree && d.has_child[u]));
+    const size_t o = ((size_t)b * 2 * N + rs) * nv;
+    float mk = -INFINITY;
+    double sk = 0.0;
+    float m = -INFINITY;
+    if (need)
+      for (int k = k0; k < nv; k += GL) m = fmaxf(m, a.part_m[o + k]);
+    for (int off = GL >> 1; off >= 1; off >>= 1) m = fmaxf(m, __shfl_xor(m, off));
+    double sum = 0.0;
+    if (need && m != -INFINITY)
+      for (int k = k0; k < nv; k += GL) {
+        mk = a.part_m[o + k];
+        sk = a.part_s[o + k];
+        if (mk != -INFINITY) sum += sk * exp((double)mk - (double)m);
+      }
+    for (int off = GL >> 1; off >= 1; off >>= 1) sum += __shfl_xor(sum, off);
+    if (need && k0 == 0) {
+      d.m[kind][u] = m;
+      d.s[kind][u] = sum;
+      d.lz[kind][u] = (double)m + log(sum);
+    }
+  }
+  __syncthreads();
+  if (tid == 0) d.acc[0] = 1;
+  if (c_tok < N) {
+    bool ok = false;
+    if (!bad_tree) {
+      if (x < 0 || x >= V) {
+        d.bad = 2;
+      } else {
+        double ratio;
+        if (dl == -INFINITY)
+          ratio = (tl == -INFINITY) ? 0.0 : INFINITY;
+        else
+          ratio = exp(((double)tl - d.lz[0][p]) - ((double)dl - d.lz[1][p]));
+        uint32_t c0 = (uint32_t)c_tok, c1 = 0u, c2 = (uint32_t)b, c3 = a.ctr3_base + 0u;
+        philox4x32_10(c0, c1, c2, c3, a.key0, a.key1);
+        ok = uniform24(c0) < ratio;
       }
     }
+    d.acc[c_tok] = ok;
   }
   __syncthreads();
-  if (tid == 0) acc[0] = 1;
-  for (int c = 1 + tid; c < N; c += kSampleThreads) {
-    acc[c] = 0;
-    if (bad_tree) continue;
-    const int p = parent_of(a, b, c);
-    const int x = a.tokens[(size_t)b * N + c];
-    if (x < 0 || x >= V) {
-      s_bad = 2;
-      continue;
-    }
-    const float tl = a.target[((size_t)b * N + p) * V + x];
-    const float dl = a.draft[((size_t)b * N + p) * V + x];
-    double ratio;
-    if (dl == -INFINITY)
-      ratio = (tl == -INFINITY) ? 0.0 : INFINITY;
-    else
-      ratio = exp(((double)tl - st_lz[0][p]) - ((double)dl - st_lz[1][p]));
-    uint32_t c0 = (uint32_t)c, c1 = 0u, c2 = (uint32_t)b, c3 = a.ctr3_base + 0u;
-    philox4x32_10(c0, c1, c2, c3, a.key0, a.key1);
-    acc[c] = uniform24(c0) < ratio;
-  }
-  __syncthreads();
-  const bool bad = s_bad != 0;
+  const bool bad = d.bad != 0;
   // Walk from the root: at each node take the first child, in index order,
   // that passed its test.  Children have larger indices than their parent.
   if (tid < kWave) {
     int cur = 0, len = 1;
-    if (tid == 0) path[0] = 0;
+    if (tid == 0) d.path[0] = 0;
     if (!bad) {
       while (true) {
         int nxt = -1;
         for (int base = cur + 1; base < N && nxt < 0; base += kWave) {
           const int c = base + tid;
-          const bool hit = c < N && acc[c] && parent_of(a, b, c) == cur;
+          const bool hit = c < N && d.acc[c] && parent_of(a, b, c) == cur;
           const unsigned long long ball = __ballot(hit);
           if (ball) nxt = base + __ffsll((long long)ball) - 1;
         }
         if (nxt < 0) break;
-        if (tid == 0) path[len] = nxt;
+        if (tid == 0) d.path[len] = nxt;
         ++len;
         cur = nxt;
       }
     }
-    if (tid == 0) s_len = len;
+    if (tid == 0) {
+      d.len = len;
+      d.stop = cur;
+      d.residual = d.has_child[cur] != 0;
+    }
   }
   __syncthreads();
-  const int len = s_len;
-  const int r = path[len - 1];               // stop row
-  const bool residual = has_child[r] != 0;   // rejection happened among r's children
+}
 
-  if (grp == 0) {
+// Residual (or target) mass of one 1024-id race chunk of the stop row.  Every
+// work-group of a sequence derives the same decision; group 0 stores it.
+template <bool VEC4>
+__global__ __launch_bounds__(kSampleThreads) void sample_resid(SampleArgs a) {
+  __shared__ Decision d;
+  __shared__ double redd[4];
+  const int q = blockIdx.x, b = blockIdx.y;
+  const int N = a.N, V = a.V;
+  const int tid = threadIdx.x;
+  decide_sequence(a, b, d);
+  const bool bad = d.bad != 0;
+  const bool residual = d.residual;
+  const int r = d.stop;
+  if (q == 0) {
     int32_t* dec = a.decision + (size_t)b * a.dec_stride;
     for (int c = tid; c < N; c += kSampleThreads) {
-      dec[4 + c] = c < len ? path[c] : -1;
-      dec[4 + N + c] = acc[c];
+      dec[4 + c] = c < d.len ? d.path[c] : -1;
+      dec[4 + N + c] = d.acc[c];
     }
     if (tid == 0) {
-      dec[0] = len;
-      dec[1] = bad ? s_bad : 0;
+      dec[0] = d.len;
+      dec[1] = d.bad;
       dec[2] = residual;
-      double* lz = reinterpret_cast<double*>(a.decision_lz) + (size_t)b * 2;
-      lz[0] = st_lz[0][r];
-      lz[1] = residual ? st_lz[1][r] : 0.0;
+      dec[3] = r;
+      double* st = a.decision_lz + (size_t)b * 2;
+      st[0] = d.lz[0][r];
+      st[1] = residual ? d.lz[1][r] : 0.0;
     }
   }
-
-  // ---- residual (or target) mass of this group's race chunks ----
-  const float* trow = a.target + ((size_t)b * N + r) * V;
-  const float* drow = a.draft + ((size_t)b * N + r) * V;
-  const float tm = st_m[0][r];
-  const float tinv = (float)(1.0 / st_s[0][r]);
-  const float dm = residual ? st_m[1][r] : 0.f;
-  const float dinv = residual ? (float)(1.0 / st_s[1][r]) : 0.f;
-  const int q0 = (int)((long long)a.n_race * grp / a.n_groups);
-  const int q1 = (int)((long long)a.n_race * (grp + 1) / a.n_groups);
-  for (int q = q0; q < q1; ++q) {
-    float sw = 0.f, spt = 0.f;
-    if (!bad) {
-      const int e0 = q * kRaceChunk + 4 * tid;
-      float tv[4], dv[4];
-      if (VEC4) {
-        f32x4 t4 = {-INFINITY, -INFINITY, -INFINITY, -INFINITY}, d4 = t4;
-        if (e0 < V) {
-          t4 = reinterpret_cast<const f32x4*>(trow)[e0 >> 2];
-          if (residual) d4 = reinterpret_cast<const f32x4*>(drow)[e0 >> 2];
-        }
-#pragma unroll
-        for (int k = 0; k < 4; ++k) {
-          tv[k] = t4[k];
-          dv[k] = d4[k];
-        }
-      } else {
-#pragma unroll
-        for (int k = 0; k < 4; ++k) {
-          const int e = e0 + k;
-          tv[k] = e < V ? trow[e] : -INFINITY;
-          dv[k] = (e < V && residual) ? drow[e] : -INFINITY;
-        }
+  float sw = 0.f, spt = 0.f;
+  if (!bad) {
+    const float* trow = a.target + ((size_t)b * N + r) * V;
+    const float* drow = a.draft + ((size_t)b * N + r) * V;
+    const float tm = d.m[0][r];
+    const float tinv = (float)(1.0 / d.s[0][r]);
+    const float dm = residual ? d.m[1][r] : 0.f;
+    const float dinv = residual ? (float)(1.0 / d.s[1][r]) : 0.f;
+    const int e0 = q * kRaceChunk + 4 * tid;
+    float tv[4], dv[4];
+    if (VEC4) {
+      f32x4 t4 = {-INFINITY, -INFINITY, -INFINITY, -INFINITY}, d4 = t4;
+      if (e0 < V) {
+        t4 = reinterpret_cast<const f32x4*>(trow)[e0 >> 2];
+        if (residual) d4 = reinterpret_cast<const f32x4*>(drow)[e0 >> 2];
       }
 #pragma unroll
       for (int k = 0; k < 4; ++k) {
-        const float pt = fast_exp2((tv[k] - tm) * kLog2e) * tinv;
-        const float pd = residual ? fast_exp2((dv[k] - dm) * kLog2e) * dinv : 0.f;
-        spt += pt;
-        sw += fmaxf(pt - pd, 0.f);
+        tv[k] = t4[k];
+        dv[k] = d4[k];
+      }
+    } else {
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        const int e = e0 + k;
+        tv[k] = e < V ? trow[e] : -INFINITY;
+        dv[k] = (e < V && residual) ? drow[e] : -INFINITY;
       }
     }
-    const double tw = block_sum((double)sw, redd);
-    const double tp = block_sum((double)spt, redd);
-    if (tid == 0) {
-      double* o = a.race_w + ((size_t)b * a.n_race + q) * 2;
-      o[0] = tw;
-      o[1] = tp;
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      const float pt = fast_exp2((tv[k] - tm) * kLog2e) * tinv;
+      const float pd = residual ? fast_exp2((dv[k] - dm) * kLog2e) * dinv : 0.f;
+      spt += pt;
+      sw += fmaxf(pt - pd, 0.f);
     }
+  }
+  const double tw = block_sum((double)sw, redd);
+  const double tp = block_sum((double)spt, redd);
+  if (tid == 0) {
+    double* o = a.race_w + ((size_t)b * a.n_race + q) * 2;
+    o[0] = tw;
+    o[1] = tp;
   }
 }
 
@@ -387,9 +418,9 @@ __global__ __launch_bounds__(kSampleThreads) void sample_race(SampleArgs a) {
     }
     return;
   }
-  const int r = dec[4 + len - 1];
-  const double* lz = reinterpret_cast<const double*>(a.decision_lz) + (size_t)b * 2;
-  const double lzt = lz[0], lzd = lz[1];
+  const int r = dec[3];
+  const double* st = a.decision_lz + (size_t)b * 2;
+  const double lzt = st[0], lzd = st[1];
   const float* trow = a.target + ((size_t)b * N + r) * V;
   const float* drow = a.draft + ((size_t)b * N + r) * V;
 
@@ -477,10 +508,7 @@ SamplePlan plan_sample(int32_t B, int32_t N, int32_t V) {
   p.vchunk = kStatsChunk;
   p.n_vchunks = (V + kStatsChunk - 1) / kStatsChunk;
   p.n_race = (V + kRaceChunk - 1) / kRaceChunk;
-  long long groups = (512 + (long long)B - 1) / (B > 0 ? B : 1);
-  if (groups > p.n_race) groups = p.n_race;
-  if (groups < 1) groups = 1;
-  p.n_groups = (int)groups;
+  p.n_groups = p.n_race;   // one race chunk per residual work-group
   p.dec_stride = 4 + 2 * N;
   const size_t rows = (size_t)B * 2 * N * p.n_vchunks;
   p.off_m = 0;

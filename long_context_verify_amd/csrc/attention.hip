@@ -182,13 +182,13 @@ __device__ __forceinline__ void window_append(const AttnArgs& a, const UnitGeom&
 // ---------------------------------------------------------------------------
 // bf16 MFMA split kernel.  QB = MFMA query blocks (16 rows each) per slice.
 // ---------------------------------------------------------------------------
-template <int D, int QB, bool WINDOW>
-__global__ __launch_bounds__(kThreads, 2) void attn_split_mfma(AttnArgs a) {
+template <int D, int QB, bool WINDOW, int NW = kWaves>
+__global__ __launch_bounds__(NW * kWave, 8 / NW) void attn_split_mfma(AttnArgs a) {
   constexpr int DS = D / 32;             // MFMA k-steps over the head dim for S
   constexpr int SR = 16 * QB;            // query rows per slice
   constexpr int LDS_STRIDE = D + 1;
-  __shared__ float lds_o[kWaves][SR][LDS_STRIDE];
-  __shared__ float lds_ml[kWaves][SR][2];
+  __shared__ float lds_o[NW][SR][LDS_STRIDE];
+  __shared__ float lds_ml[NW][SR][2];
   __shared__ bf16x8 lds_q[QB][DS][kWave];
 
   int unit, split, qs;
@@ -298,9 +298,11 @@ __global__ __launch_bounds__(kThreads, 2) void attn_split_mfma(AttnArgs a) {
     bf16x8 pop[QB];
 #pragma unroll
     for (int qb = 0; qb < QB; ++qb) {
+      // Raw scores; the softmax scale (> 0, in log2 units) is applied to the
+      // max and folded into the exponent's FMA.
       float sv[8];
 #pragma unroll
-      for (int t = 0; t < 8; ++t) sv[t] = sacc[qb][t >> 2][t & 3] * a.scale_log2;
+      for (int t = 0; t < 8; ++t) sv[t] = sacc[qb][t >> 2][t & 3];
       if (need_mask) {
 #pragma unroll
         for (int t = 0; t < 8; ++t) {
@@ -315,7 +317,7 @@ __global__ __launch_bounds__(kThreads, 2) void attn_split_mfma(AttnArgs a) {
       float cm = sv[0];
 #pragma unroll
       for (int t = 1; t < 8; ++t) cm = fmaxf(cm, sv[t]);
-      cm = xgroup_max(cm);
+      cm = xgroup_max(cm) * a.scale_log2;
       const float mn = fmaxf(m[qb], cm);
       const float mu = (mn == -INFINITY) ? 0.f : mn;
       const float alpha = fast_exp2(m[qb] - mu);
@@ -324,7 +326,7 @@ __global__ __launch_bounds__(kThreads, 2) void attn_split_mfma(AttnArgs a) {
       float ps = 0.f;
 #pragma unroll
       for (int t = 0; t < 8; ++t) {
-        p[t] = fast_exp2(sv[t] - mu);
+        p[t] = fast_exp2(fmaf(sv[t], a.scale_log2, -mu));
         ps += p[t];
       }
       lsum[qb] = lsum[qb] * alpha + ps;
@@ -345,7 +347,8 @@ __global__ __launch_bounds__(kThreads, 2) void attn_split_mfma(AttnArgs a) {
       for (int e = 0; e < 4; ++e) {
         const uint32_t lo = vraw[2 * e][j >> 1];
         const uint32_t hi = vraw[2 * e + 1][j >> 1];
-        w[e] = (j & 1) ? ((lo >> 16) | (hi & 0xffff0000u)) : ((lo & 0xffffu) | (hi << 16));
+        // one byte-select per dword: low (even j) or high (odd j) halves of lo, hi
+        w[e] = __builtin_amdgcn_perm(hi, lo, (j & 1) ? 0x07060302u : 0x05040100u);
       }
       vop[j] = __builtin_bit_cast(bf16x8, w);
     }
@@ -363,14 +366,14 @@ __global__ __launch_bounds__(kThreads, 2) void attn_split_mfma(AttnArgs a) {
     load_v(c * kChunk, vraw);
     if constexpr (WINDOW) {
       // A few chunks per wave: peel the last one so nothing is read twice.
-      for (; c + kWaves < c1; c += kWaves)
-        chunk_step(std::true_type{}, c * kChunk, (c + kWaves) * kChunk);
+      for (; c + NW < c1; c += NW)
+        chunk_step(std::true_type{}, c * kChunk, (c + NW) * kChunk);
       chunk_step(std::false_type{}, c * kChunk, 0);
     } else {
       // Tens of chunks per wave: a branch-free loop whose last iteration
       // re-reads its own chunk schedules better than the peeled form.
-      for (; c < c1; c += kWaves)
-        chunk_step(std::true_type{}, c * kChunk, (c + kWaves < c1 ? c + kWaves : c) * kChunk);
+      for (; c < c1; c += NW)
+        chunk_step(std::true_type{}, c * kChunk, (c + NW < c1 ? c + NW : c) * kChunk);
     }
   }
 
@@ -401,15 +404,15 @@ __global__ __launch_bounds__(kThreads, 2) void attn_split_mfma(AttnArgs a) {
   float* wml = a.ws_ml + part * SR * 2;
   const bool direct = a.n_splits == 1;
   const size_t orow0 = (size_t)(u.b * a.Hq + u.hk * a.g) * a.n_q + (size_t)qs * SR;
-  for (int idx = threadIdx.x; idx < SR * D; idx += kThreads) {
+  for (int idx = threadIdx.x; idx < SR * D; idx += NW * kWave) {
     const int row = idx / D, d = idx - row * D;
     float mx = -INFINITY;
 #pragma unroll
-    for (int w = 0; w < kWaves; ++w) mx = fmaxf(mx, lds_ml[w][row][0]);
+    for (int w = 0; w < NW; ++w) mx = fmaxf(mx, lds_ml[w][row][0]);
     const float mu = (mx == -INFINITY) ? 0.f : mx;
     float o = 0.f, l = 0.f;
 #pragma unroll
-    for (int w = 0; w < kWaves; ++w) {
+    for (int w = 0; w < NW; ++w) {
       const float sc = fast_exp2(lds_ml[w][row][0] - mu);
       o += sc * lds_o[w][row][d];
       l += sc * lds_ml[w][row][1];
@@ -436,20 +439,22 @@ __global__ __launch_bounds__(kThreads, 2) void attn_split_mfma(AttnArgs a) {
 //
 // Each wave owns 32 query rows (two MFMA blocks, Q in registers); the
 // work-group covers WAVES*32 rows of one (sequence, kv head) unit, so one
-// pass over the keys serves them all.  Chunks of 32 keys (16 KB) are copied
+// pass over the keys serves them all.  Chunks of 64 keys (32 KB) are copied
 // HBM -> LDS with direct-to-LDS loads (global_load_lds_dwordx4: lane l's 16
-// bytes land at base + 16 l), NBUF-1 chunks ahead of the one being computed,
-// into a ring of NBUF tiles; one barrier per chunk.  A tile holds
-//   K: 8 operand units of 1 KB in MFMA A-operand order (unit kb*4+s, lane
+// bytes land at base + 16 l), two chunks ahead of the one being computed,
+// into a ring of three tiles; one barrier per chunk.  A tile holds
+//   K: 16 operand units of 1 KB in MFMA A-operand order (unit kb*4+s, lane
 //      (h,r) = K[16 kb + r][32 s + 8 h .. +8]) -- read back conflict-free;
-//   V: 32 rows x 256 B, row-major -- each wave reads its eight 16-byte row
-//      pieces and transposes them in registers as in the streaming kernel.
-// The running max is only moved (and O rescaled) when a row's chunk max
-// exceeds it by more than 2^8 (log2 domain); otherwise the exponentials are
-// taken against the old max and stay below 256, which keeps the rescale off
-// the VALU in the common case.
+//   V: 64 rows x 256 B, row-major -- each wave reads its 16-byte row pieces
+//      and transposes them in registers as in the streaming kernel.
+// A chunk is two 32-key halves; the softmax of a row runs once per chunk over
+// its 16 scores per lane.  The running max is only moved (and O rescaled)
+// when a chunk exceeds it by more than 2^8 (log2 domain); otherwise the
+// exponentials are taken against the old max and stay below 256, which keeps
+// the rescale off the VALU in the common case.
 // ---------------------------------------------------------------------------
-constexpr int kTreeNBuf = 4;
+constexpr int kTreeChunk = 64;        // keys per chunk
+constexpr int kTreeNBuf = 3;          // LDS tiles in the ring
 constexpr float kRescaleTau = 8.0f;   // log2 units
 
 __device__ __forceinline__ void lds_dma16(const void* src, void* lds_base) {
@@ -469,11 +474,11 @@ __device__ __forceinline__ void wait_vmcnt(int n) {
 }
 
 template <int WAVES>
-__global__ __launch_bounds__(WAVES * kWave, 8 / WAVES) void attn_tree_mfma(AttnArgs a) {
+__global__ __launch_bounds__(WAVES * kWave, 1) void attn_tree_mfma(AttnArgs a) {
   constexpr int D = 128, DS = 4, QB = 2;
   constexpr int SR = WAVES * 32;              // query rows per work-group
-  constexpr int TILE = 16384;                 // bytes per chunk (K 8 KB + V 8 KB)
-  constexpr int UPW = 16 / WAVES;             // 1 KB load units per wave per chunk
+  constexpr int TILE = 32768;                 // bytes per chunk (K 16 KB + V 16 KB)
+  constexpr int UPW = 32 / WAVES;             // 1 KB load units per wave per chunk
   __shared__ __attribute__((aligned(16))) char tiles[kTreeNBuf][TILE];
 
   int unit, split, qs;
@@ -503,26 +508,28 @@ __global__ __launch_bounds__(WAVES * kWave, 8 / WAVES) void attn_tree_mfma(AttnA
     anc[qb] = live ? ancestor_mask(a, u.b, row % a.n_q) : 1ull;
   }
 
-  int c0, c1;
-  chunk_range(u.n_keys, split, a.n_splits, c0, c1);
+  // This split's range of 64-key chunks.
+  const long long nch = (u.n_keys + kTreeChunk - 1) / kTreeChunk;
+  const int c0 = (int)(nch * split / a.n_splits);
+  const int c1 = (int)(nch * (split + 1) / a.n_splits);
   const int last = u.n_keys - 1;
   const char* kbase_p = static_cast<const char*>(a.k) + (size_t)u.unit * a.L_cap * row_bytes;
   const char* vbase_p = static_cast<const char*>(a.v) + (size_t)u.unit * a.L_cap * row_bytes;
 
-  // This wave's share of one chunk: UPW 1 KB units out of 16 (8 K + 8 V).
+  // This wave's share of one chunk: UPW 1 KB units out of 32 (16 K + 16 V).
   auto issue = [&](int c, int buf) {
-    const int kbase = c * kChunk;
+    const int kbase = c * kTreeChunk;
     char* tile = tiles[buf];
 #pragma unroll
     for (int i = 0; i < UPW; ++i) {
       const int unit_id = wave * UPW + i;
-      if (unit_id < 8) {      // K operand unit (kb, s)
+      if (unit_id < 16) {     // K operand unit (kb, s)
         const int kb = unit_id >> 2, s = unit_id & 3;
         int key = kbase + 16 * kb + r;
         key = key < last ? key : last;
         lds_dma16(kbase_p + (size_t)key * row_bytes + (32 * s + 8 * h) * 2, tile + unit_id * 1024);
-      } else {                // V rows 4 (unit_id - 8) .. +3, 16 lanes per row
-        int key = kbase + 4 * (unit_id - 8) + (lane >> 4);
+      } else {                // V rows 4 (unit_id - 16) .. +3, 16 lanes per row
+        int key = kbase + 4 * (unit_id - 16) + (lane >> 4);
         key = key < last ? key : last;
         lds_dma16(vbase_p + (size_t)key * row_bytes + (lane & 15) * 16, tile + unit_id * 1024);
       }
@@ -552,37 +559,44 @@ __global__ __launch_bounds__(WAVES * kWave, 8 / WAVES) void attn_tree_mfma(AttnA
     if (!wave_live) continue;
 
     const char* tile = tiles[c % kTreeNBuf];
-    const int kbase = c * kChunk;
-    bf16x8 kop[2][DS];
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-      for (int s = 0; s < DS; ++s)
-        kop[kb][s] = *reinterpret_cast<const bf16x8*>(tile + (kb * 4 + s) * 1024 + lane * 16);
+    const int kbase = c * kTreeChunk;
 
-    f32x4 sacc[QB][2];
+    // S^T for both 32-key halves: sacc[qb][kb][e] = score(key 16 kb + 4 h + e, row qb*16 + r).
+    f32x4 sacc[QB][4];
 #pragma unroll
-    for (int qb = 0; qb < QB; ++qb) {
-      f32x4 acc0 = {0.f, 0.f, 0.f, 0.f}, acc1 = acc0;
+    for (int half = 0; half < 2; ++half) {
+      bf16x8 kop[2][DS];
 #pragma unroll
-      for (int s = 0; s < DS; ++s) {
-        acc0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kop[0][s], qop[qb][s], acc0, 0, 0, 0);
-        acc1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kop[1][s], qop[qb][s], acc1, 0, 0, 0);
+      for (int kk = 0; kk < 2; ++kk)
+#pragma unroll
+        for (int s = 0; s < DS; ++s)
+          kop[kk][s] = *reinterpret_cast<const bf16x8*>(
+              tile + ((2 * half + kk) * 4 + s) * 1024 + lane * 16);
+#pragma unroll
+      for (int qb = 0; qb < QB; ++qb) {
+        f32x4 acc0 = {0.f, 0.f, 0.f, 0.f}, acc1 = acc0;
+#pragma unroll
+        for (int s = 0; s < DS; ++s) {
+          acc0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kop[0][s], qop[qb][s], acc0, 0, 0, 0);
+          acc1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kop[1][s], qop[qb][s], acc1, 0, 0, 0);
+        }
+        sacc[qb][2 * half] = acc0;
+        sacc[qb][2 * half + 1] = acc1;
       }
-      sacc[qb][0] = acc0;
-      sacc[qb][1] = acc1;
     }
 
-    const bool need_mask = kbase + kChunk > u.p0;
-    bf16x8 pop[QB];
+    const bool need_mask = kbase + kTreeChunk > u.p0;
+    bf16x8 pop[QB][2];
 #pragma unroll
     for (int qb = 0; qb < QB; ++qb) {
-      float sv[8];
+      // Raw scores; the softmax scale (> 0, in log2 units) is applied to the
+      // max and folded into the exponent's FMA.
+      float sv[16];
 #pragma unroll
-      for (int t = 0; t < 8; ++t) sv[t] = sacc[qb][t >> 2][t & 3] * a.scale_log2;
+      for (int t = 0; t < 16; ++t) sv[t] = sacc[qb][t >> 2][t & 3];
       if (need_mask) {
 #pragma unroll
-        for (int t = 0; t < 8; ++t) {
+        for (int t = 0; t < 16; ++t) {
           const int key = kbase + 16 * (t >> 2) + 4 * h + (t & 3);
           const int rel = key - u.p0;
           const bool anc_ok = ((anc[qb] >> (rel & 63)) & 1ull) != 0;
@@ -592,8 +606,8 @@ __global__ __launch_bounds__(WAVES * kWave, 8 / WAVES) void attn_tree_mfma(AttnA
       }
       float cm = sv[0];
 #pragma unroll
-      for (int t = 1; t < 8; ++t) cm = fmaxf(cm, sv[t]);
-      cm = xgroup_max(cm);
+      for (int t = 1; t < 16; ++t) cm = fmaxf(cm, sv[t]);
+      cm = xgroup_max(cm) * a.scale_log2;
       const bool grow = cm > m[qb] + kRescaleTau;
       if (__any(grow)) {
         const float mn = grow ? cm : m[qb];
@@ -604,38 +618,47 @@ __global__ __launch_bounds__(WAVES * kWave, 8 / WAVES) void attn_tree_mfma(AttnA
         for (int j = 0; j < 8; ++j) oacc[qb][j] *= alpha;
       }
       const float mu = (m[qb] == -INFINITY) ? 0.f : m[qb];
-      float p[8];
+      float p[16];
       float ps = 0.f;
 #pragma unroll
-      for (int t = 0; t < 8; ++t) {
-        p[t] = fast_exp2(sv[t] - mu);
+      for (int t = 0; t < 16; ++t) {
+        p[t] = fast_exp2(fmaf(sv[t], a.scale_log2, -mu));
         ps += p[t];
       }
       lsum[qb] += ps;
-      u32x4 pk = {pack_bf16x2(p[0], p[1]), pack_bf16x2(p[2], p[3]), pack_bf16x2(p[4], p[5]),
-                  pack_bf16x2(p[6], p[7])};
-      pop[qb] = __builtin_bit_cast(bf16x8, pk);
+#pragma unroll
+      for (int half = 0; half < 2; ++half) {
+        const float* ph = p + 8 * half;
+        u32x4 pk = {pack_bf16x2(ph[0], ph[1]), pack_bf16x2(ph[2], ph[3]),
+                    pack_bf16x2(ph[4], ph[5]), pack_bf16x2(ph[6], ph[7])};
+        pop[qb][half] = __builtin_bit_cast(bf16x8, pk);
+      }
     }
 
-    u32x4 vraw[8];
 #pragma unroll
-    for (int t = 0; t < 8; ++t) {
-      const int krow = 16 * (t >> 2) + 4 * h + (t & 3);
-      vraw[t] = *reinterpret_cast<const u32x4*>(tile + 8192 + krow * 256 + r * 16);
-    }
+    for (int half = 0; half < 2; ++half) {
+      u32x4 vraw[8];
 #pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      u32x4 w;
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const uint32_t lo = vraw[2 * e][j >> 1];
-        const uint32_t hi = vraw[2 * e + 1][j >> 1];
-        w[e] = (j & 1) ? ((lo >> 16) | (hi & 0xffff0000u)) : ((lo & 0xffffu) | (hi << 16));
+      for (int t = 0; t < 8; ++t) {
+        const int krow = 32 * half + 16 * (t >> 2) + 4 * h + (t & 3);
+        vraw[t] = *reinterpret_cast<const u32x4*>(tile + 16384 + krow * 256 + r * 16);
       }
-      const bf16x8 vop = __builtin_bit_cast(bf16x8, w);
 #pragma unroll
-      for (int qb = 0; qb < QB; ++qb)
-        oacc[qb][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vop, pop[qb], oacc[qb][j], 0, 0, 0);
+      for (int j = 0; j < 8; ++j) {
+        u32x4 w;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const uint32_t lo = vraw[2 * e][j >> 1];
+          const uint32_t hi = vraw[2 * e + 1][j >> 1];
+          // one byte-select per dword: low (even j) or high (odd j) halves of lo, hi
+        w[e] = __builtin_amdgcn_perm(hi, lo, (j & 1) ? 0x07060302u : 0x05040100u);
+        }
+        const bf16x8 vop = __builtin_bit_cast(bf16x8, w);
+#pragma unroll
+        for (int qb = 0; qb < QB; ++qb)
+          oacc[qb][j] =
+              __builtin_amdgcn_mfma_f32_16x16x32_bf16(vop, pop[qb][half], oacc[qb][j], 0, 0, 0);
+      }
     }
   }
 
@@ -828,14 +851,15 @@ AttnPlan plan_attention(int32_t B, int32_t Hkv, int32_t M, int32_t D, int32_t n_
   const int chunks = ceil_div(n_keys_max, kChunk);
   // Query blocks wider than one streaming slice (candidate trees) go to the
   // LDS-shared kernel, so the K/V of a unit is read once for all its rows.
-  p.tree_waves = (mfma && !window && D == 128 && M > 32) ? (M > 128 ? 8 : 4) : 0;
+  p.tree_waves = (mfma && !window && D == 128 && M > 32) ? 8 : 0;
   p.slice_rows = p.tree_waves ? 32 * p.tree_waves : (mfma ? (M <= 16 ? 16 : 32) : kValuSlice);
   p.n_qs = ceil_div(M, p.slice_rows);
   if (num_splits > 0) {
     p.n_splits = num_splits;
   } else if (window) {
     // The draft window is a few hundred keys and latency-bound: spread it so
-    // that every wave gets one chunk.
+    // that every wave gets one chunk (measured faster than one work-group
+    // per unit, which avoids the merge kernel but serialises the chunks).
     p.n_splits = (int)(mfma ? (chunks + kWaves - 1) / kWaves : (chunks + 7) / 8);
     if (p.n_splits < 1) p.n_splits = 1;
   } else {
@@ -864,8 +888,20 @@ static hipError_t launch_split(const AttnArgs& a, spec_dtype_t dtype, hipStream_
   dim3 grid(a.grid), block(kThreads);
   if (!WINDOW && a.tree_waves == 8) {
     hipLaunchKernelGGL(attn_tree_mfma<8>, grid, dim3(512), 0, stream, a);
-  } else if (!WINDOW && a.tree_waves == 4) {
-    hipLaunchKernelGGL(attn_tree_mfma<4>, grid, dim3(256), 0, stream, a);
+  } else if (WINDOW && dtype == SPEC_BF16 && a.n_splits == 1) {
+    // One work-group per unit: 8 waves share the window and merge in LDS.
+    dim3 wblock(8 * kWave);
+    if (a.D == 128) {
+      if (a.slice_rows == 16)
+        hipLaunchKernelGGL((attn_split_mfma<128, 1, true, 8>), grid, wblock, 0, stream, a);
+      else
+        hipLaunchKernelGGL((attn_split_mfma<128, 2, true, 8>), grid, wblock, 0, stream, a);
+    } else {
+      if (a.slice_rows == 16)
+        hipLaunchKernelGGL((attn_split_mfma<64, 1, true, 8>), grid, wblock, 0, stream, a);
+      else
+        hipLaunchKernelGGL((attn_split_mfma<64, 2, true, 8>), grid, wblock, 0, stream, a);
+    }
   } else if (dtype == SPEC_BF16) {
     if (a.D == 128) {
       if (a.slice_rows == 16)

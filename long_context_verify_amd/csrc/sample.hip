@@ -16,12 +16,12 @@
 //                  (every target row and the draft rows of nodes that have
 //                  children) and writes per-chunk (max, sum of exp(x - max));
 //                  fp32 inside a thread, fp64 across threads.
-//   sample_resid   grid (race chunks, B).  Every work-group of a sequence
-//                  derives the same decision (fp64 log-normalisers, one Philox
-//                  uniform and acceptance test per node, the walk from the
-//                  root: a few hundred scalars, two memory round trips), then
-//                  the residual (or target) mass of one 1024-id chunk of the
-//                  stop row.  Group 0 stores the decision.
+//   sample_resid   grid (groups, B).  Every work-group of a sequence derives
+//                  the same decision (fp64 log-normalisers, one Philox uniform
+//                  and acceptance test per node, the walk from the root: a few
+//                  hundred scalars, two memory round trips), then the residual
+//                  (or target) mass of its 1024-id race chunks of the stop
+//                  row.  Group 0 stores the decision.
 //   sample_race    grid (B).  The two-level exponential race in fp64 at the
 //                  stop row, and the outputs.
 //
@@ -316,20 +316,21 @@ __device__ void decide_sequence(const SampleArgs& a, int b, Decision& d) {
   __syncthreads();
 }
 
-// Residual (or target) mass of one 1024-id race chunk of the stop row.  Every
-// work-group of a sequence derives the same decision; group 0 stores it.
+// Residual (or target) mass of the stop row's 1024-id race chunks q0 .. q1-1
+// of this group.  Every work-group of a sequence derives the same decision;
+// group 0 stores it.
 template <bool VEC4>
 __global__ __launch_bounds__(kSampleThreads) void sample_resid(SampleArgs a) {
   __shared__ Decision d;
   __shared__ double redd[4];
-  const int q = blockIdx.x, b = blockIdx.y;
+  const int grp = blockIdx.x, b = blockIdx.y;
   const int N = a.N, V = a.V;
   const int tid = threadIdx.x;
   decide_sequence(a, b, d);
   const bool bad = d.bad != 0;
   const bool residual = d.residual;
   const int r = d.stop;
-  if (q == 0) {
+  if (grp == 0) {
     int32_t* dec = a.decision + (size_t)b * a.dec_stride;
     for (int c = tid; c < N; c += kSampleThreads) {
       dec[4 + c] = c < d.len ? d.path[c] : -1;
@@ -345,49 +346,74 @@ __global__ __launch_bounds__(kSampleThreads) void sample_resid(SampleArgs a) {
       st[1] = residual ? d.lz[1][r] : 0.0;
     }
   }
-  float sw = 0.f, spt = 0.f;
-  if (!bad) {
-    const float* trow = a.target + ((size_t)b * N + r) * V;
-    const float* drow = a.draft + ((size_t)b * N + r) * V;
-    const float tm = d.m[0][r];
-    const float tinv = (float)(1.0 / d.s[0][r]);
-    const float dm = residual ? d.m[1][r] : 0.f;
-    const float dinv = residual ? (float)(1.0 / d.s[1][r]) : 0.f;
-    const int e0 = q * kRaceChunk + 4 * tid;
-    float tv[4], dv[4];
-    if (VEC4) {
-      f32x4 t4 = {-INFINITY, -INFINITY, -INFINITY, -INFINITY}, d4 = t4;
-      if (e0 < V) {
-        t4 = reinterpret_cast<const f32x4*>(trow)[e0 >> 2];
-        if (residual) d4 = reinterpret_cast<const f32x4*>(drow)[e0 >> 2];
-      }
+  const float* trow = a.target + ((size_t)b * N + r) * V;
+  const float* drow = a.draft + ((size_t)b * N + r) * V;
+  const float tm = d.m[0][r];
+  const float tinv = (float)(1.0 / d.s[0][r]);
+  const float dm = residual ? d.m[1][r] : 0.f;
+  const float dinv = residual ? (float)(1.0 / d.s[1][r]) : 0.f;
+  const int q0 = (int)((long long)a.n_race * grp / a.n_groups);
+  const int q1 = (int)((long long)a.n_race * (grp + 1) / a.n_groups);
+  // Per chunk: each wave reduces its lanes with shuffles and parks the two
+  // partial sums in LDS; one block pass per batch of chunks adds the waves.
+  constexpr int kBatch = 64;
+  __shared__ double part[kSampleThreads / kWave][kBatch][2];
+  const int wave = tid >> 6, lane = tid & 63;
+  for (int qb = q0; qb < q1; qb += kBatch) {
+    const int nq = min(kBatch, q1 - qb);
+    for (int i = 0; i < nq; ++i) {
+      const int q = qb + i;
+      float sw = 0.f, spt = 0.f;
+      if (!bad) {
+        const int e0 = q * kRaceChunk + 4 * tid;
+        float tv[4], dv[4];
+        if (VEC4) {
+          f32x4 t4 = {-INFINITY, -INFINITY, -INFINITY, -INFINITY}, d4 = t4;
+          if (e0 < V) {
+            t4 = reinterpret_cast<const f32x4*>(trow)[e0 >> 2];
+            if (residual) d4 = reinterpret_cast<const f32x4*>(drow)[e0 >> 2];
+          }
 #pragma unroll
-      for (int k = 0; k < 4; ++k) {
-        tv[k] = t4[k];
-        dv[k] = d4[k];
-      }
-    } else {
+          for (int k = 0; k < 4; ++k) {
+            tv[k] = t4[k];
+            dv[k] = d4[k];
+          }
+        } else {
 #pragma unroll
-      for (int k = 0; k < 4; ++k) {
-        const int e = e0 + k;
-        tv[k] = e < V ? trow[e] : -INFINITY;
-        dv[k] = (e < V && residual) ? drow[e] : -INFINITY;
+          for (int k = 0; k < 4; ++k) {
+            const int e = e0 + k;
+            tv[k] = e < V ? trow[e] : -INFINITY;
+            dv[k] = (e < V && residual) ? drow[e] : -INFINITY;
+          }
+        }
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+          const float pt = fast_exp2((tv[k] - tm) * kLog2e) * tinv;
+          const float pd = residual ? fast_exp2((dv[k] - dm) * kLog2e) * dinv : 0.f;
+          spt += pt;
+          sw += fmaxf(pt - pd, 0.f);
+        }
+      }
+      const double tw = wave_sum((double)sw);
+      const double tp = wave_sum((double)spt);
+      if (lane == 0) {
+        part[wave][i][0] = tw;
+        part[wave][i][1] = tp;
       }
     }
+    __syncthreads();
+    if (tid < nq) {
+      double tw = 0.0, tp = 0.0;
 #pragma unroll
-    for (int k = 0; k < 4; ++k) {
-      const float pt = fast_exp2((tv[k] - tm) * kLog2e) * tinv;
-      const float pd = residual ? fast_exp2((dv[k] - dm) * kLog2e) * dinv : 0.f;
-      spt += pt;
-      sw += fmaxf(pt - pd, 0.f);
+      for (int w = 0; w < kSampleThreads / kWave; ++w) {
+        tw += part[w][tid][0];
+        tp += part[w][tid][1];
+      }
+      double* o = a.race_w + ((size_t)b * a.n_race + qb + tid) * 2;
+      o[0] = tw;
+      o[1] = tp;
     }
-  }
-  const double tw = block_sum((double)sw, redd);
-  const double tp = block_sum((double)spt, redd);
-  if (tid == 0) {
-    double* o = a.race_w + ((size_t)b * a.n_race + q) * 2;
-    o[0] = tw;
-    o[1] = tp;
+    __syncthreads();
   }
 }
 
@@ -508,7 +534,13 @@ SamplePlan plan_sample(int32_t B, int32_t N, int32_t V) {
   p.vchunk = kStatsChunk;
   p.n_vchunks = (V + kStatsChunk - 1) / kStatsChunk;
   p.n_race = (V + kRaceChunk - 1) / kRaceChunk;
-  p.n_groups = p.n_race;   // one race chunk per residual work-group
+  // Residual work-groups per sequence: one race chunk each while the total
+  // stays near 1024 work-groups, more chunks each beyond (every group also
+  // re-derives the sequence's decision, so fewer groups is less overhead).
+  long long groups = (1024 + (long long)B - 1) / (B > 0 ? B : 1);
+  if (groups > p.n_race) groups = p.n_race;
+  if (groups < 1) groups = 1;
+  p.n_groups = (int)groups;
   p.dec_stride = 4 + 2 * N;
   const size_t rows = (size_t)B * 2 * N * p.n_vchunks;
   p.off_m = 0;

@@ -240,6 +240,22 @@ def main():
         ops.append(("window_attn", lambda i: op_window()))
     ops.append(("sample", op_sample))
 
+    # The commit after sampling updates lengths in place, so it is timed on
+    # its own (not part of the step) with the lengths restored before each
+    # call, outside the timed bracket.
+    kl_c = att["kv_len"].clone()
+    tl_c = None if win is None else win["total_len"].clone()
+
+    def prep_commit():
+        kl_c.copy_(att["kv_len"])
+        if tl_c is not None:
+            tl_c.copy_(win["total_len"])
+
+    def op_commit(i):
+        L.kv_commit(att["k"], att["v"], kl_c, s_out["out_count"], nq,
+                    path=s_out["out_path"] if cfg.tree else None, draft_total_len=tl_c,
+                    draft_appended=nq - 1 if tl_c is not None else 0)
+
     if args.copy_probe_mib > 0:
         n = args.copy_probe_mib << 20
         src_b = torch.ones(n, dtype=torch.uint8, device=dev)
@@ -278,8 +294,10 @@ def main():
                    "window_attn": 0 if win is None else
                    (win["k_ring"].numel() + win["k_sink"].numel()) * esz * 2,
                    "sample": smp["target"].numel() * 8}
+    op_bytes_in["kv_commit"] = 0
     op_us = {}
-    for name, f in ops:
+    preps = {"kv_commit": prep_commit}
+    for name, f in ops + [("kv_commit", op_commit)]:
         pairs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
                  for _ in range(args.steps)]
         need_flush = op_bytes_in[name] < (768 << 20)
@@ -288,6 +306,8 @@ def main():
         for i, (e0, e1) in enumerate(pairs):
             if need_flush:
                 flush.amax()
+            if name in preps:
+                preps[name]()
             e0.record(stream)
             f(args.warmup + args.steps + i)
             e1.record(stream)
@@ -314,6 +334,19 @@ def main():
     ops_report["sample"] = {"us": op_us["sample"], "bytes": sbytes,
                             "GBps": sbytes / op_us["sample"] / 1e3}
     ops_report["sample"]["hbm_frac"] = ops_report["sample"]["GBps"] / HBM_PEAK_GBPS
+    # Commit: K and V rows of the accepted path read and written back, from the
+    # first node that is not already in place (a chain moves nothing).
+    counts = s_out["out_count"].cpu().numpy()
+    moved = 0
+    if cfg.tree:
+        paths = s_out["out_path"].cpu().numpy()
+        for b in range(B):
+            c = int(counts[b])
+            j0 = next((j for j in range(c) if paths[b, j] != j), c)
+            moved += c - j0
+    cbytes = 2 * 2 * moved * Hkv * D * esz
+    ops_report["kv_commit"] = {"us": op_us["kv_commit"], "bytes": cbytes,
+                               "rows_moved": moved, "accepted_mean": float(counts.mean())}
 
     drafts = B * (N - 1)
     value = drafts / (ms_step / 1e3)

@@ -68,6 +68,7 @@ typedef enum { SPEC_F32 = 0, SPEC_BF16 = 1 } spec_dtype_t;
 #define SPEC_DEVERR_PARENT 0x2    /* parent[c] outside [-1, c) (sampling: a root other than 0) */
 #define SPEC_DEVERR_TOTAL_LEN 0x4 /* total_len[b] < 1 */
 #define SPEC_DEVERR_TOKEN 0x8     /* drafted token outside [0, V) */
+#define SPEC_DEVERR_PATH 0x10     /* commit: count or path entries not a valid accepted path */
 
 /* Largest supported query block (one 64-bit ancestor mask per node). */
 #define SPEC_MAX_NQ 64
@@ -203,6 +204,46 @@ spec_status_t spec_sample(const float* target_logits, const float* draft_logits,
                           size_t workspace_bytes, int32_t* dev_err, hipStream_t stream);
 
 size_t spec_sample_workspace(int32_t B, int32_t N, int32_t V);
+
+/*
+ * spec_kv_commit -- keep the accepted path's K/V, drop the rest.
+ *
+ * Defines: "Speculative Decoding in LLM Serving Systems" (blog notes),
+ * section "Core idea" (only the wrong guesses are rolled back), and "Guide to
+ * MagicDec", step 3 of its reference implementation (verifier and rollback
+ * controller).  Runs after spec_sample on the same round.  For every sequence
+ * b with p0 = kv_len[b] - n_q (the block's first cache position, as in
+ * spec_verify_attention) and c = count[b]:
+ *     K[b,h,p0+j,:] = old K[b,h,p0+path[b][j],:]  and the same for V, j < c;
+ *     kv_len[b]     = p0 + c;
+ * positions before p0 are not touched, positions p0+c .. are left as they are
+ * (stale, outside the new length).  The token drawn by spec_sample has no K/V
+ * yet: it is the next round's node 0.
+ *
+ *   k_cache, v_cache  [B, Hkv, L_cap, D], dtype, updated in place
+ *   kv_len            [B] int32, device, updated in place (must not be NULL)
+ *   path              [B, n_q] int32 nullable: spec_sample's out_path (N = n_q).
+ *                     NULL means a chain: the path is 0, 1, .., c-1 and no row
+ *                     moves, only kv_len changes.
+ *   count             [B] int32: spec_sample's out_count.  A sequence with
+ *                     count 0 (flagged by spec_sample) is left unchanged.
+ *   draft_total_len   [B] int32 nullable, device, updated in place: the draft
+ *                     ring's total_len (spec_window_attention).  The draft
+ *                     appended one entry per chain node 0 .. draft_appended-1
+ *                     this round; the entries of nodes >= c are dropped:
+ *                     total_len -= max(0, draft_appended - c).  Slots of
+ *                     dropped entries are reused by the next appends.
+ *   draft_appended    0 .. n_q (ignored when draft_total_len is NULL).
+ * Device-data errors (kv_len outside [n_q, L_cap]; c outside [1, n_q]; a path
+ * not starting at 0, not strictly increasing or reaching n_q; a rewind below 1)
+ * set SPEC_DEVERR_KV_LEN / _PATH / _TOTAL_LEN and leave that sequence's cache
+ * rows, kv_len and draft_total_len unchanged.
+ * D in {64, 128}; the call needs no workspace.
+ */
+spec_status_t spec_kv_commit(void* k_cache, void* v_cache, int32_t* kv_len, const int32_t* path,
+                             const int32_t* count, int32_t B, int32_t Hkv, int32_t n_q, int32_t D,
+                             int32_t L_cap, spec_dtype_t dtype, int32_t* draft_total_len,
+                             int32_t draft_appended, int32_t* dev_err, hipStream_t stream);
 
 /*
  * spec_validate_tree -- host-side check of a parent array (host pointer).

@@ -8,7 +8,9 @@ The computation lives in ``libspecverify.so`` (hand-written HIP, built from
 * ``window_attention`` -- the draft's bounded attention over sink tokens and
   a FIFO ring of the last W tokens, with an optional fused append;
 * ``spec_sample`` -- vocabulary softmax, min(1, target/draft) acceptance and
-  the residual / bonus draw.
+  the residual / bonus draw;
+* ``kv_commit`` -- after sampling, keep the accepted path's K/V right after
+  the prefix, set the new lengths, and rewind the draft ring.
 
 This package only marshals torch tensors into those calls.
 """
@@ -17,6 +19,7 @@ from .api import (  # noqa: F401
     SPEC_BF16,
     SPEC_F32,
     SpecError,
+    kv_commit,
     lib,
     sample_workspace_bytes,
     spec_sample,
@@ -30,7 +33,7 @@ from .api import (  # noqa: F401
 )
 
 __all__ = [
-    "SPEC_BF16", "SPEC_F32", "SpecError", "lib", "sample_workspace_bytes", "spec_sample",
+    "SPEC_BF16", "SPEC_F32", "SpecError", "kv_commit", "lib", "sample_workspace_bytes", "spec_sample",
     "status_str", "validate_tree", "verify_attention", "verify_attention_auto_splits",
     "verify_attention_workspace_bytes", "window_attention", "window_attention_workspace_bytes",
 ]

@@ -38,6 +38,8 @@ _SIGNATURES = {
     "spec_sample": (_i32, [_vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _u64, _u64, _vp, _vp, _vp,
                            _vp, _vp, _sz, _vp, _vp]),
     "spec_sample_workspace": (_sz, [_i32] * 3),
+    "spec_kv_commit": (_i32, [_vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _i32, _i32, _vp,
+                              _i32, _vp, _vp]),
     "spec_validate_tree": (_i32, [_vp, _i32, _i32]),
     "spec_status_str": (ctypes.c_char_p, [_i32]),
 }
@@ -220,6 +222,30 @@ def spec_sample(target_logits, draft_logits, tokens, parent=None, seed: int = 0,
     _check(st, "spec_sample")
     return {"out_tokens": out_tokens, "out_count": out_count, "out_path": out_path,
             "out_accept": out_accept}
+
+
+def kv_commit(k_cache, v_cache, kv_len, count, n_q: int, path=None, draft_total_len=None,
+              draft_appended: int = 0, dev_err=None):
+    """spec_kv_commit on torch tensors; updates k_cache, v_cache, kv_len (and
+    draft_total_len) in place.  ``path`` is [B, n_q] (spec_sample's out_path)
+    or None for a chain."""
+    _need_gpu(k_cache, v_cache, kv_len, count, path, draft_total_len, dev_err)
+    if k_cache.shape != v_cache.shape or k_cache.dtype != v_cache.dtype:
+        raise ValueError("k_cache and v_cache must match")
+    if not (k_cache.is_contiguous() and v_cache.is_contiguous()):
+        raise ValueError("caches must be contiguous")
+    for name, t in (("kv_len", kv_len), ("count", count), ("path", path),
+                    ("draft_total_len", draft_total_len)):
+        if t is not None and (t.dtype != torch.int32 or not t.is_contiguous()):
+            raise ValueError(f"{name} must be contiguous int32")
+    B, Hkv, L_cap, D = k_cache.shape
+    if path is not None and tuple(path.shape) != (B, n_q):
+        raise ValueError("path must be [B, n_q]")
+    st = lib().spec_kv_commit(
+        _p(k_cache), _p(v_cache), _p(kv_len), _p(path), _p(count), B, Hkv, int(n_q), D, L_cap,
+        _DTYPES[k_cache.dtype], _p(draft_total_len), int(draft_appended), _p(dev_err),
+        _stream(k_cache.device))
+    _check(st, "spec_kv_commit")
 
 
 def validate_tree(parent, require_single_root: bool = True) -> int:

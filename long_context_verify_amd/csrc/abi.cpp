@@ -268,4 +268,35 @@ spec_status_t spec_sample(const float* target_logits, const float* draft_logits,
   return launch_sample(a, stream) == hipSuccess ? SPEC_OK : SPEC_ERR_HIP;
 }
 
+spec_status_t spec_kv_commit(void* k_cache, void* v_cache, int32_t* kv_len, const int32_t* path,
+                             const int32_t* count, int32_t B, int32_t Hkv, int32_t n_q, int32_t D,
+                             int32_t L_cap, spec_dtype_t dtype, int32_t* draft_total_len,
+                             int32_t draft_appended, int32_t* dev_err, hipStream_t stream) {
+  spec_status_t st = verify_shape(B, Hkv, Hkv, n_q, D, L_cap, dtype, 0);
+  if (st != SPEC_OK) return st;
+  if (draft_total_len && (draft_appended < 0 || draft_appended > n_q)) return SPEC_ERR_INVALID_ARG;
+  if ((long long)B * Hkv > (1ll << 31) - 1) return SPEC_ERR_UNSUPPORTED;
+  if (B == 0) return SPEC_OK;
+  if (!aligned(k_cache, 16) || !aligned(v_cache, 16) || !aligned(kv_len, 4) ||
+      !aligned(count, 4) || !aligned_or_null(path, 4) || !aligned_or_null(draft_total_len, 4) ||
+      !aligned_or_null(dev_err, 4))
+    return SPEC_ERR_MISALIGNED;
+  CommitArgs a;
+  memset(&a, 0, sizeof(a));
+  a.k = k_cache;
+  a.v = v_cache;
+  a.kv_len = kv_len;
+  a.path = path;
+  a.count = count;
+  a.draft_total_len = draft_total_len;
+  a.draft_appended = draft_total_len ? draft_appended : 0;
+  a.B = B;
+  a.Hkv = Hkv;
+  a.n_q = n_q;
+  a.L_cap = L_cap;
+  a.row_bytes = D * (dtype == SPEC_BF16 ? 2 : 4);
+  a.dev_err = dev_err;
+  return launch_commit(a, stream) == hipSuccess ? SPEC_OK : SPEC_ERR_HIP;
+}
+
 }  // extern "C"

@@ -322,7 +322,6 @@ __device__ void decide_sequence(const SampleArgs& a, int b, Decision& d) {
 template <bool VEC4>
 __global__ __launch_bounds__(kSampleThreads) void sample_resid(SampleArgs a) {
   __shared__ Decision d;
-  __shared__ double redd[4];
   const int grp = blockIdx.x, b = blockIdx.y;
   const int N = a.N, V = a.V;
   const int tid = threadIdx.x;

@@ -98,4 +98,19 @@ struct SamplePlan {
 SamplePlan plan_sample(int32_t B, int32_t N, int32_t V);
 hipError_t launch_sample(const SampleArgs& a, hipStream_t stream);
 
+// Keeping the accepted path's K/V after a verification round.
+struct CommitArgs {
+  void* k;                  // [B, Hkv, L_cap, row_bytes]
+  void* v;
+  int32_t* kv_len;          // [B], updated in place
+  const int32_t* path;      // [B, n_q] accepted node ids, nullable (chain: identity)
+  const int32_t* count;     // [B] accepted path length
+  int32_t* draft_total_len; // [B] nullable, rewound in place
+  int32_t draft_appended;
+  int32_t B, Hkv, n_q, L_cap, row_bytes;
+  int32_t* dev_err;
+};
+
+hipError_t launch_commit(const CommitArgs& a, hipStream_t stream);
+
 }  // namespace specv

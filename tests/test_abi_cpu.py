@@ -111,6 +111,26 @@ def test_sample_argument_checks():
     assert _sample() == WORKSPACE
 
 
+def _commit(B=2, Hkv=2, n_q=5, D=128, L_cap=64, dtype=1, k=P, kv_len=P, path=NULL, count=P,
+            total=NULL, appended=0):
+    return L.lib().spec_kv_commit(k, P, kv_len, path, count, B, Hkv, n_q, D, L_cap, dtype, total,
+                                  appended, NULL, NULL)
+
+
+def test_kv_commit_argument_checks():
+    assert _commit(B=0) == OK
+    assert _commit(B=0, n_q=0) == INVALID
+    assert _commit(n_q=65) == UNSUPPORTED
+    assert _commit(D=96) == UNSUPPORTED
+    assert _commit(L_cap=4) == INVALID
+    assert _commit(dtype=7) == INVALID
+    assert _commit(total=P, appended=6) == INVALID
+    assert _commit(total=P, appended=-1) == INVALID
+    assert _commit(k=P_ODD) == MISALIGNED
+    assert _commit(kv_len=NULL) == MISALIGNED
+    assert _commit(count=NULL) == MISALIGNED
+
+
 @pytest.mark.parametrize("parent,single,expect", [
     ([-1, 0, 0, 1, 3], True, OK),
     ([-1, 0, 2], True, BAD_TREE),          # parent not before child

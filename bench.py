@@ -251,6 +251,16 @@ def main():
         if tl_c is not None:
             tl_c.copy_(win["total_len"])
 
+    d_tok = torch.empty(B, dtype=torch.int32, device=dev)
+    d_lp = torch.empty(B, dtype=torch.float32, device=dev)
+    ws_d = torch.zeros(max(L.draft_sample_workspace_bytes(B, V), 256), dtype=torch.uint8,
+                       device=dev)
+
+    def op_draft(i):
+        # One draft step: the draw of node 1 from draft row 0 of every sequence.
+        L.draft_sample(smp["draft"][:, 0], 1, seed=seed, offset=i, out_token=d_tok,
+                       out_logprob=d_lp, workspace=ws_d)
+
     def op_commit(i):
         L.kv_commit(att["k"], att["v"], kl_c, s_out["out_count"], nq,
                     path=s_out["out_path"] if cfg.tree else None, draft_total_len=tl_c,
@@ -295,9 +305,10 @@ def main():
                    (win["k_ring"].numel() + win["k_sink"].numel()) * esz * 2,
                    "sample": smp["target"].numel() * 8}
     op_bytes_in["kv_commit"] = 0
+    op_bytes_in["draft_sample"] = B * V * 4
     op_us = {}
     preps = {"kv_commit": prep_commit}
-    for name, f in ops + [("kv_commit", op_commit)]:
+    for name, f in ops + [("draft_sample", op_draft), ("kv_commit", op_commit)]:
         pairs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
                  for _ in range(args.steps)]
         need_flush = op_bytes_in[name] < (768 << 20)
@@ -334,6 +345,9 @@ def main():
     ops_report["sample"] = {"us": op_us["sample"], "bytes": sbytes,
                             "GBps": sbytes / op_us["sample"] / 1e3}
     ops_report["sample"]["hbm_frac"] = ops_report["sample"]["GBps"] / HBM_PEAK_GBPS
+    dbytes = B * V * 4
+    ops_report["draft_sample"] = {"us": op_us["draft_sample"], "bytes": dbytes,
+                                  "GBps": dbytes / op_us["draft_sample"] / 1e3}
     # Commit: K and V rows of the accepted path read and written back, from the
     # first node that is not already in place (a chain moves nothing).
     counts = s_out["out_count"].cpu().numpy()

@@ -69,6 +69,7 @@ typedef enum { SPEC_F32 = 0, SPEC_BF16 = 1 } spec_dtype_t;
 #define SPEC_DEVERR_TOTAL_LEN 0x4 /* total_len[b] < 1 */
 #define SPEC_DEVERR_TOKEN 0x8     /* drafted token outside [0, V) */
 #define SPEC_DEVERR_PATH 0x10     /* commit: count or path entries not a valid accepted path */
+#define SPEC_DEVERR_LOGITS 0x20   /* draft draw: a row with no finite logit */
 
 /* Largest supported query block (one 64-bit ancestor mask per node). */
 #define SPEC_MAX_NQ 64
@@ -204,6 +205,41 @@ spec_status_t spec_sample(const float* target_logits, const float* draft_logits,
                           size_t workspace_bytes, int32_t* dev_err, hipStream_t stream);
 
 size_t spec_sample_workspace(int32_t B, int32_t N, int32_t V);
+
+/*
+ * spec_draft_sample -- one draft-step token draw per sequence.
+ *
+ * Defines: "Guide to MagicDec", step 2 of its reference implementation (the
+ * drafter): at each draft step the draft logits of the next position go
+ * through a softmax and one token is drawn from the result; the verifier
+ * later uses the same distribution (spec_sample recomputes it from the same
+ * logits row).  The draw is an exponential race over p = softmax(l): id x
+ * scores p_x / E_x with E_x = -ln U_x, U_x = U(ctr = (x/4, node, b,
+ * 4*offset+1)) from output word x%4 (U as in spec_sample); the largest score
+ * wins, ties go to the lowest id.  The race picks x with probability p_x.
+ *
+ *   draft_logits  fp32, row b at draft_logits + b*row_stride, V entries
+ *                 (row_stride 0 = V).  With row_stride = N*V and the pointer
+ *                 at row u of spec_sample's [B, N, V] draft logits, the draw
+ *                 reads, in place, the row that u's child is drawn from.
+ *   node          id of the node being drawn (chain: draft step j draws node
+ *                 j+1); distinct nodes of one round get independent uniforms.
+ *   seed, offset  as in spec_sample (same round => same offset).
+ *   out_token     int32, out_token[b*token_stride] = drawn id (token_stride 0
+ *                 = 1; with N it writes column `node` of spec_sample's tokens
+ *                 array when out_token points at tokens + node).
+ *   out_logprob   [B] fp32 nullable: ln p of the drawn id.
+ *   workspace     spec_draft_sample_workspace(B, V) bytes.
+ * A row with no finite logit sets SPEC_DEVERR_LOGITS and gets token -1 (and
+ * a NaN log-probability).  Logits must be finite or -inf.
+ */
+spec_status_t spec_draft_sample(const float* draft_logits, int64_t row_stride, int32_t B,
+                                int32_t V, uint64_t seed, uint64_t offset, int32_t node,
+                                int32_t* out_token, int32_t token_stride, float* out_logprob,
+                                void* workspace, size_t workspace_bytes, int32_t* dev_err,
+                                hipStream_t stream);
+
+size_t spec_draft_sample_workspace(int32_t B, int32_t V);
 
 /*
  * spec_kv_commit -- keep the accepted path's K/V, drop the rest.

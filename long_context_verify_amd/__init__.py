@@ -9,6 +9,7 @@ The computation lives in ``libspecverify.so`` (hand-written HIP, built from
   a FIFO ring of the last W tokens, with an optional fused append;
 * ``spec_sample`` -- vocabulary softmax, min(1, target/draft) acceptance and
   the residual / bonus draw;
+* ``draft_sample`` -- one draft-step token draw from softmax(draft logits);
 * ``kv_commit`` -- after sampling, keep the accepted path's K/V right after
   the prefix, set the new lengths, and rewind the draft ring.
 
@@ -19,6 +20,8 @@ from .api import (  # noqa: F401
     SPEC_BF16,
     SPEC_F32,
     SpecError,
+    draft_sample,
+    draft_sample_workspace_bytes,
     kv_commit,
     lib,
     sample_workspace_bytes,
@@ -33,7 +36,8 @@ from .api import (  # noqa: F401
 )
 
 __all__ = [
-    "SPEC_BF16", "SPEC_F32", "SpecError", "kv_commit", "lib", "sample_workspace_bytes", "spec_sample",
+    "SPEC_BF16", "SPEC_F32", "SpecError", "draft_sample", "draft_sample_workspace_bytes",
+    "kv_commit", "lib", "sample_workspace_bytes", "spec_sample",
     "status_str", "validate_tree", "verify_attention", "verify_attention_auto_splits",
     "verify_attention_workspace_bytes", "window_attention", "window_attention_workspace_bytes",
 ]

@@ -38,6 +38,9 @@ _SIGNATURES = {
     "spec_sample": (_i32, [_vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _u64, _u64, _vp, _vp, _vp,
                            _vp, _vp, _sz, _vp, _vp]),
     "spec_sample_workspace": (_sz, [_i32] * 3),
+    "spec_draft_sample": (_i32, [_vp, ctypes.c_int64, _i32, _i32, _u64, _u64, _i32, _vp, _i32,
+                                 _vp, _vp, _sz, _vp, _vp]),
+    "spec_draft_sample_workspace": (_sz, [_i32, _i32]),
     "spec_kv_commit": (_i32, [_vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _i32, _i32, _vp,
                               _i32, _vp, _vp]),
     "spec_validate_tree": (_i32, [_vp, _i32, _i32]),
@@ -95,11 +98,11 @@ def _stream(device) -> ctypes.c_void_p:
     return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
 
 
-def _need_gpu(*ts):
-    for t in ts:
+def _need_gpu(*ts, strided_ok=()):
+    for i, t in enumerate(ts):
         if t is not None and not t.is_cuda:
             raise ValueError("tensors must live on a HIP device")
-        if t is not None and not t.is_contiguous():
+        if t is not None and i not in strided_ok and not t.is_contiguous():
             raise ValueError("tensors must be contiguous")
 
 
@@ -222,6 +225,42 @@ def spec_sample(target_logits, draft_logits, tokens, parent=None, seed: int = 0,
     _check(st, "spec_sample")
     return {"out_tokens": out_tokens, "out_count": out_count, "out_path": out_path,
             "out_accept": out_accept}
+
+
+def draft_sample_workspace_bytes(B, V) -> int:
+    return int(lib().spec_draft_sample_workspace(B, V))
+
+
+def draft_sample(draft_logits, node: int, seed: int = 0, offset: int = 0, out_token=None,
+                 out_logprob=None, workspace=None, dev_err=None, want_logprob: bool = True):
+    """spec_draft_sample on torch tensors.
+
+    ``draft_logits`` is [B, V] fp32 whose rows may be strided (e.g. ``x[:, u]``
+    of a [B, N, V] tensor); ``out_token`` may be a strided column of a [B, N]
+    int32 tensor.  Returns (out_token, out_logprob)."""
+    _need_gpu(draft_logits, out_token, out_logprob, dev_err, strided_ok=(0, 1))
+    if draft_logits.dtype != torch.float32 or draft_logits.dim() != 2:
+        raise ValueError("draft_logits must be a [B, V] float32 tensor")
+    if draft_logits.stride(1) != 1:
+        raise ValueError("draft_logits rows must be contiguous")
+    B, V = draft_logits.shape
+    dev = draft_logits.device
+    if out_token is None:
+        out_token = torch.empty(B, dtype=torch.int32, device=dev)
+    if out_token.dtype != torch.int32 or out_token.dim() != 1 or out_token.numel() != B:
+        raise ValueError("out_token must be [B] int32")
+    if B > 1 and (draft_logits.stride(0) < V or out_token.stride(0) < 1):
+        raise ValueError("rows of draft_logits and entries of out_token must not overlap")
+    if out_logprob is None and want_logprob:
+        out_logprob = torch.empty(B, dtype=torch.float32, device=dev)
+    ws = _workspace(draft_sample_workspace_bytes(B, V), dev, workspace)
+    st = lib().spec_draft_sample(
+        _p(draft_logits), int(draft_logits.stride(0)) if B > 1 else V, B, V,
+        int(seed) & (2**64 - 1), int(offset), int(node), _p(out_token),
+        int(out_token.stride(0)) if B > 1 else 1, _p(out_logprob), _p(ws), ws.numel(),
+        _p(dev_err), _stream(dev))
+    _check(st, "spec_draft_sample")
+    return out_token, out_logprob
 
 
 def kv_commit(k_cache, v_cache, kv_len, count, n_q: int, path=None, draft_total_len=None,

@@ -268,6 +268,53 @@ spec_status_t spec_sample(const float* target_logits, const float* draft_logits,
   return launch_sample(a, stream) == hipSuccess ? SPEC_OK : SPEC_ERR_HIP;
 }
 
+size_t spec_draft_sample_workspace(int32_t B, int32_t V) {
+  if (B < 1 || V < 1 || V > (1 << 27) || B > 65535) return 0;
+  return plan_draft(B, V).bytes;
+}
+
+spec_status_t spec_draft_sample(const float* draft_logits, int64_t row_stride, int32_t B,
+                                int32_t V, uint64_t seed, uint64_t offset, int32_t node,
+                                int32_t* out_token, int32_t token_stride, float* out_logprob,
+                                void* workspace, size_t workspace_bytes, int32_t* dev_err,
+                                hipStream_t stream) {
+  if (B < 0 || V < 1 || node < 0 || token_stride < 0) return SPEC_ERR_INVALID_ARG;
+  if (V > (1 << 27) || B > 65535) return SPEC_ERR_UNSUPPORTED;
+  if (offset >= (1ull << 30)) return SPEC_ERR_INVALID_ARG;
+  if (row_stride == 0) row_stride = V;
+  if (row_stride < V) return SPEC_ERR_INVALID_ARG;
+  if (B == 0) return SPEC_OK;
+  if (!aligned(draft_logits, 4) || !aligned(out_token, 4) || !aligned_or_null(out_logprob, 4) ||
+      !aligned_or_null(dev_err, 4))
+    return SPEC_ERR_MISALIGNED;
+  const DraftPlan p = plan_draft(B, V);
+  if (!aligned(workspace, 256) || workspace_bytes < p.bytes) return SPEC_ERR_WORKSPACE;
+  DraftArgs a;
+  memset(&a, 0, sizeof(a));
+  a.logits = draft_logits;
+  a.row_stride = row_stride;
+  a.B = B;
+  a.V = V;
+  a.key0 = (uint32_t)(seed & 0xffffffffu);
+  a.key1 = (uint32_t)(seed >> 32);
+  a.ctr3 = (uint32_t)(4 * offset + 1);
+  a.node = node;
+  a.out_token = out_token;
+  a.token_stride = token_stride ? token_stride : 1;
+  a.out_logprob = out_logprob;
+  char* ws = static_cast<char*>(workspace);
+  a.part_best = reinterpret_cast<float*>(ws + p.off_best);
+  a.part_idx = reinterpret_cast<int32_t*>(ws + p.off_idx);
+  a.part_x = reinterpret_cast<float*>(ws + p.off_x);
+  a.part_m = reinterpret_cast<float*>(ws + p.off_m);
+  a.part_s = reinterpret_cast<double*>(ws + p.off_s);
+  a.n_chunks = p.n_chunks;
+  a.dev_err = dev_err;
+  // 16-byte loads when every row starts 16-byte aligned and holds whole vectors.
+  const bool vec4 = aligned(draft_logits, 16) && V % 4 == 0 && row_stride % 4 == 0;
+  return launch_draft(a, vec4, stream) == hipSuccess ? SPEC_OK : SPEC_ERR_HIP;
+}
+
 spec_status_t spec_kv_commit(void* k_cache, void* v_cache, int32_t* kv_len, const int32_t* path,
                              const int32_t* count, int32_t B, int32_t Hkv, int32_t n_q, int32_t D,
                              int32_t L_cap, spec_dtype_t dtype, int32_t* draft_total_len,

@@ -11,11 +11,10 @@
 // The draft model's ring drops the entries of rejected drafts: it appended
 // one entry per chain node 0 .. appended-1, of which the first count survive.
 //
-// Work-group (b, kv head, K|V) stages its source rows in LDS and writes them
-// back in path order, so moves that overlap (path[j] > j) never read a row
-// that is already overwritten.  A chain's path is the identity and moves
-// nothing.  The lengths are updated by a second, tiny kernel, after every
-// move of the sequence has read the old kv_len.
+// One work-group per sequence stages the source rows of every kv head in LDS
+// before writing them back in path order, so moves that overlap
+// (path[j] > j) never read a row that is already overwritten, and then sets
+// the lengths.  A chain's path is the identity and moves nothing.
 
 #include <hip/hip_runtime.h>
 
@@ -25,81 +24,97 @@
 namespace specv {
 
 constexpr int kCommitThreads = 256;
+constexpr int kCommitBatch = 2048;   // 16-byte pieces staged per round (32 KB of LDS)
 
-// The path of sequence b, or the identity when no path is given.
-__device__ __forceinline__ int path_at(const CommitArgs& a, int b, int j) {
-  return a.path ? a.path[(size_t)b * a.n_q + j] : j;
-}
+// Validation of one sequence by one wave, all loads issued at once: lane t
+// holds path[t] (t < n_q; the identity when no path is given).  status is 0
+// when the sequence can be committed, -1 for a sequence the sampler already
+// flagged (count 0: left alone, no new error), else the error bits it earns.
+struct CommitView {
+  int status, p0, count, path;
+};
 
-// 0 when sequence b can be committed; otherwise the error bits it earns
-// (-1: a sequence the sampler already flagged, out_count == 0: left alone).
-__device__ __forceinline__ int commit_check(const CommitArgs& a, int b, int& p0, int& count) {
+__device__ __forceinline__ CommitView commit_check(const CommitArgs& a, int b) {
+  const int lane = threadIdx.x & 63;
   const int L = a.kv_len[b];
-  count = a.count[b];
-  p0 = L - a.n_q;
-  if (count == 0) return -1;
-  if (L < a.n_q || L > a.L_cap) return SPEC_DEVERR_KV_LEN;
-  if (count < 1 || count > a.n_q || path_at(a, b, 0) != 0) return SPEC_DEVERR_PATH;
-  for (int j = 1; j < count; ++j) {
-    const int pj = path_at(a, b, j);
-    if (pj <= path_at(a, b, j - 1) || pj >= a.n_q) return SPEC_DEVERR_PATH;
+  const int count = a.count[b];
+  const int T = a.draft_total_len ? a.draft_total_len[b] : 0x40000000;
+  int pj = lane;
+  if (a.path && lane < a.n_q) pj = a.path[(size_t)b * a.n_q + lane];
+  const int prev = __shfl(pj, lane > 0 ? lane - 1 : 0);
+  CommitView v{0, L - a.n_q, count, pj};
+  if (count == 0) {
+    v.status = -1;
+  } else if (L < a.n_q || L > a.L_cap) {
+    v.status = SPEC_DEVERR_KV_LEN;
+  } else if (count < 1 || count > a.n_q) {
+    v.status = SPEC_DEVERR_PATH;
+  } else {
+    // path[0] == 0, strictly increasing, below n_q.
+    const bool bad = lane < count && (lane == 0 ? pj != 0 : (pj <= prev || pj >= a.n_q));
+    if (__any(bad))
+      v.status = SPEC_DEVERR_PATH;
+    else if (a.draft_total_len && a.draft_appended > count && T - (a.draft_appended - count) < 1)
+      v.status = SPEC_DEVERR_TOTAL_LEN;
   }
-  if (a.draft_total_len && a.draft_total_len[b] - (a.draft_appended - count) < 1 &&
-      a.draft_appended > count)
-    return SPEC_DEVERR_TOTAL_LEN;
-  return 0;
+  return v;
 }
 
-__global__ __launch_bounds__(kCommitThreads) void kv_commit_move(CommitArgs a) {
-  extern __shared__ u32x4 stage[];  // [count - j0][row_bytes / 16]
-  const int unit = blockIdx.x;      // b * Hkv + kv head
-  const int b = unit / a.Hkv;
-  int p0, count;
-  if (commit_check(a, b, p0, count) != 0) return;
-  // path[j] == j up to the first moved row j0; after it path[j] > j throughout.
-  int j0 = 0;
-  while (j0 < count && path_at(a, b, j0) == j0) ++j0;
-  if (j0 == count) return;
-  const int n16 = a.row_bytes / 16;
-  char* base = static_cast<char*>(blockIdx.y ? a.v : a.k) +
-               ((size_t)unit * a.L_cap + p0) * (size_t)a.row_bytes;
-  const int total = (count - j0) * n16;
-  for (int i = threadIdx.x; i < total; i += kCommitThreads) {
-    const int j = j0 + i / n16, piece = i % n16;
-    const char* src = base + (size_t)path_at(a, b, j) * a.row_bytes;
-    stage[i] = reinterpret_cast<const u32x4*>(src)[piece];
-  }
-  __syncthreads();
-  for (int i = threadIdx.x; i < total; i += kCommitThreads) {
-    const int j = j0 + i / n16, piece = i % n16;
-    reinterpret_cast<u32x4*>(base + (size_t)j * a.row_bytes)[piece] = stage[i];
-  }
-}
-
-__global__ __launch_bounds__(kCommitThreads) void kv_commit_lengths(CommitArgs a) {
-  const int b = blockIdx.x * kCommitThreads + threadIdx.x;
-  if (b >= a.B) return;
-  int p0, count;
-  const int bad = commit_check(a, b, p0, count);
-  if (bad) {
-    if (bad > 0) report_error(a.dev_err, bad);
+// One work-group per sequence: it alone reads and writes that sequence's
+// rows and lengths, so one launch needs no ordering between work-groups.
+// The rows to move (every kv head, K and V) are staged through LDS in
+// batches of kCommitBatch 16-byte pieces: all loads of a batch, a barrier,
+// all stores, a barrier.
+__global__ __launch_bounds__(kCommitThreads) void kv_commit(CommitArgs a) {
+  __shared__ u32x4 stage[kCommitBatch];
+  const int b = blockIdx.x;
+  const CommitView cv = commit_check(a, b);
+  const int lane = threadIdx.x & 63;
+  if (cv.status != 0) {
+    if (cv.status > 0 && threadIdx.x == 0) report_error(a.dev_err, cv.status);
     return;
   }
-  a.kv_len[b] = p0 + count;
-  if (a.draft_total_len && a.draft_appended > count)
-    a.draft_total_len[b] -= a.draft_appended - count;
+  // path[j] == j up to the first moved row j0; after it path[j] > j throughout.
+  const uint64_t moved = __ballot(lane < cv.count && cv.path != lane);
+  if (moved) {
+    const int j0 = __builtin_ctzll(moved);
+    const int n16 = a.row_bytes / 16;
+    const int per_pair = (cv.count - j0) * n16;    // pieces per (kv head, K|V)
+    const int total = 2 * a.Hkv * per_pair;
+    for (int base_i = 0; base_i < total; base_i += kCommitBatch) {
+      const int n = min(kCommitBatch, total - base_i);
+      char* dst[kCommitBatch / kCommitThreads];
+#pragma unroll
+      for (int k = 0; k < kCommitBatch / kCommitThreads; ++k) {
+        const int t = k * kCommitThreads + threadIdx.x;
+        const int i = base_i + (t < n ? t : 0);
+        const int pair = i / per_pair, rem = i - pair * per_pair;
+        const int j = j0 + rem / n16, piece = rem % n16;
+        const int src_row = __shfl(cv.path, j);   // every lane takes part in the shuffle
+        char* row0 = static_cast<char*>((pair & 1) ? a.v : a.k) +
+                     (((size_t)b * a.Hkv + (pair >> 1)) * a.L_cap + cv.p0) * (size_t)a.row_bytes +
+                     (size_t)piece * 16;
+        dst[k] = row0 + (size_t)j * a.row_bytes;
+        if (t < n) stage[t] = *reinterpret_cast<const u32x4*>(row0 + (size_t)src_row * a.row_bytes);
+      }
+      __syncthreads();
+#pragma unroll
+      for (int k = 0; k < kCommitBatch / kCommitThreads; ++k) {
+        const int t = k * kCommitThreads + threadIdx.x;
+        if (t < n) *reinterpret_cast<u32x4*>(dst[k]) = stage[t];
+      }
+      __syncthreads();
+    }
+  }
+  if (threadIdx.x == 0) {
+    a.kv_len[b] = cv.p0 + cv.count;
+    if (a.draft_total_len && a.draft_appended > cv.count)
+      a.draft_total_len[b] -= a.draft_appended - cv.count;
+  }
 }
 
 hipError_t launch_commit(const CommitArgs& a, hipStream_t stream) {
-  dim3 block(kCommitThreads);
-  if (a.path) {
-    const size_t lds = (size_t)a.n_q * a.row_bytes;
-    hipLaunchKernelGGL(kv_commit_move, dim3(a.B * a.Hkv, 2), block, lds, stream, a);
-    const hipError_t e = hipGetLastError();
-    if (e != hipSuccess) return e;
-  }
-  hipLaunchKernelGGL(kv_commit_lengths, dim3((a.B + kCommitThreads - 1) / kCommitThreads), block,
-                     0, stream, a);
+  hipLaunchKernelGGL(kv_commit, dim3(a.B), dim3(kCommitThreads), 0, stream, a);
   return hipGetLastError();
 }
 

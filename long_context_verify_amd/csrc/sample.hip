@@ -32,6 +32,7 @@
 //   accept test of node c:      (c, 0, b, 4*offset + 0), word 0
 //   race over chunks at row r:  (chunk, r, b, 4*offset + 2), word 0
 //   race over ids in a chunk:   (id / 4, r, b, 4*offset + 3), word id % 4
+//   draft-step draw of node c:  (id / 4, c, b, 4*offset + 1), word id % 4
 
 #include <hip/hip_runtime.h>
 
@@ -43,6 +44,7 @@ namespace specv {
 constexpr int kSampleThreads = 256;
 constexpr int kRaceChunk = 1024;
 constexpr int kStatsChunk = 8192;   // ids per stats work-group (32 per thread)
+constexpr int kDraftChunk = 2048;   // ids per draft-draw work-group (8 per thread)
 
 __device__ __forceinline__ void philox4x32_10(uint32_t& c0, uint32_t& c1, uint32_t& c2,
                                               uint32_t& c3, uint32_t k0, uint32_t k1) {
@@ -563,6 +565,170 @@ hipError_t launch_sample(const SampleArgs& a, hipStream_t stream) {
     hipLaunchKernelGGL(sample_resid<false>, g2, blk, 0, stream, a);
     hipLaunchKernelGGL(sample_race<false>, g3, blk, 0, stream, a);
   }
+  return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------
+// Draft-step draw ("Guide to MagicDec", step 2 of its reference
+// implementation: softmax of the draft logits, then one multinomial draw).
+// An exponential race over softmax(l): id x scores p_x / E_x with
+// E_x = -ln U_x, the largest score wins (ties: lowest id).  In log2 units the
+// score is l_x log2(e) - log2(-log2 U_x) plus a constant, so the race needs
+// neither the row max nor the normaliser; those are still gathered (per
+// chunk: max and sum of exp2) for the drawn token's log-probability.
+// ---------------------------------------------------------------------------
+// Arg-max of (score, id) with ties to the lowest id, carrying the winner's
+// scaled logit along.
+struct RaceBest {
+  float s;
+  int i;
+  float x;
+};
+
+__device__ __forceinline__ void better_f(RaceBest& r, float s2, int i2, float x2) {
+  if (s2 > r.s || (s2 == r.s && i2 < r.i)) r = RaceBest{s2, i2, x2};
+}
+
+__device__ __forceinline__ void block_argmax_f(RaceBest& r, RaceBest* red) {
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) {
+    const float s2 = __shfl_xor(r.s, off);
+    const int i2 = __shfl_xor(r.i, off);
+    const float x2 = __shfl_xor(r.x, off);
+    better_f(r, s2, i2, x2);
+  }
+  const int w = threadIdx.x >> 6;
+  __syncthreads();
+  if ((threadIdx.x & 63) == 0) red[w] = r;
+  __syncthreads();
+  r = red[0];
+#pragma unroll
+  for (int k = 1; k < 4; ++k) better_f(r, red[k].s, red[k].i, red[k].x);
+}
+
+// grid (chunks of 2048 ids, B).  Thread t holds the id groups
+// g = chunk*512 + t + 256*i (i < 2), four consecutive ids per group, so one
+// Philox call serves one 16-byte load.  Small chunks give many work-groups:
+// the Philox rounds, not the bytes, set the time of a 0.5 MB row.
+template <bool VEC4>
+__global__ __launch_bounds__(kSampleThreads) void draft_partial(DraftArgs a) {
+  __shared__ float redf[4];
+  __shared__ double redd[4];
+  __shared__ RaceBest redr[4];
+  const int chunk = blockIdx.x, b = blockIdx.y;
+  const float* row = a.logits + (size_t)b * a.row_stride;
+  constexpr int GROUPS = kDraftChunk / 4 / kSampleThreads;  // 2
+  const int g0 = chunk * (kDraftChunk / 4) + threadIdx.x;
+  float x[4 * GROUPS];
+#pragma unroll
+  for (int i = 0; i < GROUPS; ++i) {
+    const int e = 4 * (g0 + kSampleThreads * i);
+    if (VEC4) {
+      f32x4 v = {-INFINITY, -INFINITY, -INFINITY, -INFINITY};
+      if (e < a.V) v = reinterpret_cast<const f32x4*>(row)[e >> 2];
+#pragma unroll
+      for (int k = 0; k < 4; ++k) x[4 * i + k] = v[k] * kLog2e;
+    } else {
+#pragma unroll
+      for (int k = 0; k < 4; ++k) x[4 * i + k] = e + k < a.V ? row[e + k] * kLog2e : -INFINITY;
+    }
+  }
+  // Race: one Philox block per group of four ids.
+  RaceBest best{-INFINITY, 0x7fffffff, -INFINITY};
+#pragma unroll
+  for (int i = 0; i < GROUPS; ++i) {
+    const int g = g0 + kSampleThreads * i;
+    if (4 * g >= a.V) break;
+    uint32_t c0 = (uint32_t)g, c1 = (uint32_t)a.node, c2 = (uint32_t)b, c3 = a.ctr3;
+    philox4x32_10(c0, c1, c2, c3, a.key0, a.key1);
+    const uint32_t w[4] = {c0, c1, c2, c3};
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      // (2 (w >> 9) + 1) 2^-24 is exact in fp32 and lies in (0, 1).
+      const float u = (float)(2u * (w[k] >> 9) + 1u) * 5.9604644775390625e-08f;
+      const float s = x[4 * i + k] - __builtin_amdgcn_logf(-__builtin_amdgcn_logf(u));
+      better_f(best, s, 4 * g + k, x[4 * i + k]);   // ids past V carry x = -inf: never beat a real id
+    }
+  }
+  block_argmax_f(best, redr);
+  float mx = x[0];
+#pragma unroll
+  for (int i = 1; i < 4 * GROUPS; ++i) mx = fmaxf(mx, x[i]);
+  mx = block_max(mx, redf);
+  float sum = 0.f;
+  if (mx != -INFINITY) {
+#pragma unroll
+    for (int i = 0; i < 4 * GROUPS; ++i) sum += fast_exp2(x[i] - mx);
+  }
+  const double tot = block_sum((double)sum, redd);
+  if (threadIdx.x == 0) {
+    const size_t o = (size_t)b * a.n_chunks + chunk;
+    a.part_best[o] = best.s;
+    a.part_idx[o] = best.i;
+    a.part_x[o] = best.x;
+    a.part_m[o] = mx;
+    a.part_s[o] = tot;
+  }
+}
+
+// grid (B).  Combines the chunk partials of one row: the race winner (chunks
+// are in id order, so ties still go to the lowest id), the fp64 log2
+// normaliser, and the winner's log-probability.
+__global__ __launch_bounds__(kSampleThreads) void draft_finish(DraftArgs a) {
+  __shared__ float redf[4];
+  __shared__ double redd[4];
+  __shared__ RaceBest redr[4];
+  const int b = blockIdx.x;
+  const size_t o = (size_t)b * a.n_chunks;
+  float mx = -INFINITY;
+  RaceBest best{-INFINITY, 0x7fffffff, -INFINITY};
+  for (int c = threadIdx.x; c < a.n_chunks; c += kSampleThreads) {
+    better_f(best, a.part_best[o + c], a.part_idx[o + c], a.part_x[o + c]);
+    mx = fmaxf(mx, a.part_m[o + c]);
+  }
+  block_argmax_f(best, redr);
+  mx = block_max(mx, redf);
+  double sum = 0.0;
+  if (mx != -INFINITY)
+    for (int c = threadIdx.x; c < a.n_chunks; c += kSampleThreads) {
+      const float m = a.part_m[o + c];
+      if (m != -INFINITY) sum += a.part_s[o + c] * exp2((double)m - (double)mx);
+    }
+  sum = block_sum(sum, redd);
+  if (threadIdx.x == 0) {
+    int tok = best.i;
+    float lp = NAN;
+    if (best.s == -INFINITY || best.s != best.s || tok < 0 || tok >= a.V) {
+      tok = -1;
+      report_error(a.dev_err, SPEC_DEVERR_LOGITS);
+    } else {
+      lp = (float)(((double)best.x - (double)mx - log2(sum)) * 0.6931471805599453);
+    }
+    a.out_token[(size_t)b * a.token_stride] = tok;
+    if (a.out_logprob) a.out_logprob[b] = lp;
+  }
+}
+
+DraftPlan plan_draft(int32_t B, int32_t V) {
+  DraftPlan p{};
+  p.n_chunks = (V + kDraftChunk - 1) / kDraftChunk;
+  const size_t n = (size_t)B * p.n_chunks;
+  p.off_best = 0;
+  p.off_idx = align256(p.off_best + n * sizeof(float));
+  p.off_x = align256(p.off_idx + n * sizeof(int32_t));
+  p.off_m = align256(p.off_x + n * sizeof(float));
+  p.off_s = align256(p.off_m + n * sizeof(float));
+  p.bytes = align256(p.off_s + n * sizeof(double));
+  return p;
+}
+
+hipError_t launch_draft(const DraftArgs& a, bool vec4, hipStream_t stream) {
+  dim3 g1(a.n_chunks, a.B), g2(a.B), blk(kSampleThreads);
+  if (vec4)
+    hipLaunchKernelGGL(draft_partial<true>, g1, blk, 0, stream, a);
+  else
+    hipLaunchKernelGGL(draft_partial<false>, g1, blk, 0, stream, a);
+  hipLaunchKernelGGL(draft_finish, g2, blk, 0, stream, a);
   return hipGetLastError();
 }
 

@@ -113,4 +113,32 @@ struct CommitArgs {
 
 hipError_t launch_commit(const CommitArgs& a, hipStream_t stream);
 
+// One draft-step token draw per sequence.
+struct DraftArgs {
+  const float* logits;      // row b at logits + b * row_stride, V entries
+  int64_t row_stride;
+  int32_t B, V;
+  uint32_t key0, key1;
+  uint32_t ctr3;            // 4 * offset + 1
+  int32_t node;
+  int32_t* out_token;       // out_token[b * token_stride]
+  int32_t token_stride;
+  float* out_logprob;       // nullable, [B]
+  float* part_best;         // [B][n_chunks] best race score (log2 units)
+  int32_t* part_idx;        // [B][n_chunks] its id
+  float* part_x;            // [B][n_chunks] its logit * log2(e)
+  float* part_m;            // [B][n_chunks] max of logit * log2(e)
+  double* part_s;           // [B][n_chunks] sum of exp2(x - max)
+  int32_t n_chunks;
+  int32_t* dev_err;
+};
+
+struct DraftPlan {
+  int32_t n_chunks;
+  size_t off_best, off_idx, off_x, off_m, off_s, bytes;
+};
+
+DraftPlan plan_draft(int32_t B, int32_t V);
+hipError_t launch_draft(const DraftArgs& a, bool vec4, hipStream_t stream);
+
 }  // namespace specv

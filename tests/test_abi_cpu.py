@@ -111,6 +111,26 @@ def test_sample_argument_checks():
     assert _sample() == WORKSPACE
 
 
+def _draft(B=2, V=1000, stride=0, node=1, offset=0, logits=P, tok=P, tstride=0, ws_bytes=0):
+    return L.lib().spec_draft_sample(logits, stride, B, V, 1, offset, node, tok, tstride, NULL, P,
+                                     ws_bytes, NULL, NULL)
+
+
+def test_draft_sample_argument_checks():
+    assert _draft(B=0) == OK
+    assert _draft(V=0) == INVALID
+    assert _draft(V=(1 << 27) + 1) == UNSUPPORTED
+    assert _draft(node=-1) == INVALID
+    assert _draft(offset=1 << 30) == INVALID
+    assert _draft(stride=999) == INVALID
+    assert _draft(tstride=-1) == INVALID
+    assert _draft(logits=NULL) == MISALIGNED
+    assert _draft(tok=ctypes.c_void_p(0x10002)) == MISALIGNED
+    assert _draft() == WORKSPACE
+    assert L.draft_sample_workspace_bytes(8, 128256) >= 8 * 16 * 20
+    assert L.draft_sample_workspace_bytes(0, 10) == 0
+
+
 def _commit(B=2, Hkv=2, n_q=5, D=128, L_cap=64, dtype=1, k=P, kv_len=P, path=NULL, count=P,
             total=NULL, appended=0):
     return L.lib().spec_kv_commit(k, P, kv_len, path, count, B, Hkv, n_q, D, L_cap, dtype, total,

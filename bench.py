@@ -87,6 +87,9 @@ def parse():
     p.add_argument("--workload", default="llama8b_32k_chain")
     p.add_argument("--cpu-budget", type=float, default=12.0,
                    help="seconds of oracle work for the CPU baseline (0 disables it)")
+    p.add_argument("--page-size", type=int, default=0,
+                   help="read the verify cache through a block table of pages of this many "
+                        "keys (a seeded shuffle of the contiguous cache); 0 = contiguous")
     p.add_argument("--copy-probe-mib", type=int, default=0,
                    help="also run plain device copies of this many MiB (calibrates HBM "
                         "byte counters: the copy reads and writes exactly this much)")
@@ -225,9 +228,20 @@ def main():
     ws_s = torch.zeros(max(L.sample_workspace_bytes(B, N, V), 256), dtype=torch.uint8, device=dev)
     seed = 0x5EED0000 + cfg.seed
 
+    if args.page_size:
+        from workloads import make_paged_inputs
+        pg = make_paged_inputs(att["k"], att["v"], att["kv_len"], args.page_size, seed=cfg.seed)
+        ws_v = torch.zeros(max(L.verify_attention_paged_workspace_bytes(
+            B, Hq, Hkv, nq, D, Lk, args.page_size, dt), 256), dtype=torch.uint8, device=dev)
+
     def op_verify():
-        L.verify_attention(att["q"], att["k"], att["v"], att["kv_len"], parent=par_t, out=out,
-                           lse=lse, workspace=ws_v)
+        if args.page_size:
+            L.verify_attention_paged(att["q"], pg["k_pages"], pg["v_pages"], pg["block_table"],
+                                     att["kv_len"], Lk, parent=par_t, out=out, lse=lse,
+                                     workspace=ws_v)
+        else:
+            L.verify_attention(att["q"], att["k"], att["v"], att["kv_len"], parent=par_t,
+                               out=out, lse=lse, workspace=ws_v)
 
     def op_window():
         L.window_attention(win["q"], win["k_ring"], win["v_ring"], win["k_sink"], win["v_sink"],
@@ -395,7 +409,9 @@ def main():
         "config": {"workload": cfg.name, "batch": B, "q_heads": Hq, "kv_heads": Hkv,
                    "head_dim": D, "kv_len": Lk, "block": "tree" if cfg.tree else "chain",
                    "gamma": nq - 1, "draft_window": cfg.window, "sinks": cfg.sinks,
-                   "vocab": V, "parallelism": "single-gpu"},
+                   "vocab": V, "kv_layout": (f"paged, {args.page_size} keys per page"
+                                             if args.page_size else "contiguous"),
+                   "parallelism": "single-gpu"},
         "verify_attn_GBps": ops_report["verify_attn"]["GBps"],
         "verify_attn_hbm_frac": ops_report["verify_attn"]["hbm_frac"],
         "roofline": {

@@ -70,6 +70,7 @@ typedef enum { SPEC_F32 = 0, SPEC_BF16 = 1 } spec_dtype_t;
 #define SPEC_DEVERR_TOKEN 0x8     /* drafted token outside [0, V) */
 #define SPEC_DEVERR_PATH 0x10     /* commit: count or path entries not a valid accepted path */
 #define SPEC_DEVERR_LOGITS 0x20   /* draft draw: a row with no finite logit */
+#define SPEC_DEVERR_PAGE 0x40     /* paged verify: a block_table entry outside [0, num_pages) */
 
 /* Largest supported query block (one 64-bit ancestor mask per node). */
 #define SPEC_MAX_NQ 64
@@ -125,6 +126,45 @@ size_t spec_verify_attention_workspace(int32_t B, int32_t Hq, int32_t Hkv, int32
 /* Split count spec_verify_attention uses when num_splits == 0 (0 on invalid sizes). */
 int32_t spec_verify_attention_auto_splits(int32_t B, int32_t Hq, int32_t Hkv, int32_t n_q,
                                           int32_t D, int32_t L_cap, spec_dtype_t dtype);
+
+/*
+ * spec_verify_attention_paged -- spec_verify_attention over a paged KV cache.
+ *
+ * Defines: the same attention as spec_verify_attention.  "Guide to MagicDec"
+ * places the target's verification in serving engines under continuous
+ * batching (sections "High-Concurrency Serving Throughput and VRAM Footprint"
+ * and 4, "High-Concurrency Memory Scheduling in Serving Engines": vLLM /
+ * TensorRT-LLM schedulers), whose KV caches are lists of fixed-size blocks.
+ * Here:
+ *
+ *   k_pages, v_pages  [num_pages, Hkv, P, D] dtype, one page = P consecutive
+ *                     keys of every kv head of one sequence (heads outermost,
+ *                     so one page-head is P*D contiguous elements);
+ *   block_table       [B, block_table_stride] int32: page id holding keys
+ *                     i*P .. i*P+P-1 of sequence b; stride >= ceil(L_max / P);
+ *                     only the entries covering kv_len[b] keys are read;
+ *   page_size (P)     a power of two, 64 .. 2^20;
+ *   kv_len            [B] int32, required, in [n_q, L_max]; the block's own
+ *                     K/V sit at keys kv_len-n_q .. kv_len-1 as in the
+ *                     contiguous call;
+ *   L_max             largest kv_len (sizes the launch plan and workspace).
+ * Every other argument is as in spec_verify_attention.  A block_table entry
+ * outside [0, num_pages) sets SPEC_DEVERR_PAGE; the key range of the split
+ * that met it is dropped (the output stays finite, and no memory outside the
+ * pool is read).  With pages, num_splits is raised where needed so a split's
+ * keys span at most 511 pages.
+ */
+spec_status_t spec_verify_attention_paged(
+    const void* q, const void* k_pages, const void* v_pages, const int32_t* block_table,
+    int32_t block_table_stride, int32_t num_pages, int32_t page_size, void* out, float* lse,
+    const int32_t* kv_len, const int32_t* parent, int32_t parent_batch_stride, int32_t B,
+    int32_t Hq, int32_t Hkv, int32_t n_q, int32_t D, int32_t L_max, spec_dtype_t dtype,
+    float scale, int32_t num_splits, void* workspace, size_t workspace_bytes, int32_t* dev_err,
+    hipStream_t stream);
+
+size_t spec_verify_attention_paged_workspace(int32_t B, int32_t Hq, int32_t Hkv, int32_t n_q,
+                                             int32_t D, int32_t L_max, int32_t page_size,
+                                             spec_dtype_t dtype, int32_t num_splits);
 
 /*
  * spec_window_attention -- bounded draft attention over sinks + a FIFO ring.

@@ -5,6 +5,7 @@ The computation lives in ``libspecverify.so`` (hand-written HIP, built from
 
 * ``verify_attention`` -- block-of-queries attention against the full KV
   cache, chain (causal) or candidate tree (ancestor-only) mask;
+  ``verify_attention_paged`` reads the cache through a block table;
 * ``window_attention`` -- the draft's bounded attention over sink tokens and
   a FIFO ring of the last W tokens, with an optional fused append;
 * ``spec_sample`` -- vocabulary softmax, min(1, target/draft) acceptance and
@@ -30,6 +31,8 @@ from .api import (  # noqa: F401
     validate_tree,
     verify_attention,
     verify_attention_auto_splits,
+    verify_attention_paged,
+    verify_attention_paged_workspace_bytes,
     verify_attention_workspace_bytes,
     window_attention,
     window_attention_workspace_bytes,
@@ -39,5 +42,6 @@ __all__ = [
     "SPEC_BF16", "SPEC_F32", "SpecError", "draft_sample", "draft_sample_workspace_bytes",
     "kv_commit", "lib", "sample_workspace_bytes", "spec_sample",
     "status_str", "validate_tree", "verify_attention", "verify_attention_auto_splits",
+    "verify_attention_paged", "verify_attention_paged_workspace_bytes",
     "verify_attention_workspace_bytes", "window_attention", "window_attention_workspace_bytes",
 ]

@@ -32,6 +32,10 @@ _SIGNATURES = {
                                      _i32, _i32, _i32, _i32, _f32, _i32, _vp, _sz, _vp, _vp]),
     "spec_verify_attention_workspace": (_sz, [_i32] * 8),
     "spec_verify_attention_auto_splits": (_i32, [_i32] * 7),
+    "spec_verify_attention_paged": (_i32, [_vp, _vp, _vp, _vp, _i32, _i32, _i32, _vp, _vp, _vp, _vp,
+                                           _i32, _i32, _i32, _i32, _i32, _i32, _i32, _i32, _f32,
+                                           _i32, _vp, _sz, _vp, _vp]),
+    "spec_verify_attention_paged_workspace": (_sz, [_i32] * 9),
     "spec_window_attention": (_i32, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i32, _i32,
                                      _i32, _i32, _i32, _i32, _i32, _f32, _i32, _vp, _sz, _vp, _vp]),
     "spec_window_attention_workspace": (_sz, [_i32] * 8),
@@ -160,6 +164,46 @@ def verify_attention(q, k_cache, v_cache, kv_len=None, parent=None, scale: float
         B, Hq, Hkv, n_q, D, L_cap, _DTYPES[q.dtype], float(scale), int(num_splits), _p(ws),
         ws.numel(), _p(dev_err), _stream(dev))
     _check(st, "spec_verify_attention")
+    return out, lse
+
+
+def verify_attention_paged_workspace_bytes(B, Hq, Hkv, n_q, D, L_max, page_size, dtype,
+                                           num_splits=0) -> int:
+    return int(lib().spec_verify_attention_paged_workspace(B, Hq, Hkv, n_q, D, L_max, page_size,
+                                                           _DTYPES[dtype], num_splits))
+
+
+def verify_attention_paged(q, k_pages, v_pages, block_table, kv_len, L_max: int, parent=None,
+                           scale: float = 0.0, num_splits: int = 0, out=None, lse=None,
+                           workspace=None, dev_err=None, want_lse: bool = True):
+    """spec_verify_attention_paged on torch tensors.
+
+    k_pages, v_pages: [num_pages, Hkv, P, D]; block_table: [B, stride] int32;
+    kv_len: [B] int32 (required).  Returns (out, lse or None)."""
+    _need_gpu(q, k_pages, v_pages, block_table, kv_len, out, lse, dev_err)
+    if q.dtype not in _DTYPES or k_pages.dtype != q.dtype or v_pages.dtype != q.dtype:
+        raise ValueError("q, k, v must share dtype float32 or bfloat16")
+    if k_pages.shape != v_pages.shape:
+        raise ValueError("k_pages and v_pages must match")
+    if block_table.dtype != torch.int32 or kv_len.dtype != torch.int32:
+        raise ValueError("block_table and kv_len must be int32")
+    B, Hq, n_q, D = q.shape
+    num_pages, Hkv, P, _ = k_pages.shape
+    dev = q.device
+    if out is None:
+        out = torch.empty_like(q)
+    if lse is None and want_lse:
+        lse = torch.empty(B, Hq, n_q, dtype=torch.float32, device=dev)
+    par, pstride = _parent_arg(parent, B, n_q, dev)
+    nbytes = verify_attention_paged_workspace_bytes(B, Hq, Hkv, n_q, D, L_max, P, q.dtype,
+                                                    num_splits)
+    ws = _workspace(nbytes, dev, workspace)
+    st = lib().spec_verify_attention_paged(
+        _p(q), _p(k_pages), _p(v_pages), _p(block_table), int(block_table.shape[1]), num_pages, P,
+        _p(out), _p(lse), _p(kv_len), _p(par), pstride, B, Hq, Hkv, n_q, D, int(L_max),
+        _DTYPES[q.dtype], float(scale), int(num_splits), _p(ws), ws.numel(), _p(dev_err),
+        _stream(dev))
+    _check(st, "spec_verify_attention_paged")
     return out, lse
 
 

@@ -99,23 +99,48 @@ size_t spec_verify_attention_workspace(int32_t B, int32_t Hq, int32_t Hkv, int32
   return plan_attention(B, Hkv, (Hq / Hkv) * n_q, D, L_cap, dtype, num_splits, false).ws_bytes;
 }
 
-spec_status_t spec_verify_attention(const void* q, const void* k_cache, const void* v_cache,
-                                    void* out, float* lse, const int32_t* kv_len,
-                                    const int32_t* parent, int32_t parent_batch_stride,
-                                    int32_t B, int32_t Hq, int32_t Hkv, int32_t n_q, int32_t D,
-                                    int32_t L_cap, spec_dtype_t dtype, float scale,
-                                    int32_t num_splits, void* workspace, size_t workspace_bytes,
-                                    int32_t* dev_err, hipStream_t stream) {
+}  // extern "C"
+
+namespace {
+
+// Paging parameters of a verify call (all zero for a contiguous cache).
+struct Paging {
+  const int32_t* block_table;
+  int32_t bt_stride, num_pages, page_size;
+};
+
+int32_t log2_exact(int32_t x) {
+  int32_t s = 0;
+  while ((1 << s) < x) ++s;
+  return (1 << s) == x ? s : -1;
+}
+
+spec_status_t paging_check(const Paging& pg, int32_t L_max, const int32_t* kv_len) {
+  if (pg.page_size > (1 << 20) || log2_exact(pg.page_size) < 6) return SPEC_ERR_UNSUPPORTED;
+  if (pg.num_pages < 1) return SPEC_ERR_INVALID_ARG;
+  if (pg.bt_stride < (L_max + pg.page_size - 1) / pg.page_size) return SPEC_ERR_INVALID_ARG;
+  if (!aligned(pg.block_table, 4) || !aligned(kv_len, 4)) return SPEC_ERR_MISALIGNED;
+  return SPEC_OK;
+}
+
+spec_status_t verify_call(const void* q, const void* k_cache, const void* v_cache, void* out,
+                          float* lse, const int32_t* kv_len, const int32_t* parent,
+                          int32_t parent_batch_stride, int32_t B, int32_t Hq, int32_t Hkv,
+                          int32_t n_q, int32_t D, int32_t L_cap, spec_dtype_t dtype, float scale,
+                          int32_t num_splits, void* workspace, size_t workspace_bytes,
+                          int32_t* dev_err, hipStream_t stream, const Paging& pg) {
   spec_status_t st = verify_shape(B, Hq, Hkv, n_q, D, L_cap, dtype, num_splits);
   if (st != SPEC_OK) return st;
   if (parent && parent_batch_stride != 0 && parent_batch_stride != n_q) return SPEC_ERR_INVALID_ARG;
+  if (pg.page_size && (st = paging_check(pg, L_cap, kv_len)) != SPEC_OK) return st;
   if (B == 0) return SPEC_OK;
   if (!aligned(q, 16) || !aligned(k_cache, 16) || !aligned(v_cache, 16) || !aligned(out, 16) ||
       !aligned_or_null(lse, 4) || !aligned_or_null(kv_len, 4) || !aligned_or_null(parent, 4) ||
       !aligned_or_null(dev_err, 4))
     return SPEC_ERR_MISALIGNED;
   const int32_t g = Hq / Hkv;
-  const AttnPlan p = plan_attention(B, Hkv, g * n_q, D, L_cap, dtype, num_splits, false);
+  const AttnPlan p =
+      plan_attention(B, Hkv, g * n_q, D, L_cap, dtype, num_splits, false, pg.page_size);
   if (!aligned(workspace, 256) || workspace_bytes < p.ws_bytes) return SPEC_ERR_WORKSPACE;
 
   AttnArgs a;
@@ -126,6 +151,12 @@ spec_status_t spec_verify_attention(const void* q, const void* k_cache, const vo
   a.lens = kv_len;
   a.parent = parent;
   a.parent_stride = parent ? parent_batch_stride : 0;
+  if (pg.page_size) {
+    a.block_table = pg.block_table;
+    a.bt_stride = pg.bt_stride;
+    a.page_shift = log2_exact(pg.page_size);
+    a.num_pages = pg.num_pages;
+  }
   a.ws_o = static_cast<float*>(workspace);
   a.ws_ml = reinterpret_cast<float*>(static_cast<char*>(workspace) + p.ws_o_bytes);
   a.B = B;
@@ -147,6 +178,44 @@ spec_status_t spec_verify_attention(const void* q, const void* k_cache, const vo
   a.out = out;
   a.lse = lse;
   return launch_attention(a, false, dtype, out, lse, stream) == hipSuccess ? SPEC_OK : SPEC_ERR_HIP;
+}
+
+}  // namespace
+
+extern "C" {
+
+spec_status_t spec_verify_attention(const void* q, const void* k_cache, const void* v_cache,
+                                    void* out, float* lse, const int32_t* kv_len,
+                                    const int32_t* parent, int32_t parent_batch_stride,
+                                    int32_t B, int32_t Hq, int32_t Hkv, int32_t n_q, int32_t D,
+                                    int32_t L_cap, spec_dtype_t dtype, float scale,
+                                    int32_t num_splits, void* workspace, size_t workspace_bytes,
+                                    int32_t* dev_err, hipStream_t stream) {
+  return verify_call(q, k_cache, v_cache, out, lse, kv_len, parent, parent_batch_stride, B, Hq,
+                     Hkv, n_q, D, L_cap, dtype, scale, num_splits, workspace, workspace_bytes,
+                     dev_err, stream, Paging{nullptr, 0, 0, 0});
+}
+
+size_t spec_verify_attention_paged_workspace(int32_t B, int32_t Hq, int32_t Hkv, int32_t n_q,
+                                             int32_t D, int32_t L_max, int32_t page_size,
+                                             spec_dtype_t dtype, int32_t num_splits) {
+  if (verify_shape(B, Hq, Hkv, n_q, D, L_max, dtype, num_splits) != SPEC_OK || B == 0) return 0;
+  if (page_size > (1 << 20) || log2_exact(page_size) < 6) return 0;
+  return plan_attention(B, Hkv, (Hq / Hkv) * n_q, D, L_max, dtype, num_splits, false, page_size)
+      .ws_bytes;
+}
+
+spec_status_t spec_verify_attention_paged(
+    const void* q, const void* k_pages, const void* v_pages, const int32_t* block_table,
+    int32_t block_table_stride, int32_t num_pages, int32_t page_size, void* out, float* lse,
+    const int32_t* kv_len, const int32_t* parent, int32_t parent_batch_stride, int32_t B,
+    int32_t Hq, int32_t Hkv, int32_t n_q, int32_t D, int32_t L_max, spec_dtype_t dtype,
+    float scale, int32_t num_splits, void* workspace, size_t workspace_bytes, int32_t* dev_err,
+    hipStream_t stream) {
+  if (page_size < 1) return SPEC_ERR_INVALID_ARG;
+  return verify_call(q, k_pages, v_pages, out, lse, kv_len, parent, parent_batch_stride, B, Hq,
+                     Hkv, n_q, D, L_max, dtype, scale, num_splits, workspace, workspace_bytes,
+                     dev_err, stream, Paging{block_table, block_table_stride, num_pages, page_size});
 }
 
 size_t spec_window_attention_workspace(int32_t B, int32_t Hq, int32_t Hkv, int32_t D, int32_t W,

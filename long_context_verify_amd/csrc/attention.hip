@@ -108,6 +108,53 @@ __device__ __forceinline__ const char* key_row(const AttnArgs& a, const UnitGeom
   }
 }
 
+// ---------------------------------------------------------------------------
+// Paged caches (verify only).  K and V live in a pool of pages
+// [num_pages, Hkv, P, D] with P = 2^page_shift keys, and block_table[b][i]
+// names the page holding keys i*P .. i*P+P-1 of sequence b.  P is a multiple
+// of every kernel's chunk, so a chunk never straddles pages.  A work-group
+// stages the page ids of its key range in LDS once (the launch plan keeps
+// the range within kPageCap pages) and each chunk reads its page from there.
+// ---------------------------------------------------------------------------
+constexpr int kPageCap = 512;
+
+// Stage the page ids of keys [key_begin, key_end) of unit u; doubles as the
+// work-group barrier that follows the Q staging.  False (and an error bit) if
+// a page id lies outside the pool: the caller then drops its key range.
+template <bool PAGED>
+__device__ __forceinline__ bool stage_pages(const AttnArgs& a, const UnitGeom& u, int key_begin,
+                                            int key_end, int32_t* lds_pages, int& first) {
+  int bad = 0;
+  first = 0;
+  if (PAGED && key_end > key_begin) {
+    first = key_begin >> a.page_shift;
+    const int n = ((key_end - 1) >> a.page_shift) - first + 1;
+    const int32_t* bt = a.block_table + (size_t)u.b * a.bt_stride + first;
+    for (int i = threadIdx.x; i < n; i += blockDim.x) {
+      const int pid = bt[i];
+      bad |= pid < 0 || pid >= a.num_pages;
+      lds_pages[i] = pid;
+    }
+  }
+  bad = __syncthreads_or(bad);
+  if (bad && threadIdx.x == 0) report_error(a.dev_err, SPEC_DEVERR_PAGE);
+  return !bad;
+}
+
+// Address of key `key` of unit u (K: kv = 0, V: kv = 1) in the verify cache,
+// contiguous [B, Hkv, L_cap, D] or paged; with pages, `key` must lie in the
+// staged range.  Keys of one chunk are consecutive rows from the chunk's base.
+template <bool PAGED>
+__device__ __forceinline__ const char* cache_row(const AttnArgs& a, const UnitGeom& u, int key,
+                                                 int kv, size_t row_bytes,
+                                                 const int32_t* lds_pages, int first) {
+  const char* pool = static_cast<const char*>(kv ? a.v : a.k);
+  if (!PAGED) return pool + ((size_t)u.unit * a.L_cap + key) * row_bytes;
+  const int page = lds_pages[(key >> a.page_shift) - first];
+  const size_t in_page = (size_t)(key & ((1 << a.page_shift) - 1));
+  return pool + ((((size_t)page * a.Hkv + u.hk) << a.page_shift) + in_page) * row_bytes;
+}
+
 // Ancestor bitmask of block node i (bit t set: node t is i or an ancestor of i).
 __device__ __forceinline__ uint64_t ancestor_mask(const AttnArgs& a, int b, int i) {
   if (!a.parent) return (i >= 63) ? ~0ull : ((2ull << i) - 1ull);
@@ -182,7 +229,7 @@ __device__ __forceinline__ void window_append(const AttnArgs& a, const UnitGeom&
 // ---------------------------------------------------------------------------
 // bf16 MFMA split kernel.  QB = MFMA query blocks (16 rows each) per slice.
 // ---------------------------------------------------------------------------
-template <int D, int QB, bool WINDOW, int NW = kWaves>
+template <int D, int QB, bool WINDOW, int NW = kWaves, bool PAGED = false>
 __global__ __launch_bounds__(NW * kWave, 8 / NW) void attn_split_mfma(AttnArgs a) {
   constexpr int DS = D / 32;             // MFMA k-steps over the head dim for S
   constexpr int SR = 16 * QB;            // query rows per slice
@@ -190,6 +237,7 @@ __global__ __launch_bounds__(NW * kWave, 8 / NW) void attn_split_mfma(AttnArgs a
   __shared__ float lds_o[NW][SR][LDS_STRIDE];
   __shared__ float lds_ml[NW][SR][2];
   __shared__ bf16x8 lds_q[QB][DS][kWave];
+  __shared__ int32_t lds_pages[PAGED ? kPageCap : 1];
 
   int unit, split, qs;
   if (!decode_tile(a, unit, split, qs)) return;
@@ -222,10 +270,17 @@ __global__ __launch_bounds__(NW * kWave, 8 / NW) void attn_split_mfma(AttnArgs a
     }
     anc[qb] = (!WINDOW && live) ? ancestor_mask(a, u.b, row % a.n_q) : 1ull;
   }
-  __syncthreads();
 
   int c0, c1;
   chunk_range(u.n_keys, split, a.n_splits, c0, c1);
+  int pfirst = 0;
+  if constexpr (PAGED) {
+    // The page-table staging doubles as the barrier after the Q staging.
+    if (!stage_pages<PAGED>(a, u, c0 * kChunk, min(c1 * kChunk, u.n_keys), lds_pages, pfirst))
+      c1 = c0;
+  } else {
+    __syncthreads();
+  }
 
   float m[QB], lsum[QB];
   f32x4 oacc[QB][8];
@@ -239,12 +294,21 @@ __global__ __launch_bounds__(NW * kWave, 8 / NW) void attn_split_mfma(AttnArgs a
 
   const int last = u.n_keys - 1;
   // K operands (A side): lane holds K[kbase + 16 kb + r][32 s + 8 h .. +8].
+  auto row_of = [&](int key, int kv, int kbase) -> const char* {
+    if constexpr (!PAGED) {
+      return key_row<WINDOW>(a, u, key, kv, row_bytes);
+    } else {
+      // One page lookup per chunk; the chunk's keys are consecutive rows.
+      return cache_row<PAGED>(a, u, kbase, kv, row_bytes, lds_pages, pfirst) +
+             (size_t)(key - kbase) * row_bytes;
+    }
+  };
   auto load_k = [&](int kbase, bf16x8 (&kop)[2][DS]) {
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb) {
       int key = kbase + 16 * kb + r;
       key = key < last ? key : last;
-      const char* p = key_row<WINDOW>(a, u, key, 0, row_bytes);
+      const char* p = row_of(key, 0, kbase);
 #pragma unroll
       for (int s = 0; s < DS; ++s)
         kop[kb][s] = __builtin_nontemporal_load(reinterpret_cast<const bf16x8*>(p + (32 * s + 8 * h) * 2));
@@ -260,7 +324,7 @@ __global__ __launch_bounds__(NW * kWave, 8 / NW) void attn_split_mfma(AttnArgs a
       key = key < last ? key : last;
       if (8 * r < D)
         vraw[t] = __builtin_nontemporal_load(
-            reinterpret_cast<const u32x4*>(key_row<WINDOW>(a, u, key, 1, row_bytes) + r * 16));
+            reinterpret_cast<const u32x4*>(row_of(key, 1, kbase) + r * 16));
       else
         vraw[t] = u32x4{0u, 0u, 0u, 0u};
     }
@@ -473,13 +537,14 @@ __device__ __forceinline__ void wait_vmcnt(int n) {
   }
 }
 
-template <int WAVES>
+template <int WAVES, bool PAGED = false>
 __global__ __launch_bounds__(WAVES * kWave, 1) void attn_tree_mfma(AttnArgs a) {
   constexpr int D = 128, DS = 4, QB = 2;
   constexpr int SR = WAVES * 32;              // query rows per work-group
   constexpr int TILE = 32768;                 // bytes per chunk (K 16 KB + V 16 KB)
   constexpr int UPW = 32 / WAVES;             // 1 KB load units per wave per chunk
   __shared__ __attribute__((aligned(16))) char tiles[kTreeNBuf][TILE];
+  __shared__ int32_t lds_pages[PAGED ? kPageCap : 1];
 
   int unit, split, qs;
   if (!decode_tile(a, unit, split, qs)) return;
@@ -511,15 +576,31 @@ __global__ __launch_bounds__(WAVES * kWave, 1) void attn_tree_mfma(AttnArgs a) {
   // This split's range of 64-key chunks.
   const long long nch = (u.n_keys + kTreeChunk - 1) / kTreeChunk;
   const int c0 = (int)(nch * split / a.n_splits);
-  const int c1 = (int)(nch * (split + 1) / a.n_splits);
+  int c1 = (int)(nch * (split + 1) / a.n_splits);
   const int last = u.n_keys - 1;
-  const char* kbase_p = static_cast<const char*>(a.k) + (size_t)u.unit * a.L_cap * row_bytes;
-  const char* vbase_p = static_cast<const char*>(a.v) + (size_t)u.unit * a.L_cap * row_bytes;
+  int pfirst = 0;
+  if constexpr (PAGED) {
+    if (!stage_pages<PAGED>(a, u, c0 * kTreeChunk, min(c1 * kTreeChunk, u.n_keys), lds_pages,
+                            pfirst))
+      c1 = c0;
+  }
 
   // This wave's share of one chunk: UPW 1 KB units out of 32 (16 K + 16 V).
+  const char* kbase_p = static_cast<const char*>(a.k) + (size_t)u.unit * a.L_cap * row_bytes;
+  const char* vbase_p = static_cast<const char*>(a.v) + (size_t)u.unit * a.L_cap * row_bytes;
   auto issue = [&](int c, int buf) {
     const int kbase = c * kTreeChunk;
     char* tile = tiles[buf];
+    // Keys key0 .. of this chunk are consecutive rows from kc / vc: the unit's
+    // stream in a contiguous cache, or the chunk's page (one lookup per chunk).
+    const char* kc = kbase_p;
+    const char* vc = vbase_p;
+    int key0 = 0;
+    if constexpr (PAGED) {
+      kc = cache_row<PAGED>(a, u, kbase, 0, row_bytes, lds_pages, pfirst);
+      vc = cache_row<PAGED>(a, u, kbase, 1, row_bytes, lds_pages, pfirst);
+      key0 = kbase;
+    }
 #pragma unroll
     for (int i = 0; i < UPW; ++i) {
       const int unit_id = wave * UPW + i;
@@ -527,11 +608,13 @@ __global__ __launch_bounds__(WAVES * kWave, 1) void attn_tree_mfma(AttnArgs a) {
         const int kb = unit_id >> 2, s = unit_id & 3;
         int key = kbase + 16 * kb + r;
         key = key < last ? key : last;
-        lds_dma16(kbase_p + (size_t)key * row_bytes + (32 * s + 8 * h) * 2, tile + unit_id * 1024);
+        lds_dma16(kc + (size_t)(key - key0) * row_bytes + (32 * s + 8 * h) * 2,
+                  tile + unit_id * 1024);
       } else {                // V rows 4 (unit_id - 16) .. +3, 16 lanes per row
         int key = kbase + 4 * (unit_id - 16) + (lane >> 4);
         key = key < last ? key : last;
-        lds_dma16(vbase_p + (size_t)key * row_bytes + (lane & 15) * 16, tile + unit_id * 1024);
+        lds_dma16(vc + (size_t)(key - key0) * row_bytes + (lane & 15) * 16,
+                  tile + unit_id * 1024);
       }
     }
   };
@@ -700,9 +783,10 @@ __global__ __launch_bounds__(WAVES * kWave, 1) void attn_tree_mfma(AttnArgs a) {
 // ---------------------------------------------------------------------------
 // fp32 VALU split kernel: one wave per query row, lanes over the head dim.
 // ---------------------------------------------------------------------------
-template <int D, bool WINDOW>
+template <int D, bool WINDOW, bool PAGED = false>
 __global__ __launch_bounds__(kThreads) void attn_split_valu(AttnArgs a) {
   constexpr int DPL = D / 64;  // head-dim entries per lane
+  __shared__ int32_t lds_pages[PAGED ? kPageCap : 1];
   int unit, split, qs;
   if (!decode_tile(a, unit, split, qs)) return;
   const int lane = threadIdx.x & 63;
@@ -710,6 +794,13 @@ __global__ __launch_bounds__(kThreads) void attn_split_valu(AttnArgs a) {
   const size_t row_bytes = (size_t)D * 4;
   const UnitGeom u = unit_geom<WINDOW>(a, unit, split == 0 && qs == 0 && threadIdx.x == 0);
   window_append<WINDOW>(a, u, split, qs, row_bytes);
+
+  int c0, c1;
+  chunk_range(u.n_keys, split, a.n_splits, c0, c1);
+  int pfirst = 0;
+  if (PAGED &&
+      !stage_pages<PAGED>(a, u, c0 * kChunk, min(c1 * kChunk, u.n_keys), lds_pages, pfirst))
+    c1 = c0;
 
   const int row = qs * kValuSlice + wave;
   if (row >= a.M) return;   // no barrier follows
@@ -721,8 +812,6 @@ __global__ __launch_bounds__(kThreads) void attn_split_valu(AttnArgs a) {
   for (int e = 0; e < DPL; ++e) qv[e] = qrow[lane + 64 * e];
   const uint64_t anc = WINDOW ? 1ull : ancestor_mask(a, u.b, row % a.n_q);
 
-  int c0, c1;
-  chunk_range(u.n_keys, split, a.n_splits, c0, c1);
   const int k0 = c0 * kChunk;
   const int k1 = min(c1 * kChunk, u.n_keys);
 
@@ -740,8 +829,12 @@ __global__ __launch_bounds__(kThreads) void attn_split_valu(AttnArgs a) {
       int key = kk + t;
       const bool ok_key = key < k1;
       key = ok_key ? key : k1 - 1;
-      const float* kr = reinterpret_cast<const float*>(key_row<WINDOW>(a, u, key, 0, row_bytes));
-      const float* vr = reinterpret_cast<const float*>(key_row<WINDOW>(a, u, key, 1, row_bytes));
+      const float* kr = reinterpret_cast<const float*>(
+          WINDOW ? key_row<WINDOW>(a, u, key, 0, row_bytes)
+                 : cache_row<PAGED>(a, u, key, 0, row_bytes, lds_pages, pfirst));
+      const float* vr = reinterpret_cast<const float*>(
+          WINDOW ? key_row<WINDOW>(a, u, key, 1, row_bytes)
+                 : cache_row<PAGED>(a, u, key, 1, row_bytes, lds_pages, pfirst));
       float part = 0.f;
 #pragma unroll
       for (int e = 0; e < DPL; ++e) {
@@ -844,7 +937,7 @@ __global__ __launch_bounds__(256) void attn_merge(MergeArgs a) {
 static int ceil_div(long long a, long long b) { return (int)((a + b - 1) / b); }
 
 AttnPlan plan_attention(int32_t B, int32_t Hkv, int32_t M, int32_t D, int32_t n_keys_max,
-                        spec_dtype_t dtype, int32_t num_splits, bool window) {
+                        spec_dtype_t dtype, int32_t num_splits, bool window, int32_t page_size) {
   AttnPlan p{};
   const bool mfma = dtype == SPEC_BF16;
   const long long units = (long long)B * Hkv;
@@ -874,6 +967,15 @@ AttnPlan plan_attention(int32_t B, int32_t Hkv, int32_t M, int32_t D, int32_t n_
     if (s < 1) s = 1;
     p.n_splits = (int)s;
   }
+  if (page_size > 0) {
+    // A split's key range must fit the LDS page table: at most kPageCap - 1
+    // pages of keys, so with alignment it touches at most kPageCap pages.
+    const int ck = p.tree_waves ? kTreeChunk : kChunk;
+    const long long nch = ceil_div(n_keys_max, ck);
+    const long long per_split = (long long)(kPageCap - 1) * page_size / ck;   // chunks
+    const long long smin = (nch + per_split - 1) / per_split;
+    if (p.n_splits < smin) p.n_splits = (int)smin;
+  }
   const long long tiles = units * p.n_splits;
   p.grid = (int)(p.n_qs == 1 ? tiles : ((tiles + 7) / 8) * 8 * p.n_qs);
   const size_t parts = (size_t)tiles * p.n_qs;
@@ -883,11 +985,11 @@ AttnPlan plan_attention(int32_t B, int32_t Hkv, int32_t M, int32_t D, int32_t n_
   return p;
 }
 
-template <bool WINDOW>
+template <bool WINDOW, bool PAGED>
 static hipError_t launch_split(const AttnArgs& a, spec_dtype_t dtype, hipStream_t stream) {
   dim3 grid(a.grid), block(kThreads);
   if (!WINDOW && a.tree_waves == 8) {
-    hipLaunchKernelGGL(attn_tree_mfma<8>, grid, dim3(512), 0, stream, a);
+    hipLaunchKernelGGL((attn_tree_mfma<8, PAGED>), grid, dim3(512), 0, stream, a);
   } else if (WINDOW && dtype == SPEC_BF16 && a.n_splits == 1) {
     // One work-group per unit: 8 waves share the window and merge in LDS.
     dim3 wblock(8 * kWave);
@@ -905,27 +1007,33 @@ static hipError_t launch_split(const AttnArgs& a, spec_dtype_t dtype, hipStream_
   } else if (dtype == SPEC_BF16) {
     if (a.D == 128) {
       if (a.slice_rows == 16)
-        hipLaunchKernelGGL((attn_split_mfma<128, 1, WINDOW>), grid, block, 0, stream, a);
+        hipLaunchKernelGGL((attn_split_mfma<128, 1, WINDOW, kWaves, PAGED>), grid, block, 0, stream,
+                           a);
       else
-        hipLaunchKernelGGL((attn_split_mfma<128, 2, WINDOW>), grid, block, 0, stream, a);
+        hipLaunchKernelGGL((attn_split_mfma<128, 2, WINDOW, kWaves, PAGED>), grid, block, 0, stream,
+                           a);
     } else {
       if (a.slice_rows == 16)
-        hipLaunchKernelGGL((attn_split_mfma<64, 1, WINDOW>), grid, block, 0, stream, a);
+        hipLaunchKernelGGL((attn_split_mfma<64, 1, WINDOW, kWaves, PAGED>), grid, block, 0, stream,
+                           a);
       else
-        hipLaunchKernelGGL((attn_split_mfma<64, 2, WINDOW>), grid, block, 0, stream, a);
+        hipLaunchKernelGGL((attn_split_mfma<64, 2, WINDOW, kWaves, PAGED>), grid, block, 0, stream,
+                           a);
     }
   } else {
     if (a.D == 128)
-      hipLaunchKernelGGL((attn_split_valu<128, WINDOW>), grid, block, 0, stream, a);
+      hipLaunchKernelGGL((attn_split_valu<128, WINDOW, PAGED>), grid, block, 0, stream, a);
     else
-      hipLaunchKernelGGL((attn_split_valu<64, WINDOW>), grid, block, 0, stream, a);
+      hipLaunchKernelGGL((attn_split_valu<64, WINDOW, PAGED>), grid, block, 0, stream, a);
   }
   return hipGetLastError();
 }
 
 hipError_t launch_attention(const AttnArgs& a, bool window, spec_dtype_t dtype, void* out,
                             float* lse, hipStream_t stream) {
-  hipError_t e = window ? launch_split<true>(a, dtype, stream) : launch_split<false>(a, dtype, stream);
+  hipError_t e = window           ? launch_split<true, false>(a, dtype, stream)
+                 : a.block_table ? launch_split<false, true>(a, dtype, stream)
+                                 : launch_split<false, false>(a, dtype, stream);
   if (e != hipSuccess || a.n_splits == 1) return e;
   MergeArgs m;
   m.ws_o = a.ws_o;

@@ -27,6 +27,10 @@ struct AttnArgs {
   const int32_t* lens;    // verify: kv_len (nullable); window: total_len
   const int32_t* parent;  // verify: nullable parent array
   int32_t parent_stride;
+  const int32_t* block_table;  // paged verify: [B, bt_stride] page ids; NULL = contiguous cache
+  int32_t bt_stride;
+  int32_t page_shift;     // log2 of the page size (keys per page)
+  int32_t num_pages;      // pages in the pool (bounds check of block_table entries)
   float* ws_o;            // [n_partials][slice_rows][D]
   float* ws_ml;           // [n_partials][slice_rows][2]  (running max in log2 units, sum)
   void* out;              // [B, Hq, n_q, D]: written directly when n_splits == 1
@@ -57,8 +61,10 @@ struct AttnPlan {
   size_t ws_o_bytes, ws_ml_bytes, ws_bytes;
 };
 
+// page_size: keys per page of a paged verify cache (0: contiguous).
 AttnPlan plan_attention(int32_t B, int32_t Hkv, int32_t M, int32_t D, int32_t n_keys_max,
-                        spec_dtype_t dtype, int32_t num_splits, bool window);
+                        spec_dtype_t dtype, int32_t num_splits, bool window,
+                        int32_t page_size = 0);
 
 hipError_t launch_attention(const AttnArgs& a, bool window, spec_dtype_t dtype, void* out,
                             float* lse, hipStream_t stream);

@@ -21,6 +21,14 @@ verify_attention
       o = sum_j softmax(s)_j v[b,hk,j];   lse = log sum_j exp(s_j).
     A chain is the tree whose node i hangs under i-1.
 
+verify_attention_paged
+    The same attention when the cache is a pool of fixed-size pages and a
+    block table lists each sequence's pages in order (the serving engines
+    "Guide to MagicDec" names for continuous batching, vLLM and
+    TensorRT-LLM, keep caches this way): key j of sequence b is row j % P of
+    page block_table[b][j // P].  The oracle gathers the pages back into a
+    contiguous cache and applies verify_attention.
+
 window_attention
     "Guide to MagicDec", section 1 "Fixed-Window KV Cache Decoupling": the
     draft attends only to the most recent W tokens (a FIFO ring), and "Best
@@ -111,6 +119,33 @@ def verify_attention(q, k, v, kv_len=None, parent=None, scale: Optional[float] =
                 allowed[p0 + t] = True
             o[b, h, i], lse[b, h, i] = softmax_attention(q[b, h, i], K, V, allowed, scale)
     return o, lse
+
+
+def gather_pages(pages, block_table, kv_len, L_max: int):
+    """Contiguous [B, Hkv, L_max, D] cache from a page pool [num_pages, Hkv, P, D].
+
+    Key j < kv_len[b] of sequence b is row j % P of page block_table[b][j // P];
+    keys at or past kv_len[b] are NaN (verify_attention never reads them).
+    """
+    bt = np.asarray(_f64(block_table), dtype=np.int64)
+    kl = np.asarray(_f64(kv_len), dtype=np.int64)
+    _, Hkv, P, D = pages.shape
+    B = bt.shape[0]
+    out = np.full((B, Hkv, L_max, D), np.nan)
+    for b in range(B):
+        for j0 in range(0, int(kl[b]), P):           # one page at a time
+            n = min(P, int(kl[b]) - j0)
+            out[b, :, j0:j0 + n] = _f64(pages[int(bt[b, j0 // P])])[:, :n]
+    return out
+
+
+def verify_attention_paged(q, k_pages, v_pages, block_table, kv_len, L_max: int, parent=None,
+                           scale: Optional[float] = None,
+                           heads: Optional[Iterable[Tuple[int, int]]] = None):
+    """verify_attention over a paged cache (see the module notes)."""
+    k = gather_pages(k_pages, block_table, kv_len, L_max)
+    v = gather_pages(v_pages, block_table, kv_len, L_max)
+    return verify_attention(q, k, v, kv_len, parent=parent, scale=scale, heads=heads)
 
 
 def window_attention(q, hist_sink_k, hist_sink_v, hist_recent_k, hist_recent_v,

@@ -11,6 +11,7 @@ import os
 
 import numpy as np
 import pytest
+import torch
 
 import long_context_verify_amd as L
 from long_context_verify_amd import api
@@ -76,6 +77,26 @@ def test_workspace_queries():
     assert L.window_attention_workspace_bytes(8, 32, 8, 128, 512, 4, bf16) > 0
     assert L.sample_workspace_bytes(8, 5, 128256) > 0
     assert L.sample_workspace_bytes(8, 0, 128256) == 0
+
+
+def _paged(B=2, P_size=64, stride=16, num_pages=40, bt=P, kv_len=P, L_max=1000, ws_bytes=0):
+    return L.lib().spec_verify_attention_paged(P, P, P, bt, stride, num_pages, P_size, P, NULL,
+                                               kv_len, NULL, 0, B, 8, 2, 5, 128, L_max, 1, 0.0, 0,
+                                               P, ws_bytes, NULL, NULL)
+
+
+def test_verify_paged_argument_checks():
+    assert _paged(B=0) == OK
+    assert _paged(P_size=32) == UNSUPPORTED
+    assert _paged(P_size=96) == UNSUPPORTED
+    assert _paged(P_size=0) == INVALID
+    assert _paged(stride=15) == INVALID          # ceil(1000 / 64) = 16 entries needed
+    assert _paged(num_pages=0) == INVALID
+    assert _paged(bt=NULL) == MISALIGNED
+    assert _paged(kv_len=NULL) == MISALIGNED
+    assert _paged() == WORKSPACE
+    assert L.verify_attention_paged_workspace_bytes(2, 8, 2, 5, 128, 1000, 64, torch.bfloat16) > 0
+    assert L.verify_attention_paged_workspace_bytes(2, 8, 2, 5, 128, 1000, 48, torch.bfloat16) == 0
 
 
 def _window(B=2, Hq=8, Hkv=2, D=128, W=64, S=4, k_new=NULL, v_new=NULL, k_sink=P, ws_bytes=0,

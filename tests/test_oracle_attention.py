@@ -13,8 +13,10 @@ import pytest
 import torch
 import torch.nn.functional as F
 
-from oracle.attention import ancestors, verify_attention, window_attention
-from workloads import chain_parent, make_attention_inputs, make_window_inputs, random_tree
+from oracle.attention import (ancestors, gather_pages, verify_attention, verify_attention_paged,
+                              window_attention)
+from workloads import (chain_parent, make_attention_inputs, make_paged_inputs, make_window_inputs,
+                       random_tree)
 
 
 def _sdpa_last_rows(q_rows, K, V, n_q):
@@ -199,3 +201,35 @@ def test_window_is_flat_in_context_length():
     o2, _ = window_attention(a["q"], a["hist_sink_k"], a["hist_sink_v"], a["hist_recent_k"],
                              a["hist_recent_v"], [10**6], W, S)
     assert np.array_equal(o1, o2)
+
+
+def test_gather_pages_hand_worked():
+    """P = 3: sequence 0 lives on pages 2 then 0, sequence 1 on page 1."""
+    pages = np.zeros((3, 1, 3, 1))
+    pages[2, 0, :, 0] = [10, 11, 12]
+    pages[0, 0, :, 0] = [13, 14, 15]
+    pages[1, 0, :, 0] = [20, 21, 22]
+    bt = np.array([[2, 0], [1, -1]])
+    out = gather_pages(pages, bt, [5, 2], L_max=6)
+    assert out[0, 0, :5, 0].tolist() == [10, 11, 12, 13, 14]
+    assert out[1, 0, :2, 0].tolist() == [20, 21]
+    assert np.isnan(out[0, 0, 5, 0]) and np.isnan(out[1, 0, 2:, 0]).all()
+
+
+@pytest.mark.parametrize("P,tree", [(64, False), (4, True), (7, False)])
+def test_paged_equals_contiguous(P, tree):
+    """A shuffled page pool with a block table gives the contiguous result."""
+    B, Hq, Hkv, n_q, D, L = 3, 4, 2, 6, 16, 150
+    kv = [150, 97, 6]
+    x = make_attention_inputs(B, Hq, Hkv, n_q, D, L, dtype="f32", seed=8, kv_len=kv)
+    parent = random_tree(n_q, seed=3) if tree else None
+    pg = make_paged_inputs(x["k"], x["v"], x["kv_len"], P, seed=1)
+    o1, l1 = verify_attention(x["q"], x["k"], x["v"], x["kv_len"], parent=parent)
+    o2, l2 = verify_attention_paged(x["q"], pg["k_pages"], pg["v_pages"], pg["block_table"],
+                                    x["kv_len"], L, parent=parent)
+    assert np.array_equal(o1, o2) and np.array_equal(l1, l2)
+    # Entries past each sequence's pages are -1 and never needed.
+    bt = pg["block_table"].numpy()
+    for b in range(B):
+        need = (kv[b] + P - 1) // P
+        assert (bt[b, :need] >= 0).all() and (bt[b, need:] == -1).all()

@@ -42,6 +42,7 @@ import torch
 
 __all__ = [
     "CONFIGS",
+    "make_paged_inputs",
     "WorkloadConfig",
     "chain_parent",
     "random_tree",
@@ -179,6 +180,39 @@ def make_attention_inputs(B: int, Hq: int, Hkv: int, n_q: int, D: int, L: int,
     v = _normal((B, Hkv, L_cap, D), 1.0, g, device, dtype)
     kl = torch.tensor(list(kv_len), dtype=torch.int32, device=device)
     return {"q": q, "k": k, "v": v, "kv_len": kl, "L_cap": L_cap}
+
+
+def make_paged_inputs(k, v, kv_len, page_size: int, seed: int = 0, spare_pages: int = 3,
+                      junk: float = 50.0):
+    """Scatter contiguous caches [B, Hkv, L_cap, D] into a shuffled page pool.
+
+    Returns dict(k_pages, v_pages [num_pages, Hkv, P, D], block_table [B, stride]
+    int32, stride = ceil(L_cap / P)).  Sequence b gets ceil(kv_len[b] / P) pages
+    at seeded random pool positions (numpy PCG64); table entries past those are
+    -1 and the spare pages hold ``junk``, so a read outside the table shows.
+    """
+    B, Hkv, L_cap, D = k.shape
+    P = int(page_size)
+    kl = [int(x) for x in (kv_len.tolist() if hasattr(kv_len, "tolist") else kv_len)]
+    need = [(L + P - 1) // P for L in kl]
+    num_pages = sum(need) + spare_pages
+    rng = np.random.Generator(np.random.PCG64(seed))
+    perm = rng.permutation(num_pages)
+    stride = (L_cap + P - 1) // P
+    table = np.full((B, stride), -1, dtype=np.int32)
+    kp = torch.full((num_pages, Hkv, P, D), junk, dtype=k.dtype, device=k.device)
+    vp = torch.full((num_pages, Hkv, P, D), -junk, dtype=v.dtype, device=v.device)
+    nxt = 0
+    for b in range(B):
+        for i in range(need[b]):
+            pid = int(perm[nxt])
+            nxt += 1
+            table[b, i] = pid
+            lo, hi = i * P, min((i + 1) * P, L_cap)
+            kp[pid, :, :hi - lo] = k[b, :, lo:hi]
+            vp[pid, :, :hi - lo] = v[b, :, lo:hi]
+    bt = torch.as_tensor(table, device=k.device)
+    return {"k_pages": kp, "v_pages": vp, "block_table": bt, "stride": stride}
 
 
 def ring_slot_of_token(t: int, W: int, S: int) -> int:

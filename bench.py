@@ -90,6 +90,8 @@ def parse():
     p.add_argument("--page-size", type=int, default=0,
                    help="read the verify cache through a block table of pages of this many "
                         "keys (a seeded shuffle of the contiguous cache); 0 = contiguous")
+    p.add_argument("--logits", choices=["f32", "bf16"], default="f32",
+                   help="dtype of the target and draft logits given to the sampling calls")
     p.add_argument("--copy-probe-mib", type=int, default=0,
                    help="also run plain device copies of this many MiB (calibrates HBM "
                         "byte counters: the copy reads and writes exactly this much)")
@@ -204,6 +206,10 @@ def main():
     L.lib()  # fail loudly if the library is missing
     log(f"[bench] building inputs for {cfg.name}")
     att, parent, win, smp = build_inputs(cfg, dev)
+    if args.logits == "bf16":
+        smp["target"] = smp["target"].to(torch.bfloat16)
+        smp["draft"] = smp["draft"].to(torch.bfloat16)
+    lsz = smp["target"].element_size()
     B, Hq, Hkv, D, Lk, nq = cfg.batch, cfg.hq, cfg.hkv, cfg.head_dim, cfg.kv_len, cfg.n_q
     dt = att["q"].dtype
     esz = att["q"].element_size()
@@ -321,8 +327,8 @@ def main():
     op_bytes_in = {"verify_attn": att["k"].numel() * esz * 2,
                    "window_attn": 0 if win is None else
                    (win["k_ring"].numel() + win["k_sink"].numel()) * esz * 2,
-                   "sample": smp["target"].numel() * 8,
-                   "draft_sample": B * V * 4,
+                   "sample": smp["target"].numel() * 2 * lsz,
+                   "draft_sample": B * V * lsz,
                    "kv_commit": 0}
     op_us = {}
     preps = {"kv_commit": prep_commit}
@@ -366,11 +372,11 @@ def main():
         ops_report["window_attn"] = {"us": op_us["window_attn"], "bytes": wbytes,
                                      "GBps": wbytes / op_us["window_attn"] / 1e3}
     srows = sample_rows_read(N, parent if cfg.tree else None)
-    sbytes = B * srows * V * 4
+    sbytes = B * srows * V * lsz
     ops_report["sample"] = {"us": op_us["sample"], "bytes": sbytes,
                             "GBps": sbytes / op_us["sample"] / 1e3}
     ops_report["sample"]["hbm_frac"] = ops_report["sample"]["GBps"] / HBM_PEAK_GBPS
-    dbytes = B * V * 4
+    dbytes = B * V * lsz
     ops_report["draft_sample"] = {"us": op_us["draft_sample"], "bytes": dbytes,
                                   "GBps": dbytes / op_us["draft_sample"] / 1e3}
     # Commit: K and V rows of the accepted path read and written back, from the
@@ -409,7 +415,7 @@ def main():
         "config": {"workload": cfg.name, "batch": B, "q_heads": Hq, "kv_heads": Hkv,
                    "head_dim": D, "kv_len": Lk, "block": "tree" if cfg.tree else "chain",
                    "gamma": nq - 1, "draft_window": cfg.window, "sinks": cfg.sinks,
-                   "vocab": V, "kv_layout": (f"paged, {args.page_size} keys per page"
+                   "vocab": V, "logits": args.logits, "kv_layout": (f"paged, {args.page_size} keys per page"
                                              if args.page_size else "contiguous"),
                    "parallelism": "single-gpu"},
         "verify_attn_GBps": ops_report["verify_attn"]["GBps"],

@@ -247,6 +247,23 @@ spec_status_t spec_sample(const float* target_logits, const float* draft_logits,
 size_t spec_sample_workspace(int32_t B, int32_t N, int32_t V);
 
 /*
+ * spec_sample_bf16 -- spec_sample with bfloat16 logits.
+ *
+ * Defines: the same computation as spec_sample; the pages fix no logit
+ * precision, and bf16 halves the bytes of the sampling tail.  target_logits
+ * and draft_logits are [B, N, V] bfloat16 (bit patterns, 16-byte aligned);
+ * every logit widens exactly to fp32 and the arithmetic is that of
+ * spec_sample.  Workspace: spec_sample_workspace(B, N, V).
+ */
+spec_status_t spec_sample_bf16(const void* target_logits, const void* draft_logits,
+                               const int32_t* tokens, const int32_t* parent,
+                               int32_t parent_batch_stride, int32_t B, int32_t N, int32_t V,
+                               uint64_t seed, uint64_t offset, int32_t* out_tokens,
+                               int32_t* out_count, int32_t* out_path, uint8_t* out_accept,
+                               void* workspace, size_t workspace_bytes, int32_t* dev_err,
+                               hipStream_t stream);
+
+/*
  * spec_draft_sample -- one draft-step token draw per sequence.
  *
  * Defines: "Guide to MagicDec", step 2 of its reference implementation (the
@@ -258,8 +275,8 @@ size_t spec_sample_workspace(int32_t B, int32_t N, int32_t V);
  * 4*offset+1)) from output word x%4 (U as in spec_sample); the largest score
  * wins, ties go to the lowest id.  The race picks x with probability p_x.
  *
- *   draft_logits  fp32, row b at draft_logits + b*row_stride, V entries
- *                 (row_stride 0 = V).  With row_stride = N*V and the pointer
+ *   draft_logits  dtype (SPEC_F32 or SPEC_BF16), row b at draft_logits +
+ *                 b*row_stride elements, V entries (row_stride 0 = V).  With row_stride = N*V and the pointer
  *                 at row u of spec_sample's [B, N, V] draft logits, the draw
  *                 reads, in place, the row that u's child is drawn from.
  *   node          id of the node being drawn (chain: draft step j draws node
@@ -273,8 +290,8 @@ size_t spec_sample_workspace(int32_t B, int32_t N, int32_t V);
  * A row with no finite logit sets SPEC_DEVERR_LOGITS and gets token -1 (and
  * a NaN log-probability).  Logits must be finite or -inf.
  */
-spec_status_t spec_draft_sample(const float* draft_logits, int64_t row_stride, int32_t B,
-                                int32_t V, uint64_t seed, uint64_t offset, int32_t node,
+spec_status_t spec_draft_sample(const void* draft_logits, spec_dtype_t dtype, int64_t row_stride,
+                                int32_t B, int32_t V, uint64_t seed, uint64_t offset, int32_t node,
                                 int32_t* out_token, int32_t token_stride, float* out_logprob,
                                 void* workspace, size_t workspace_bytes, int32_t* dev_err,
                                 hipStream_t stream);

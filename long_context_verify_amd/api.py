@@ -42,8 +42,10 @@ _SIGNATURES = {
     "spec_sample": (_i32, [_vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _u64, _u64, _vp, _vp, _vp,
                            _vp, _vp, _sz, _vp, _vp]),
     "spec_sample_workspace": (_sz, [_i32] * 3),
-    "spec_draft_sample": (_i32, [_vp, ctypes.c_int64, _i32, _i32, _u64, _u64, _i32, _vp, _i32,
-                                 _vp, _vp, _sz, _vp, _vp]),
+    "spec_sample_bf16": (_i32, [_vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _u64, _u64, _vp, _vp,
+                                _vp, _vp, _vp, _sz, _vp, _vp]),
+    "spec_draft_sample": (_i32, [_vp, _i32, ctypes.c_int64, _i32, _i32, _u64, _u64, _i32, _vp,
+                                 _i32, _vp, _vp, _sz, _vp, _vp]),
     "spec_draft_sample_workspace": (_sz, [_i32, _i32]),
     "spec_kv_commit": (_i32, [_vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _i32, _i32, _vp,
                               _i32, _vp, _vp]),
@@ -246,8 +248,8 @@ def spec_sample(target_logits, draft_logits, tokens, parent=None, seed: int = 0,
     """spec_sample on torch tensors.  Returns dict(out_tokens, out_count, out_path, out_accept)."""
     _need_gpu(target_logits, draft_logits, tokens, out_tokens, out_count, out_path, out_accept,
               dev_err)
-    if target_logits.dtype != torch.float32 or draft_logits.dtype != torch.float32:
-        raise ValueError("logits must be float32")
+    if target_logits.dtype not in _DTYPES or draft_logits.dtype != target_logits.dtype:
+        raise ValueError("logits must be float32 or bfloat16 (both the same)")
     if tokens.dtype != torch.int32:
         raise ValueError("tokens must be int32")
     B, N, V = target_logits.shape
@@ -262,7 +264,8 @@ def spec_sample(target_logits, draft_logits, tokens, parent=None, seed: int = 0,
         out_accept = torch.empty(B, N, dtype=torch.uint8, device=dev)
     par, pstride = _parent_arg(parent, B, N, dev)
     ws = _workspace(sample_workspace_bytes(B, N, V), dev, workspace)
-    st = lib().spec_sample(
+    entry = lib().spec_sample_bf16 if target_logits.dtype == torch.bfloat16 else lib().spec_sample
+    st = entry(
         _p(target_logits), _p(draft_logits), _p(tokens), _p(par), pstride, B, N, V,
         int(seed) & (2**64 - 1), int(offset), _p(out_tokens), _p(out_count), _p(out_path),
         _p(out_accept), _p(ws), ws.numel(), _p(dev_err), _stream(dev))
@@ -283,8 +286,8 @@ def draft_sample(draft_logits, node: int, seed: int = 0, offset: int = 0, out_to
     of a [B, N, V] tensor); ``out_token`` may be a strided column of a [B, N]
     int32 tensor.  Returns (out_token, out_logprob)."""
     _need_gpu(draft_logits, out_token, out_logprob, dev_err, strided_ok=(0, 1))
-    if draft_logits.dtype != torch.float32 or draft_logits.dim() != 2:
-        raise ValueError("draft_logits must be a [B, V] float32 tensor")
+    if draft_logits.dtype not in _DTYPES or draft_logits.dim() != 2:
+        raise ValueError("draft_logits must be a [B, V] float32 or bfloat16 tensor")
     if draft_logits.stride(1) != 1:
         raise ValueError("draft_logits rows must be contiguous")
     B, V = draft_logits.shape
@@ -299,7 +302,8 @@ def draft_sample(draft_logits, node: int, seed: int = 0, offset: int = 0, out_to
         out_logprob = torch.empty(B, dtype=torch.float32, device=dev)
     ws = _workspace(draft_sample_workspace_bytes(B, V), dev, workspace)
     st = lib().spec_draft_sample(
-        _p(draft_logits), int(draft_logits.stride(0)) if B > 1 else V, B, V,
+        _p(draft_logits), _DTYPES[draft_logits.dtype], int(draft_logits.stride(0)) if B > 1 else V,
+        B, V,
         int(seed) & (2**64 - 1), int(offset), int(node), _p(out_token),
         int(out_token.stride(0)) if B > 1 else 1, _p(out_logprob), _p(ws), ws.numel(),
         _p(dev_err), _stream(dev))

@@ -287,12 +287,17 @@ size_t spec_sample_workspace(int32_t B, int32_t N, int32_t V) {
   return plan_sample(B, N, V).bytes;
 }
 
-spec_status_t spec_sample(const float* target_logits, const float* draft_logits,
+}  // extern "C"
+
+namespace {
+
+spec_status_t sample_call(const void* target_logits, const void* draft_logits,
                           const int32_t* tokens, const int32_t* parent,
                           int32_t parent_batch_stride, int32_t B, int32_t N, int32_t V,
                           uint64_t seed, uint64_t offset, int32_t* out_tokens, int32_t* out_count,
                           int32_t* out_path, uint8_t* out_accept, void* workspace,
-                          size_t workspace_bytes, int32_t* dev_err, hipStream_t stream) {
+                          size_t workspace_bytes, int32_t* dev_err, hipStream_t stream,
+                          bool bf16) {
   spec_status_t st = sample_shape(B, N, V);
   if (st != SPEC_OK) return st;
   if (offset >= (1ull << 30)) return SPEC_ERR_INVALID_ARG;
@@ -333,8 +338,36 @@ spec_status_t spec_sample(const float* target_logits, const float* draft_logits,
   a.vchunk = p.vchunk;
   a.n_race = p.n_race;
   a.n_groups = p.n_groups;
+  a.logits_bf16 = bf16 ? 1 : 0;
   a.dev_err = dev_err;
   return launch_sample(a, stream) == hipSuccess ? SPEC_OK : SPEC_ERR_HIP;
+}
+
+}  // namespace
+
+extern "C" {
+
+spec_status_t spec_sample(const float* target_logits, const float* draft_logits,
+                          const int32_t* tokens, const int32_t* parent,
+                          int32_t parent_batch_stride, int32_t B, int32_t N, int32_t V,
+                          uint64_t seed, uint64_t offset, int32_t* out_tokens, int32_t* out_count,
+                          int32_t* out_path, uint8_t* out_accept, void* workspace,
+                          size_t workspace_bytes, int32_t* dev_err, hipStream_t stream) {
+  return sample_call(target_logits, draft_logits, tokens, parent, parent_batch_stride, B, N, V,
+                     seed, offset, out_tokens, out_count, out_path, out_accept, workspace,
+                     workspace_bytes, dev_err, stream, false);
+}
+
+spec_status_t spec_sample_bf16(const void* target_logits, const void* draft_logits,
+                               const int32_t* tokens, const int32_t* parent,
+                               int32_t parent_batch_stride, int32_t B, int32_t N, int32_t V,
+                               uint64_t seed, uint64_t offset, int32_t* out_tokens,
+                               int32_t* out_count, int32_t* out_path, uint8_t* out_accept,
+                               void* workspace, size_t workspace_bytes, int32_t* dev_err,
+                               hipStream_t stream) {
+  return sample_call(target_logits, draft_logits, tokens, parent, parent_batch_stride, B, N, V,
+                     seed, offset, out_tokens, out_count, out_path, out_accept, workspace,
+                     workspace_bytes, dev_err, stream, true);
 }
 
 size_t spec_draft_sample_workspace(int32_t B, int32_t V) {
@@ -342,18 +375,20 @@ size_t spec_draft_sample_workspace(int32_t B, int32_t V) {
   return plan_draft(B, V).bytes;
 }
 
-spec_status_t spec_draft_sample(const float* draft_logits, int64_t row_stride, int32_t B,
-                                int32_t V, uint64_t seed, uint64_t offset, int32_t node,
+spec_status_t spec_draft_sample(const void* draft_logits, spec_dtype_t dtype, int64_t row_stride,
+                                int32_t B, int32_t V, uint64_t seed, uint64_t offset, int32_t node,
                                 int32_t* out_token, int32_t token_stride, float* out_logprob,
                                 void* workspace, size_t workspace_bytes, int32_t* dev_err,
                                 hipStream_t stream) {
   if (B < 0 || V < 1 || node < 0 || token_stride < 0) return SPEC_ERR_INVALID_ARG;
+  if (dtype != SPEC_F32 && dtype != SPEC_BF16) return SPEC_ERR_INVALID_ARG;
   if (V > (1 << 27) || B > 65535) return SPEC_ERR_UNSUPPORTED;
   if (offset >= (1ull << 30)) return SPEC_ERR_INVALID_ARG;
   if (row_stride == 0) row_stride = V;
   if (row_stride < V) return SPEC_ERR_INVALID_ARG;
   if (B == 0) return SPEC_OK;
-  if (!aligned(draft_logits, 4) || !aligned(out_token, 4) || !aligned_or_null(out_logprob, 4) ||
+  const size_t elt = dtype == SPEC_BF16 ? 2 : 4;
+  if (!aligned(draft_logits, elt) || !aligned(out_token, 4) || !aligned_or_null(out_logprob, 4) ||
       !aligned_or_null(dev_err, 4))
     return SPEC_ERR_MISALIGNED;
   const DraftPlan p = plan_draft(B, V);
@@ -378,9 +413,10 @@ spec_status_t spec_draft_sample(const float* draft_logits, int64_t row_stride, i
   a.part_m = reinterpret_cast<float*>(ws + p.off_m);
   a.part_s = reinterpret_cast<double*>(ws + p.off_s);
   a.n_chunks = p.n_chunks;
+  a.logits_bf16 = dtype == SPEC_BF16 ? 1 : 0;
   a.dev_err = dev_err;
-  // 16-byte loads when every row starts 16-byte aligned and holds whole vectors.
-  const bool vec4 = aligned(draft_logits, 16) && V % 4 == 0 && row_stride % 4 == 0;
+  // Vector loads (4 ids) when every row starts aligned and holds whole vectors.
+  const bool vec4 = aligned(draft_logits, 4 * elt) && V % 4 == 0 && row_stride % 4 == 0;
   return launch_draft(a, vec4, stream) == hipSuccess ? SPEC_OK : SPEC_ERR_HIP;
 }
 

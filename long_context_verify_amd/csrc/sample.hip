@@ -69,6 +69,24 @@ __device__ __forceinline__ double uniform24(uint32_t w) {
   return ((double)(w >> 9) * 2.0 + 1.0) * 5.9604644775390625e-08;  // 2^-24
 }
 
+// Logit loads, fp32 or bf16 in memory, fp32 in registers (bf16 widens exactly).
+template <typename T>
+__device__ __forceinline__ float ld1(const T* row, size_t e) {
+  return (float)row[e];
+}
+// Ids e .. e+3 (e a multiple of 4, rows aligned to whole vectors): one 16-byte
+// (fp32) or 8-byte (bf16) load.
+template <typename T>
+__device__ __forceinline__ f32x4 ld4(const T* row, size_t e) {
+  if constexpr (sizeof(T) == 4) {
+    return reinterpret_cast<const f32x4*>(row)[e >> 2];
+  } else {
+    const uint2 w = reinterpret_cast<const uint2*>(row)[e >> 2];
+    return f32x4{__uint_as_float(w.x << 16), __uint_as_float(w.x & 0xffff0000u),
+                 __uint_as_float(w.y << 16), __uint_as_float(w.y & 0xffff0000u)};
+  }
+}
+
 __device__ __forceinline__ int parent_of(const SampleArgs& a, int b, int c) {
   if (!a.parent) return c - 1;
   return a.parent[(size_t)b * a.parent_stride + c];
@@ -125,7 +143,7 @@ __device__ __forceinline__ void block_argmax(double& s, int& i, double* reds, in
 // ---------------------------------------------------------------------------
 // Row statistics.
 // ---------------------------------------------------------------------------
-template <bool VEC4>
+template <bool VEC4, typename T>
 __global__ __launch_bounds__(kSampleThreads) void sample_stats(SampleArgs a) {
   __shared__ float redf[4];
   __shared__ double redd[4];
@@ -138,17 +156,16 @@ __global__ __launch_bounds__(kSampleThreads) void sample_stats(SampleArgs a) {
     for (int c = 1 + threadIdx.x; c < a.N; c += kSampleThreads) has |= parent_of(a, b, c) == u;
     if (!__syncthreads_or(has)) return;
   }
-  const float* row = (kind ? a.draft : a.target) + ((size_t)b * a.N + u) * a.V;
+  const T* row = static_cast<const T*>(kind ? a.draft : a.target) + ((size_t)b * a.N + u) * a.V;
   const int x0 = chunk * a.vchunk;
   constexpr int PER = kStatsChunk / kSampleThreads;  // 32
   float x[PER];
   if (VEC4) {
-    const f32x4* row4 = reinterpret_cast<const f32x4*>(row);
 #pragma unroll
     for (int i = 0; i < PER / 4; ++i) {
       const int e = x0 + 4 * (threadIdx.x + kSampleThreads * i);
       f32x4 v = {-INFINITY, -INFINITY, -INFINITY, -INFINITY};
-      if (e < a.V) v = row4[e >> 2];   // V % 4 == 0: a vector is wholly in or out
+      if (e < a.V) v = ld4(row, e);   // V % 4 == 0: a vector is wholly in or out
 #pragma unroll
       for (int k = 0; k < 4; ++k) x[4 * i + k] = v[k];
     }
@@ -156,7 +173,7 @@ __global__ __launch_bounds__(kSampleThreads) void sample_stats(SampleArgs a) {
 #pragma unroll
     for (int i = 0; i < PER; ++i) {
       const int e = x0 + threadIdx.x + kSampleThreads * i;
-      x[i] = e < a.V ? row[e] : -INFINITY;
+      x[i] = e < a.V ? ld1(row, e) : -INFINITY;
     }
   }
   float mx = x[0];
@@ -205,6 +222,7 @@ struct Decision {
   bool residual;
 };
 
+template <typename T>
 __device__ void decide_sequence(const SampleArgs& a, int b, Decision& d) {
   const int N = a.N, V = a.V;
   const int tid = threadIdx.x;
@@ -217,8 +235,8 @@ __device__ void decide_sequence(const SampleArgs& a, int b, Decision& d) {
     p = parent_of(a, b, c_tok);
     x = a.tokens[(size_t)b * N + c_tok];
     if (p >= 0 && p < c_tok && x >= 0 && x < V) {
-      tl = a.target[((size_t)b * N + p) * V + x];
-      dl = a.draft[((size_t)b * N + p) * V + x];
+      tl = ld1(static_cast<const T*>(a.target), ((size_t)b * N + p) * V + x);
+      dl = ld1(static_cast<const T*>(a.draft), ((size_t)b * N + p) * V + x);
     }
   }
   if (tid == 0) d.bad = 0;
@@ -321,13 +339,13 @@ __device__ void decide_sequence(const SampleArgs& a, int b, Decision& d) {
 // Residual (or target) mass of the stop row's 1024-id race chunks q0 .. q1-1
 // of this group.  Every work-group of a sequence derives the same decision;
 // group 0 stores it.
-template <bool VEC4>
+template <bool VEC4, typename T>
 __global__ __launch_bounds__(kSampleThreads) void sample_resid(SampleArgs a) {
   __shared__ Decision d;
   const int grp = blockIdx.x, b = blockIdx.y;
   const int N = a.N, V = a.V;
   const int tid = threadIdx.x;
-  decide_sequence(a, b, d);
+  decide_sequence<T>(a, b, d);
   const bool bad = d.bad != 0;
   const bool residual = d.residual;
   const int r = d.stop;
@@ -347,8 +365,8 @@ __global__ __launch_bounds__(kSampleThreads) void sample_resid(SampleArgs a) {
       st[1] = residual ? d.lz[1][r] : 0.0;
     }
   }
-  const float* trow = a.target + ((size_t)b * N + r) * V;
-  const float* drow = a.draft + ((size_t)b * N + r) * V;
+  const T* trow = static_cast<const T*>(a.target) + ((size_t)b * N + r) * V;
+  const T* drow = static_cast<const T*>(a.draft) + ((size_t)b * N + r) * V;
   const float tm = d.m[0][r];
   const float tinv = (float)(1.0 / d.s[0][r]);
   const float dm = residual ? d.m[1][r] : 0.f;
@@ -371,8 +389,8 @@ __global__ __launch_bounds__(kSampleThreads) void sample_resid(SampleArgs a) {
         if (VEC4) {
           f32x4 t4 = {-INFINITY, -INFINITY, -INFINITY, -INFINITY}, d4 = t4;
           if (e0 < V) {
-            t4 = reinterpret_cast<const f32x4*>(trow)[e0 >> 2];
-            if (residual) d4 = reinterpret_cast<const f32x4*>(drow)[e0 >> 2];
+            t4 = ld4(trow, e0);
+            if (residual) d4 = ld4(drow, e0);
           }
 #pragma unroll
           for (int k = 0; k < 4; ++k) {
@@ -383,8 +401,8 @@ __global__ __launch_bounds__(kSampleThreads) void sample_resid(SampleArgs a) {
 #pragma unroll
           for (int k = 0; k < 4; ++k) {
             const int e = e0 + k;
-            tv[k] = e < V ? trow[e] : -INFINITY;
-            dv[k] = (e < V && residual) ? drow[e] : -INFINITY;
+            tv[k] = e < V ? ld1(trow, e) : -INFINITY;
+            dv[k] = (e < V && residual) ? ld1(drow, e) : -INFINITY;
           }
         }
 #pragma unroll
@@ -421,7 +439,7 @@ __global__ __launch_bounds__(kSampleThreads) void sample_resid(SampleArgs a) {
 // ---------------------------------------------------------------------------
 // The draw at the stop row and the outputs: one work-group per sequence.
 // ---------------------------------------------------------------------------
-template <bool VEC4>
+template <typename T>
 __global__ __launch_bounds__(kSampleThreads) void sample_race(SampleArgs a) {
   __shared__ double redd[4];
   __shared__ int redi[4];
@@ -448,8 +466,8 @@ __global__ __launch_bounds__(kSampleThreads) void sample_race(SampleArgs a) {
   const int r = dec[3];
   const double* st = a.decision_lz + (size_t)b * 2;
   const double lzt = st[0], lzd = st[1];
-  const float* trow = a.target + ((size_t)b * N + r) * V;
-  const float* drow = a.draft + ((size_t)b * N + r) * V;
+  const T* trow = static_cast<const T*>(a.target) + ((size_t)b * N + r) * V;
+  const T* drow = static_cast<const T*>(a.draft) + ((size_t)b * N + r) * V;
 
   // Level 1: chunks race with score W_c / E1_c.  After a rejection the
   // weights are the residual masses; if they all vanish, the target's.
@@ -485,10 +503,10 @@ __global__ __launch_bounds__(kSampleThreads) void sample_race(SampleArgs a) {
     pt[k] = 0.0;
     wx[k] = 0.0;
     if (e < V) {
-      pt[k] = exp((double)trow[e] - lzt);
+      pt[k] = exp((double)ld1(trow, e) - lzt);
       wx[k] = pt[k];
       if (use_resid) {
-        const double pd = exp((double)drow[e] - lzd);
+        const double pd = exp((double)ld1(drow, e) - lzd);
         wx[k] = pt[k] - pd > 0.0 ? pt[k] - pd : 0.0;
       }
     }
@@ -553,19 +571,23 @@ SamplePlan plan_sample(int32_t B, int32_t N, int32_t V) {
   return p;
 }
 
-hipError_t launch_sample(const SampleArgs& a, hipStream_t stream) {
+template <typename T>
+static hipError_t launch_sample_t(const SampleArgs& a, hipStream_t stream) {
   const bool vec4 = (a.V % 4) == 0;
   dim3 g1(a.n_vchunks, 2 * a.N, a.B), g2(a.n_groups, a.B), g3(a.B), blk(kSampleThreads);
   if (vec4) {
-    hipLaunchKernelGGL(sample_stats<true>, g1, blk, 0, stream, a);
-    hipLaunchKernelGGL(sample_resid<true>, g2, blk, 0, stream, a);
-    hipLaunchKernelGGL(sample_race<true>, g3, blk, 0, stream, a);
+    hipLaunchKernelGGL((sample_stats<true, T>), g1, blk, 0, stream, a);
+    hipLaunchKernelGGL((sample_resid<true, T>), g2, blk, 0, stream, a);
   } else {
-    hipLaunchKernelGGL(sample_stats<false>, g1, blk, 0, stream, a);
-    hipLaunchKernelGGL(sample_resid<false>, g2, blk, 0, stream, a);
-    hipLaunchKernelGGL(sample_race<false>, g3, blk, 0, stream, a);
+    hipLaunchKernelGGL((sample_stats<false, T>), g1, blk, 0, stream, a);
+    hipLaunchKernelGGL((sample_resid<false, T>), g2, blk, 0, stream, a);
   }
+  hipLaunchKernelGGL((sample_race<T>), g3, blk, 0, stream, a);
   return hipGetLastError();
+}
+
+hipError_t launch_sample(const SampleArgs& a, hipStream_t stream) {
+  return a.logits_bf16 ? launch_sample_t<__bf16>(a, stream) : launch_sample_t<float>(a, stream);
 }
 
 // ---------------------------------------------------------------------------
@@ -610,13 +632,13 @@ __device__ __forceinline__ void block_argmax_f(RaceBest& r, RaceBest* red) {
 // g = chunk*512 + t + 256*i (i < 2), four consecutive ids per group, so one
 // Philox call serves one 16-byte load.  Small chunks give many work-groups:
 // the Philox rounds, not the bytes, set the time of a 0.5 MB row.
-template <bool VEC4>
+template <bool VEC4, typename T>
 __global__ __launch_bounds__(kSampleThreads) void draft_partial(DraftArgs a) {
   __shared__ float redf[4];
   __shared__ double redd[4];
   __shared__ RaceBest redr[4];
   const int chunk = blockIdx.x, b = blockIdx.y;
-  const float* row = a.logits + (size_t)b * a.row_stride;
+  const T* row = static_cast<const T*>(a.logits) + (size_t)b * a.row_stride;
   constexpr int GROUPS = kDraftChunk / 4 / kSampleThreads;  // 2
   const int g0 = chunk * (kDraftChunk / 4) + threadIdx.x;
   float x[4 * GROUPS];
@@ -625,12 +647,12 @@ __global__ __launch_bounds__(kSampleThreads) void draft_partial(DraftArgs a) {
     const int e = 4 * (g0 + kSampleThreads * i);
     if (VEC4) {
       f32x4 v = {-INFINITY, -INFINITY, -INFINITY, -INFINITY};
-      if (e < a.V) v = reinterpret_cast<const f32x4*>(row)[e >> 2];
+      if (e < a.V) v = ld4(row, e);
 #pragma unroll
       for (int k = 0; k < 4; ++k) x[4 * i + k] = v[k] * kLog2e;
     } else {
 #pragma unroll
-      for (int k = 0; k < 4; ++k) x[4 * i + k] = e + k < a.V ? row[e + k] * kLog2e : -INFINITY;
+      for (int k = 0; k < 4; ++k) x[4 * i + k] = e + k < a.V ? ld1(row, e + k) * kLog2e : -INFINITY;
     }
   }
   // Race: one Philox block per group of four ids.
@@ -724,10 +746,17 @@ DraftPlan plan_draft(int32_t B, int32_t V) {
 
 hipError_t launch_draft(const DraftArgs& a, bool vec4, hipStream_t stream) {
   dim3 g1(a.n_chunks, a.B), g2(a.B), blk(kSampleThreads);
-  if (vec4)
-    hipLaunchKernelGGL(draft_partial<true>, g1, blk, 0, stream, a);
-  else
-    hipLaunchKernelGGL(draft_partial<false>, g1, blk, 0, stream, a);
+  if (a.logits_bf16) {
+    if (vec4)
+      hipLaunchKernelGGL((draft_partial<true, __bf16>), g1, blk, 0, stream, a);
+    else
+      hipLaunchKernelGGL((draft_partial<false, __bf16>), g1, blk, 0, stream, a);
+  } else {
+    if (vec4)
+      hipLaunchKernelGGL((draft_partial<true, float>), g1, blk, 0, stream, a);
+    else
+      hipLaunchKernelGGL((draft_partial<false, float>), g1, blk, 0, stream, a);
+  }
   hipLaunchKernelGGL(draft_finish, g2, blk, 0, stream, a);
   return hipGetLastError();
 }

@@ -70,8 +70,8 @@ hipError_t launch_attention(const AttnArgs& a, bool window, spec_dtype_t dtype, 
                             float* lse, hipStream_t stream);
 
 struct SampleArgs {
-  const float* target;
-  const float* draft;
+  const void* target;      // [B][N][V] logits, fp32 or bf16 (logits_bf16)
+  const void* draft;
   const int32_t* tokens;
   const int32_t* parent;
   int32_t parent_stride;
@@ -93,6 +93,7 @@ struct SampleArgs {
   int32_t vchunk;          // ids per stats chunk
   int32_t n_race;          // race chunks per row (1024 ids each)
   int32_t n_groups;        // resample work-groups per sequence
+  int32_t logits_bf16;
   int32_t* dev_err;
 };
 
@@ -121,7 +122,7 @@ hipError_t launch_commit(const CommitArgs& a, hipStream_t stream);
 
 // One draft-step token draw per sequence.
 struct DraftArgs {
-  const float* logits;      // row b at logits + b * row_stride, V entries
+  const void* logits;       // row b at logits + b * row_stride, V entries (fp32 or bf16)
   int64_t row_stride;
   int32_t B, V;
   uint32_t key0, key1;
@@ -136,6 +137,7 @@ struct DraftArgs {
   float* part_m;            // [B][n_chunks] max of logit * log2(e)
   double* part_s;           // [B][n_chunks] sum of exp2(x - max)
   int32_t n_chunks;
+  int32_t logits_bf16;
   int32_t* dev_err;
 };
 

@@ -130,11 +130,16 @@ def test_sample_argument_checks():
     assert _sample(parent=P, pstride=4) == INVALID
     assert _sample(tgt=P_ODD) == MISALIGNED
     assert _sample() == WORKSPACE
+    assert L.lib().spec_sample_bf16(P, P, P, NULL, 0, 2, 5, 1000, 1, 0, P, P, NULL, NULL, P, 0,
+                                    NULL, NULL) == WORKSPACE
+    assert L.lib().spec_sample_bf16(P_ODD, P, P, NULL, 0, 2, 5, 1000, 1, 0, P, P, NULL, NULL, P,
+                                    0, NULL, NULL) == MISALIGNED
 
 
-def _draft(B=2, V=1000, stride=0, node=1, offset=0, logits=P, tok=P, tstride=0, ws_bytes=0):
-    return L.lib().spec_draft_sample(logits, stride, B, V, 1, offset, node, tok, tstride, NULL, P,
-                                     ws_bytes, NULL, NULL)
+def _draft(B=2, V=1000, stride=0, node=1, offset=0, logits=P, tok=P, tstride=0, ws_bytes=0,
+           dtype=0):
+    return L.lib().spec_draft_sample(logits, dtype, stride, B, V, 1, offset, node, tok, tstride,
+                                     NULL, P, ws_bytes, NULL, NULL)
 
 
 def test_draft_sample_argument_checks():
@@ -146,6 +151,9 @@ def test_draft_sample_argument_checks():
     assert _draft(stride=999) == INVALID
     assert _draft(tstride=-1) == INVALID
     assert _draft(logits=NULL) == MISALIGNED
+    assert _draft(dtype=3) == INVALID
+    assert _draft(logits=ctypes.c_void_p(0x10002)) == MISALIGNED
+    assert _draft(logits=ctypes.c_void_p(0x10002), dtype=1) == WORKSPACE
     assert _draft(tok=ctypes.c_void_p(0x10002)) == MISALIGNED
     assert _draft() == WORKSPACE
     assert L.draft_sample_workspace_bytes(8, 128256) >= 8 * 16 * 20

@@ -46,13 +46,17 @@ CASES = [
 ]
 
 
-@pytest.mark.parametrize("case", CASES, ids=[c[0] for c in CASES])
+@pytest.mark.parametrize("case", CASES + [
+    ("bf16_v128256_b8", 8, 128256, 3.0), ("bf16_v5001_scalar", 64, 5001, 3.0)],
+    ids=[c[0] for c in CASES] + ["bf16_v128256_b8", "bf16_v5001_scalar"])
 def test_draft_sample_parity(case):
     import long_context_verify_amd as L
     name, B, V, std = case
     say(f"draft_sample {name}")
     g = torch.Generator().manual_seed(B * 7919 + V)
     logits = (torch.randn(B, V, generator=g) * std).float()
+    if name.startswith("bf16"):
+        logits = logits.to(torch.bfloat16)   # the oracle widens the same bf16 values
     seed, offset, node = 0xD4AF7 + V, 3, 2
     tok, lp = L.draft_sample(logits.to(DEV), node, seed=seed, offset=offset)
     torch.cuda.synchronize()

@@ -84,6 +84,47 @@ def test_sample_full_size(name):
     assert np.all((g["out_count"] >= 1) & (g["out_count"] <= cfg.n_nodes))
 
 
+BF16_CASES = [
+    # name, B, N, V, tree
+    ("bf16_chain_v5000", 48, 5, 5000, False),
+    ("bf16_chain_v5001_scalar", 32, 4, 5001, False),
+    ("bf16_tree16_v2048", 24, 16, 2048, True),
+]
+
+
+@pytest.mark.parametrize("case", BF16_CASES, ids=[c[0] for c in BF16_CASES])
+def test_sample_parity_bf16_logits(case):
+    """bf16 logits (spec_sample_bf16): the oracle reads the same bf16 values, widened exactly."""
+    name, B, N, V, tree = case
+    say(f"sample {name}")
+    parent = random_tree(N, max_depth=4, max_children=3, seed=11) if tree else None
+    x = make_sample_inputs(B, N, V, parent, 3.0, draft_noise_std=1.0, seed=sum(map(ord, name)),
+                           device=DEV)
+    x["target"] = x["target"].to(torch.bfloat16)
+    x["draft"] = x["draft"].to(torch.bfloat16)
+    for offset in (0, 3):
+        seed = 0xBF160000 + offset
+        g = _gpu(x, parent, seed, offset)
+        o = oracle_sample(x["target"], x["draft"], x["tokens"], parent, seed=seed, offset=offset)
+        _compare(g, o, f"{name} offset {offset}")
+
+
+@pytest.mark.parametrize("name", ["llama8b_32k_chain", "medusa_tree64_8k"])
+def test_sample_full_size_bf16_logits(name):
+    cfg = CONFIGS[name]
+    say(f"sample full-size bf16 logits {name}")
+    parent = random_tree(cfg.n_nodes) if cfg.tree else None
+    x = make_sample_inputs(cfg.batch, cfg.n_nodes, cfg.vocab, parent, cfg.target_std,
+                           draft_noise_std=cfg.draft_noise_std, draft_std=cfg.draft_std,
+                           seed=cfg.seed, device=DEV)
+    x["target"] = x["target"].to(torch.bfloat16)
+    x["draft"] = x["draft"].to(torch.bfloat16)
+    seed = 0xBF160000 + cfg.seed
+    g = _gpu(x, parent, seed, 0)
+    o = oracle_sample(x["target"], x["draft"], x["tokens"], parent, seed=seed, offset=0)
+    _compare(g, o, name)
+
+
 def test_equal_distributions_accept_all():
     say("sample equal distributions")
     B, N, V = 64, 5, 3000

@@ -31,6 +31,16 @@ notes of the repository):
 * the walk takes, at each node, the first child (lowest index) that passed its
   test; for a chain this is exactly "stop at the first rejection";
 * residual weights max(Pt - Pd, 0); if they sum to zero, Pt is used;
+* with ``siblings="lossless"`` (a rule the pages name through SpecInfer's
+  tree verification but do not spell out) the children of a node are tested
+  in index order against a distribution that is updated after each
+  rejection: p_0 = the target row, and after child i is rejected
+  p_i = normalised max(p_{i-1} - q, 0), q the draft row of the node.  The
+  first child with u_c < p_{i-1}(x_c) / q(x_c) is taken; if all are
+  rejected the draw comes from the last p_i.  When the children's tokens were
+  drawn independently from q this keeps every emitted token distributed as
+  the target (multi-round speculative sampling); for a chain it is the rule
+  above;
 * the draw from a weight vector w is a two-level exponential race: chunks of
   1024 ids compete with score W_c / E1_c, E1_c = -ln U(philox(c, row, b,
   4*offset+2), word 0); inside the winning chunk ids compete with score
@@ -110,7 +120,7 @@ def race_draw(w: np.ndarray, seed: int, b: int, row: int, offset: int,
 
 
 def spec_sample(target_logits, draft_logits, tokens, parent=None, seed: int = 0,
-                offset: int = 0, chunk: int = RACE_CHUNK):
+                offset: int = 0, chunk: int = RACE_CHUNK, siblings: str = "first"):
     """Accept/resample/bonus for a batch of chains or candidate trees.
 
     target_logits, draft_logits: [B,N,V]; tokens: [B,N] (tokens[:,0] unused);
@@ -121,7 +131,11 @@ def spec_sample(target_logits, draft_logits, tokens, parent=None, seed: int = 0,
       out_accept [B,N] uint8 (per-node test; node 0 reported as 1),
     and per-sequence diagnostics: ratio [B,N], u [B,N], stop_row [B],
     residual [B] bool, wsum [B], margin1 [B], margin2 [B], exempt [B] bool.
+    siblings: "first" (each node tested against the target row; the walk takes
+    the first child that passed) or "lossless" (see the module notes).
     """
+    if siblings not in ("first", "lossless"):
+        raise ValueError("siblings must be 'first' or 'lossless'")
     t = _f64(target_logits)
     d = _f64(draft_logits)
     tok = np.asarray(_f64(tokens), dtype=np.int64)
@@ -160,53 +174,101 @@ def spec_sample(target_logits, draft_logits, tokens, parent=None, seed: int = 0,
                 Pt[u] = softmax(t[b, u])
                 Pd[u] = softmax(d[b, u])
 
-        # per-node acceptance tests, each with its own counter-based uniform
+        # per-node uniforms from the counter-based generator
         cs = np.arange(1, N)
         uc = uniforms(seed, cs, 0, b, 4 * offset + STREAM_ACCEPT, 0) if N > 1 else np.zeros(0)
+        for c in range(1, N):
+            if not (0 <= int(tok[b, c]) < V):
+                raise ValueError("drafted token out of range")
+            u_all[b, c] = uc[c - 1]
+
+        def ratio_of(pnum, pden):
+            if pden > 0:
+                return pnum / pden
+            return np.inf if pnum > 0 else 0.0
+
+        near_tie = False
+        small_mass = False
         acc = np.zeros(N, dtype=bool)
         acc[0] = True
-        for c in range(1, N):
-            p = int(par[c])
-            x = int(tok[b, c])
-            if not (0 <= x < V):
-                raise ValueError("drafted token out of range")
-            pt, pd = Pt[p][x], Pd[p][x]
-            if pd > 0:
-                r = pt / pd
-            else:
-                r = np.inf if pt > 0 else 0.0
-            ratio_all[b, c] = r
-            u_all[b, c] = uc[c - 1]
-            acc[c] = uc[c - 1] < r
-        out_accept[b] = acc.astype(np.uint8)
-
-        # walk from the root: first accepted child in index order
-        cur = 0
-        path = [0]
-        near_tie = False
-        while True:
-            nxt = None
-            for c in children[cur]:
-                if abs(ratio_all[b, c] - u_all[b, c]) <= TIE_BAND:
-                    near_tie = True
-                if acc[c]:
-                    nxt = c
+        if siblings == "first":
+            # every node tested against its parent's rows; the walk takes the
+            # first child (index order) that passed
+            for c in range(1, N):
+                p = int(par[c])
+                x = int(tok[b, c])
+                ratio_all[b, c] = ratio_of(Pt[p][x], Pd[p][x])
+                acc[c] = uc[c - 1] < ratio_all[b, c]
+            cur = 0
+            path = [0]
+            while True:
+                nxt = None
+                for c in children[cur]:
+                    if abs(ratio_all[b, c] - u_all[b, c]) <= TIE_BAND:
+                        near_tie = True
+                    if acc[c]:
+                        nxt = c
+                        break
+                if nxt is None:
                     break
-            if nxt is None:
-                break
-            path.append(nxt)
-            cur = nxt
-
-        # stop row: residual after a rejection, target distribution at a leaf
-        if children[cur]:
-            w = np.maximum(Pt[cur] - Pd[cur], 0.0)
-            residual[b] = True
-            wsum[b] = float(np.sum(w))
-            if wsum[b] <= 0.0:
-                w = Pt[cur]
+                path.append(nxt)
+                cur = nxt
+            # stop row: residual after a rejection, target distribution at a leaf
+            if children[cur]:
+                w = np.maximum(Pt[cur] - Pd[cur], 0.0)
+                residual[b] = True
+                wsum[b] = float(np.sum(w))
+                if wsum[b] <= 0.0:
+                    w = Pt[cur]
+            else:
+                w = softmax(t[b, cur])
+                wsum[b] = 1.0
         else:
-            w = softmax(t[b, cur])
-            wsum[b] = 1.0
+            # siblings tested in index order against p_i, updated after each rejection
+            cur = 0
+            path = [0]
+            while True:
+                if not children[cur]:
+                    w = softmax(t[b, cur])
+                    wsum[b] = 1.0
+                    break
+                q = Pd[cur]
+                p_i = Pt[cur]
+                # p_i = max(p - shift q, 0) / mass in closed form; only used to size
+                # the near-tie band (a kernel evaluating that form in fp32 sums
+                # carries an error of about 1e-7 (p(x)/q(x) + 2 shift) / mass)
+                shift, mass = 0.0, 1.0
+                nxt = None
+                for c in children[cur]:
+                    x = int(tok[b, c])
+                    r = ratio_of(p_i[x], q[x])
+                    ratio_all[b, c] = r
+                    scale = 1.0
+                    if q[x] > 0 and np.isfinite(r):
+                        scale = max(1.0, (Pt[cur][x] / q[x] + 2.0 * shift) / mass + r)
+                    if abs(r - uc[c - 1]) <= TIE_BAND * scale:
+                        near_tie = True
+                    if uc[c - 1] < r:
+                        acc[c] = True
+                        nxt = c
+                        break
+                    res = np.maximum(p_i - q, 0.0)
+                    z = float(np.sum(res))
+                    shift, mass = shift + mass, mass * z
+                    if mass <= WSUM_FLOOR:
+                        small_mass = True
+                    if z <= 0.0:
+                        p_i = None
+                        break
+                    p_i = res / z
+                if nxt is None:
+                    residual[b] = p_i is not None
+                    w = p_i if p_i is not None else Pt[cur]
+                    wsum[b] = mass if p_i is not None else 1.0
+                    break
+                path.append(nxt)
+                cur = nxt
+        out_accept[b] = acc.astype(np.uint8)
         y, m1, m2 = race_draw(w, seed, b, cur, offset, chunk)
 
         k = len(path)
@@ -217,8 +279,8 @@ def spec_sample(target_logits, draft_logits, tokens, parent=None, seed: int = 0,
         out_count[b] = k
         stop_row[b] = cur
         margin1[b], margin2[b] = m1, m2
-        exempt[b] = (near_tie or m1 <= 1.0 + RACE_MARGIN or m2 <= 1.0 + RACE_MARGIN
-                     or (residual[b] and wsum[b] <= WSUM_FLOOR))
+        exempt[b] = (near_tie or small_mass or m1 <= 1.0 + RACE_MARGIN
+                     or m2 <= 1.0 + RACE_MARGIN or (residual[b] and wsum[b] <= WSUM_FLOOR))
 
     return {
         "out_tokens": out_tokens, "out_count": out_count, "out_path": out_path,

@@ -207,3 +207,76 @@ def test_offsets_and_seeds_give_independent_rounds():
     assert not np.array_equal(a["u"][:, 1:], c["u"][:, 1:])
     a2 = spec_sample(x["target"], x["draft"], x["tokens"], seed=1, offset=0)
     assert np.array_equal(a["out_tokens"], a2["out_tokens"])
+
+
+# --- lossless sibling rule -------------------------------------------------------------------
+
+# A tree whose node rows depend only on depth: the root, three children, and two
+# children under each of those (N = 10).
+_SIB_PARENT = np.array([-1, 0, 0, 0, 1, 1, 2, 2, 3, 3])
+_SIB_DEPTH = np.array([0, 1, 1, 1, 2, 2, 2, 2, 2, 2])
+
+
+def test_lossless_chain_equals_first_rule():
+    x = make_sample_inputs(300, 5, 700, None, 3.0, draft_noise_std=1.0, seed=41)
+    a = spec_sample(x["target"], x["draft"], x["tokens"], seed=7, offset=3)
+    b = spec_sample(x["target"], x["draft"], x["tokens"], seed=7, offset=3, siblings="lossless")
+    for k in ("out_tokens", "out_count", "out_path"):
+        assert np.array_equal(a[k], b[k]), k
+    # The lossless walk tests only the nodes it reaches (up to the first rejection).
+    for bb in range(300):
+        reach = min(int(a["out_count"][bb]) + 1, 5)
+        assert np.array_equal(a["out_accept"][bb, :reach], b["out_accept"][bb, :reach])
+        assert not b["out_accept"][bb, reach:].any()
+
+
+def test_lossless_rule_keeps_every_position_on_the_target():
+    """Siblings drawn independently from the draft row: each emitted token follows the
+    target row of its depth (chi-square), although several siblings compete."""
+    V, B = 6, 30000
+    t = _rows(V, 3, 1.3, 51)[_SIB_DEPTH]
+    d = _rows(V, 3, 1.3, 52)[_SIB_DEPTH]
+    x = make_sample_inputs(B, 10, V, _SIB_PARENT, 0, target=_batch(t, B), draft=_batch(d, B),
+                           seed=53)
+    r = spec_sample(x["target"], x["draft"], x["tokens"], _SIB_PARENT, seed=54, offset=1,
+                    siblings="lossless")
+    cnt, out = r["out_count"], r["out_tokens"]
+    assert np.all((cnt >= 1) & (cnt <= 3))
+    for pos in range(3):
+        sel = cnt >= pos + 1
+        assert _chisq_ok(out[sel, pos], softmax(t[int(np.argmax(_SIB_DEPTH == pos))].double()
+                                                 .numpy())), f"position {pos}"
+
+
+def test_lossless_rule_hand_worked_two_siblings():
+    """V = 2, p = (0.9, 0.1), q = (0.5, 0.5), two leaf children both drafting token 1.
+    The first test passes with probability 0.2; after its rejection p becomes (1, 0), so
+    the second child (token 1) can never pass and the draw is token 0."""
+    B = 20000
+    t = torch.log(torch.tensor([[0.9, 0.1]] * 3, dtype=torch.float64)).float()
+    d = torch.log(torch.tensor([[0.5, 0.5]] * 3, dtype=torch.float64)).float()
+    parent = np.array([-1, 0, 0])
+    x = make_sample_inputs(B, 3, 2, parent, 0, target=_batch(t, B), draft=_batch(d, B), seed=61)
+    x["tokens"][:, 1:] = 1
+    r = spec_sample(x["target"], x["draft"], x["tokens"], parent, seed=62, siblings="lossless")
+    cnt, path, out = r["out_count"], r["out_path"], r["out_tokens"]
+    assert not np.any(path[:, 1] == 2)                 # the second sibling never passes
+    assert np.all(out[cnt == 1, 0] == 0)               # after both rejections: token 0
+    rate = np.mean(cnt == 2)
+    assert abs(rate - 0.2) <= 4 * np.sqrt(0.2 * 0.8 / B)
+    # The first-accepted rule tests the second child against p itself: 0.2 + 0.8 * 0.2.
+    f = spec_sample(x["target"], x["draft"], x["tokens"], parent, seed=62)
+    assert abs(np.mean(f["out_count"] == 2) - 0.36) <= 4 * np.sqrt(0.36 * 0.64 / B)
+
+
+def test_lossless_first_sibling_test_is_the_plain_ratio():
+    parent = random_tree(20, seed=8)
+    x = make_sample_inputs(40, 20, 300, parent, 3.0, draft_noise_std=1.0, seed=71)
+    a = spec_sample(x["target"], x["draft"], x["tokens"], parent, seed=3)
+    b = spec_sample(x["target"], x["draft"], x["tokens"], parent, seed=3, siblings="lossless")
+    children = [[c for c in range(20) if parent[c] == u] for u in range(20)]
+    for bb in range(40):
+        for u in b["out_path"][bb][b["out_path"][bb] >= 0]:
+            if children[u]:
+                c = children[u][0]
+                assert b["ratio"][bb, c] == a["ratio"][bb, c]

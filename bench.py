@@ -90,6 +90,8 @@ def parse():
     p.add_argument("--page-size", type=int, default=0,
                    help="read the verify cache through a block table of pages of this many "
                         "keys (a seeded shuffle of the contiguous cache); 0 = contiguous")
+    p.add_argument("--siblings", choices=["first", "lossless"], default="first",
+                   help="sibling rule of the sampling tail on candidate trees")
     p.add_argument("--logits", choices=["f32", "bf16"], default="f32",
                    help="dtype of the target and draft logits given to the sampling calls")
     p.add_argument("--copy-probe-mib", type=int, default=0,
@@ -255,7 +257,7 @@ def main():
 
     def op_sample(i):
         L.spec_sample(smp["target"], smp["draft"], smp["tokens"], parent=par_t if cfg.tree else None,
-                      seed=seed, offset=i, workspace=ws_s, **s_out)
+                      seed=seed, offset=i, workspace=ws_s, siblings=args.siblings, **s_out)
 
     ops = [("verify_attn", lambda i: op_verify())]
     if win is not None:
@@ -415,7 +417,7 @@ def main():
         "config": {"workload": cfg.name, "batch": B, "q_heads": Hq, "kv_heads": Hkv,
                    "head_dim": D, "kv_len": Lk, "block": "tree" if cfg.tree else "chain",
                    "gamma": nq - 1, "draft_window": cfg.window, "sinks": cfg.sinks,
-                   "vocab": V, "logits": args.logits, "kv_layout": (f"paged, {args.page_size} keys per page"
+                   "vocab": V, "logits": args.logits, "siblings": args.siblings, "kv_layout": (f"paged, {args.page_size} keys per page"
                                              if args.page_size else "contiguous"),
                    "parallelism": "single-gpu"},
         "verify_attn_GBps": ops_report["verify_attn"]["GBps"],

@@ -63,6 +63,12 @@ typedef enum {
 
 typedef enum { SPEC_F32 = 0, SPEC_BF16 = 1 } spec_dtype_t;
 
+/* How siblings of a candidate tree are tested (spec_sample_ex). */
+typedef enum {
+  SPEC_SIBLINGS_FIRST = 0,   /* every node against the target row; first passing child */
+  SPEC_SIBLINGS_LOSSLESS = 1 /* in order, against residuals updated after each rejection */
+} spec_sibling_rule_t;
+
 /* Bits OR-ed into *dev_err by the kernels. */
 #define SPEC_DEVERR_KV_LEN 0x1    /* kv_len[b] outside [n_q, L_cap] */
 #define SPEC_DEVERR_PARENT 0x2    /* parent[c] outside [-1, c) (sampling: a root other than 0) */
@@ -337,6 +343,42 @@ spec_status_t spec_kv_commit(void* k_cache, void* v_cache, int32_t* kv_len, cons
                              const int32_t* count, int32_t B, int32_t Hkv, int32_t n_q, int32_t D,
                              int32_t L_cap, spec_dtype_t dtype, int32_t* draft_total_len,
                              int32_t draft_appended, int32_t* dev_err, hipStream_t stream);
+
+/*
+ * spec_sample_ex -- spec_sample with a logit dtype and a sibling rule.
+ *
+ * Defines: spec_sample's computation, plus the rule for candidate trees.  The
+ * pages name tree verification in the style of SpecInfer and Medusa ("Speculative
+ * Decoding in LLM Serving Systems", section "Tree-based variants"; "Speculative
+ * Decoding & Medusa Architecture", section 4) without the acceptance rule
+ * among siblings.
+ *   SPEC_SIBLINGS_FIRST     spec_sample's rule: each node c is tested with its
+ *                           own uniform against min(1, p(x_c)/q(x_c)) at its
+ *                           parent; the walk takes the first child that passed.
+ *   SPEC_SIBLINGS_LOSSLESS  at the node the walk stands on, its children are
+ *                           tested in index order against p_i, where p_0 = p
+ *                           and p_{i+1} = normalised max(p_i - q, 0) after
+ *                           child i is rejected (q the node's draft row); the
+ *                           first child with u_c < p_i(x_c)/q(x_c) is taken.
+ *                           If all are rejected the draw comes from the last
+ *                           p_i (from p if its mass vanishes).  When siblings
+ *                           are drawn independently from q, every emitted token
+ *                           follows the target distribution.  Each rejected
+ *                           sibling costs one pass over the node's two rows, in
+ *                           one extra kernel with one work-group per sequence.
+ *                           Untested nodes report out_accept 0.
+ * For a chain both rules give the same tokens, counts and paths.
+ * logits_dtype: SPEC_F32 (as spec_sample) or SPEC_BF16 (as spec_sample_bf16).
+ * Other arguments and the workspace are as in spec_sample.
+ */
+spec_status_t spec_sample_ex(const void* target_logits, const void* draft_logits,
+                             spec_dtype_t logits_dtype, spec_sibling_rule_t siblings,
+                             const int32_t* tokens, const int32_t* parent,
+                             int32_t parent_batch_stride, int32_t B, int32_t N, int32_t V,
+                             uint64_t seed, uint64_t offset, int32_t* out_tokens,
+                             int32_t* out_count, int32_t* out_path, uint8_t* out_accept,
+                             void* workspace, size_t workspace_bytes, int32_t* dev_err,
+                             hipStream_t stream);
 
 /*
  * spec_validate_tree -- host-side check of a parent array (host pointer).

@@ -42,6 +42,8 @@ _SIGNATURES = {
     "spec_sample": (_i32, [_vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _u64, _u64, _vp, _vp, _vp,
                            _vp, _vp, _sz, _vp, _vp]),
     "spec_sample_workspace": (_sz, [_i32] * 3),
+    "spec_sample_ex": (_i32, [_vp, _vp, _i32, _i32, _vp, _vp, _i32, _i32, _i32, _i32, _u64, _u64,
+                              _vp, _vp, _vp, _vp, _vp, _sz, _vp, _vp]),
     "spec_sample_bf16": (_i32, [_vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _u64, _u64, _vp, _vp,
                                 _vp, _vp, _vp, _sz, _vp, _vp]),
     "spec_draft_sample": (_i32, [_vp, _i32, ctypes.c_int64, _i32, _i32, _u64, _u64, _i32, _vp,
@@ -244,8 +246,14 @@ def sample_workspace_bytes(B, N, V) -> int:
 
 def spec_sample(target_logits, draft_logits, tokens, parent=None, seed: int = 0, offset: int = 0,
                 out_tokens=None, out_count=None, out_path=None, out_accept=None,
-                workspace=None, dev_err=None, want_path: bool = True, want_accept: bool = True):
-    """spec_sample on torch tensors.  Returns dict(out_tokens, out_count, out_path, out_accept)."""
+                workspace=None, dev_err=None, want_path: bool = True, want_accept: bool = True,
+                siblings: str = "first"):
+    """spec_sample on torch tensors.  Returns dict(out_tokens, out_count, out_path, out_accept).
+
+    fp32 logits go to spec_sample, bf16 to spec_sample_bf16; siblings="lossless"
+    selects spec_sample_ex's lossless sibling rule."""
+    if siblings not in ("first", "lossless"):
+        raise ValueError("siblings must be 'first' or 'lossless'")
     _need_gpu(target_logits, draft_logits, tokens, out_tokens, out_count, out_path, out_accept,
               dev_err)
     if target_logits.dtype not in _DTYPES or draft_logits.dtype != target_logits.dtype:
@@ -264,11 +272,16 @@ def spec_sample(target_logits, draft_logits, tokens, parent=None, seed: int = 0,
         out_accept = torch.empty(B, N, dtype=torch.uint8, device=dev)
     par, pstride = _parent_arg(parent, B, N, dev)
     ws = _workspace(sample_workspace_bytes(B, N, V), dev, workspace)
-    entry = lib().spec_sample_bf16 if target_logits.dtype == torch.bfloat16 else lib().spec_sample
-    st = entry(
-        _p(target_logits), _p(draft_logits), _p(tokens), _p(par), pstride, B, N, V,
-        int(seed) & (2**64 - 1), int(offset), _p(out_tokens), _p(out_count), _p(out_path),
-        _p(out_accept), _p(ws), ws.numel(), _p(dev_err), _stream(dev))
+    args = (_p(tokens), _p(par), pstride, B, N, V, int(seed) & (2**64 - 1), int(offset),
+            _p(out_tokens), _p(out_count), _p(out_path), _p(out_accept), _p(ws), ws.numel(),
+            _p(dev_err), _stream(dev))
+    if siblings == "lossless":
+        st = lib().spec_sample_ex(_p(target_logits), _p(draft_logits),
+                                  _DTYPES[target_logits.dtype], 1, *args)
+    elif target_logits.dtype == torch.bfloat16:
+        st = lib().spec_sample_bf16(_p(target_logits), _p(draft_logits), *args)
+    else:
+        st = lib().spec_sample(_p(target_logits), _p(draft_logits), *args)
     _check(st, "spec_sample")
     return {"out_tokens": out_tokens, "out_count": out_count, "out_path": out_path,
             "out_accept": out_accept}

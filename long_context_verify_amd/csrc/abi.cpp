@@ -297,7 +297,7 @@ spec_status_t sample_call(const void* target_logits, const void* draft_logits,
                           uint64_t seed, uint64_t offset, int32_t* out_tokens, int32_t* out_count,
                           int32_t* out_path, uint8_t* out_accept, void* workspace,
                           size_t workspace_bytes, int32_t* dev_err, hipStream_t stream,
-                          bool bf16) {
+                          bool bf16, bool lossless) {
   spec_status_t st = sample_shape(B, N, V);
   if (st != SPEC_OK) return st;
   if (offset >= (1ull << 30)) return SPEC_ERR_INVALID_ARG;
@@ -339,6 +339,7 @@ spec_status_t sample_call(const void* target_logits, const void* draft_logits,
   a.n_race = p.n_race;
   a.n_groups = p.n_groups;
   a.logits_bf16 = bf16 ? 1 : 0;
+  a.lossless = lossless ? 1 : 0;
   a.dev_err = dev_err;
   return launch_sample(a, stream) == hipSuccess ? SPEC_OK : SPEC_ERR_HIP;
 }
@@ -355,7 +356,7 @@ spec_status_t spec_sample(const float* target_logits, const float* draft_logits,
                           size_t workspace_bytes, int32_t* dev_err, hipStream_t stream) {
   return sample_call(target_logits, draft_logits, tokens, parent, parent_batch_stride, B, N, V,
                      seed, offset, out_tokens, out_count, out_path, out_accept, workspace,
-                     workspace_bytes, dev_err, stream, false);
+                     workspace_bytes, dev_err, stream, false, false);
 }
 
 spec_status_t spec_sample_bf16(const void* target_logits, const void* draft_logits,
@@ -367,7 +368,24 @@ spec_status_t spec_sample_bf16(const void* target_logits, const void* draft_logi
                                hipStream_t stream) {
   return sample_call(target_logits, draft_logits, tokens, parent, parent_batch_stride, B, N, V,
                      seed, offset, out_tokens, out_count, out_path, out_accept, workspace,
-                     workspace_bytes, dev_err, stream, true);
+                     workspace_bytes, dev_err, stream, true, false);
+}
+
+spec_status_t spec_sample_ex(const void* target_logits, const void* draft_logits,
+                             spec_dtype_t logits_dtype, spec_sibling_rule_t siblings,
+                             const int32_t* tokens, const int32_t* parent,
+                             int32_t parent_batch_stride, int32_t B, int32_t N, int32_t V,
+                             uint64_t seed, uint64_t offset, int32_t* out_tokens,
+                             int32_t* out_count, int32_t* out_path, uint8_t* out_accept,
+                             void* workspace, size_t workspace_bytes, int32_t* dev_err,
+                             hipStream_t stream) {
+  if (logits_dtype != SPEC_F32 && logits_dtype != SPEC_BF16) return SPEC_ERR_INVALID_ARG;
+  if (siblings != SPEC_SIBLINGS_FIRST && siblings != SPEC_SIBLINGS_LOSSLESS)
+    return SPEC_ERR_INVALID_ARG;
+  return sample_call(target_logits, draft_logits, tokens, parent, parent_batch_stride, B, N, V,
+                     seed, offset, out_tokens, out_count, out_path, out_accept, workspace,
+                     workspace_bytes, dev_err, stream, logits_dtype == SPEC_BF16,
+                     siblings == SPEC_SIBLINGS_LOSSLESS);
 }
 
 size_t spec_draft_sample_workspace(int32_t B, int32_t V) {

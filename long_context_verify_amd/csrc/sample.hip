@@ -42,6 +42,7 @@
 namespace specv {
 
 constexpr int kSampleThreads = 256;
+constexpr int kDecideThreads = 512;    // lossless decide: one work-group streams the rows
 constexpr int kRaceChunk = 1024;
 constexpr int kStatsChunk = 8192;   // ids per stats work-group (32 per thread)
 constexpr int kDraftChunk = 2048;   // ids per draft-draw work-group (8 per thread)
@@ -111,6 +112,21 @@ __device__ __forceinline__ double block_sum(double v, double* red) {
   if ((threadIdx.x & 63) == 0) red[w] = v;
   __syncthreads();
   return (red[0] + red[1]) + (red[2] + red[3]);
+}
+
+// Sum over a work-group of NT threads (NT / 64 waves).
+template <int NT>
+__device__ __forceinline__ double block_sum_nt(double v, double* red) {
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) v += __shfl_xor(v, off);
+  const int w = threadIdx.x >> 6;
+  __syncthreads();
+  if ((threadIdx.x & 63) == 0) red[w] = v;
+  __syncthreads();
+  double t = 0.0;
+#pragma unroll
+  for (int k = 0; k < NT / 64; ++k) t += red[k];
+  return t;
 }
 
 // Arg-max of (score, index) with ties to the lowest index.
@@ -220,10 +236,26 @@ struct Decision {
   int path[SPEC_MAX_SAMPLE_NODES];
   int len, bad, stop;
   bool residual;
+  double shift;                           // residual weights max(pt - shift * pd, 0)
 };
 
-template <typename T>
-__device__ void decide_sequence(const SampleArgs& a, int b, Decision& d) {
+// Per-node inputs of the lossless sibling walk.
+struct SiblingTests {
+  double ratio0[SPEC_MAX_SAMPLE_NODES];   // p_target(x_c) / p_draft(x_c) at the parent
+  double pt[SPEC_MAX_SAMPLE_NODES];       // p_target(x_c) at the parent
+  double pd[SPEC_MAX_SAMPLE_NODES];       // p_draft(x_c) at the parent
+  float u[SPEC_MAX_SAMPLE_NODES];         // acceptance uniform of node c
+  int16_t par[SPEC_MAX_SAMPLE_NODES];
+  double red[kDecideThreads / kWave];
+};
+
+template <typename T, int NT, bool CACHE>
+__device__ void lossless_walk(const SampleArgs& a, int b, Decision& d, SiblingTests& st);
+
+// NT: threads of the calling work-group.
+template <typename T, bool LOSSLESS = false, int NT = kSampleThreads, bool CACHE = false>
+__device__ void decide_sequence(const SampleArgs& a, int b, Decision& d,
+                                SiblingTests* st = nullptr) {
   const int N = a.N, V = a.V;
   const int tid = threadIdx.x;
 
@@ -240,9 +272,9 @@ __device__ void decide_sequence(const SampleArgs& a, int b, Decision& d) {
     }
   }
   if (tid == 0) d.bad = 0;
-  for (int u = tid; u < N; u += kSampleThreads) d.has_child[u] = 0;
+  for (int u = tid; u < N; u += NT) d.has_child[u] = 0;
   __syncthreads();
-  for (int c = 1 + tid; c < N; c += kSampleThreads) {
+  for (int c = 1 + tid; c < N; c += NT) {
     const int pc = parent_of(a, b, c);
     if (pc < 0 || pc >= c)
       d.bad = 1;
@@ -257,7 +289,7 @@ __device__ void decide_sequence(const SampleArgs& a, int b, Decision& d) {
   // rows side by side, so the partials arrive in one round.
   const int nv = a.n_vchunks;
   const int GL = nv >= 64 ? 64 : (nv > 32 ? 64 : nv > 16 ? 32 : nv > 8 ? 16 : nv > 4 ? 8 : 4);
-  const int rows_per_pass = kSampleThreads / GL;
+  const int rows_per_pass = NT / GL;
   for (int base = 0; base < 2 * N; base += rows_per_pass) {
     const int rs = base + tid / GL;
     const int k0 = tid % GL;
@@ -286,6 +318,32 @@ __device__ void decide_sequence(const SampleArgs& a, int b, Decision& d) {
     }
   }
   __syncthreads();
+  if constexpr (LOSSLESS) {
+    // Per-node log-probabilities and uniforms; the walk tests them in order.
+    if (tid == 0) d.acc[0] = 1;
+    if (c_tok < N) {
+      d.acc[c_tok] = 0;
+      st->par[c_tok] = (int16_t)p;
+      if (!bad_tree) {
+        if (x < 0 || x >= V) {
+          d.bad = 2;
+        } else {
+          const double lp = (double)tl - d.lz[0][p], lq = (double)dl - d.lz[1][p];
+          // The plain ratio is computed as in the first-accepted rule.
+          st->ratio0[c_tok] = (dl == -INFINITY) ? ((tl == -INFINITY) ? 0.0 : INFINITY)
+                                                : exp(lp - lq);
+          st->pt[c_tok] = exp(lp);
+          st->pd[c_tok] = exp(lq);
+          uint32_t c0 = (uint32_t)c_tok, c1 = 0u, c2 = (uint32_t)b, c3 = a.ctr3_base + 0u;
+          philox4x32_10(c0, c1, c2, c3, a.key0, a.key1);
+          st->u[c_tok] = (float)uniform24(c0);
+        }
+      }
+    }
+    __syncthreads();
+    lossless_walk<T, NT, CACHE>(a, b, d, *st);
+    return;
+  }
   if (tid == 0) d.acc[0] = 1;
   if (c_tok < N) {
     bool ok = false;
@@ -331,46 +389,268 @@ __device__ void decide_sequence(const SampleArgs& a, int b, Decision& d) {
       d.len = len;
       d.stop = cur;
       d.residual = d.has_child[cur] != 0;
+      d.shift = 1.0;
     }
   }
   __syncthreads();
 }
 
+// Sum over the vocabulary of max(pt - shift * pd, 0) at row r (fp32 terms, fp64
+// accumulation): the mass left after `shift` draft distributions are taken off.
+template <typename T, int NT>
+__device__ double residual_mass(const SampleArgs& a, int b, int r, const Decision& d,
+                                double shift, double* red) {
+  const int N = a.N, V = a.V;
+  const T* trow = static_cast<const T*>(a.target) + ((size_t)b * N + r) * V;
+  const T* drow = static_cast<const T*>(a.draft) + ((size_t)b * N + r) * V;
+  const float tm = d.m[0][r], tinv = (float)(1.0 / d.s[0][r]);
+  const float dm = d.m[1][r], dinv = (float)(1.0 / d.s[1][r]);
+  const float sh = (float)shift;
+  double acc = 0.0;
+  if (V % 4 == 0) {
+    // Batches of kU vectors per row per thread, all loads issued before any
+    // use: one work-group streams the rows, so memory parallelism sets the pace.
+    constexpr int kU = 8;
+    for (int e0 = 4 * threadIdx.x; e0 < V; e0 += 4 * NT * kU) {
+      f32x4 t4[kU], d4[kU];
+#pragma unroll
+      for (int j = 0; j < kU; ++j) {
+        const int e = e0 + 4 * NT * j;
+        t4[j] = f32x4{-INFINITY, -INFINITY, -INFINITY, -INFINITY};
+        d4[j] = t4[j];
+        if (e < V) {
+          t4[j] = ld4(trow, e);
+          d4[j] = ld4(drow, e);
+        }
+      }
+      float part = 0.f;
+#pragma unroll
+      for (int j = 0; j < kU; ++j)
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+          const float pt = fast_exp2((t4[j][k] - tm) * kLog2e) * tinv;
+          const float pd = fast_exp2((d4[j][k] - dm) * kLog2e) * dinv;
+          part += fmaxf(pt - sh * pd, 0.f);
+        }
+      acc += (double)part;
+    }
+  } else {
+    for (int e = threadIdx.x; e < V; e += NT) {
+      const float pt = fast_exp2((ld1(trow, e) - tm) * kLog2e) * tinv;
+      const float pd = fast_exp2((ld1(drow, e) - dm) * kLog2e) * dinv;
+      acc += (double)fmaxf(pt - sh * pd, 0.f);
+    }
+  }
+  return block_sum_nt<NT>(acc, red);
+}
+
+// Row r's probabilities held in registers: thread t keeps ids 4 t + 4 NT j + k
+// (j < kCacheVec, k < 4), the layout of residual_mass's first batch, so the
+// sums below add the same terms in the same order.
+constexpr int kCacheVec = 16;
+
+template <typename T, int NT>
+__device__ __forceinline__ void load_row_probs(const SampleArgs& a, int b, int r,
+                                               const Decision& d, float (&cpt)[4 * kCacheVec],
+                                               float (&cpd)[4 * kCacheVec]) {
+  const int N = a.N, V = a.V;
+  const T* trow = static_cast<const T*>(a.target) + ((size_t)b * N + r) * V;
+  const T* drow = static_cast<const T*>(a.draft) + ((size_t)b * N + r) * V;
+  const float tm = d.m[0][r], tinv = (float)(1.0 / d.s[0][r]);
+  const float dm = d.m[1][r], dinv = (float)(1.0 / d.s[1][r]);
+  // Two halves, so at most half the raw vectors are live next to the cache.
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    constexpr int HV = kCacheVec / 2;
+    f32x4 t4[HV], d4[HV];
+#pragma unroll
+    for (int jj = 0; jj < HV; ++jj) {
+      const int e = 4 * threadIdx.x + 4 * NT * (h * HV + jj);
+      t4[jj] = f32x4{-INFINITY, -INFINITY, -INFINITY, -INFINITY};
+      d4[jj] = t4[jj];
+      if (e < V) {
+        t4[jj] = ld4(trow, e);
+        d4[jj] = ld4(drow, e);
+      }
+    }
+#pragma unroll
+    for (int jj = 0; jj < HV; ++jj)
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        cpt[4 * (h * HV + jj) + k] = fast_exp2((t4[jj][k] - tm) * kLog2e) * tinv;
+        cpd[4 * (h * HV + jj) + k] = fast_exp2((d4[jj][k] - dm) * kLog2e) * dinv;
+      }
+  }
+}
+
+template <int NT>
+__device__ __forceinline__ double cached_mass(const float (&cpt)[4 * kCacheVec],
+                                              const float (&cpd)[4 * kCacheVec], double shift,
+                                              double* red) {
+  const float sh = (float)shift;
+  float part = 0.f;
+#pragma unroll
+  for (int i = 0; i < 4 * kCacheVec; ++i) part += fmaxf(cpt[i] - sh * cpd[i], 0.f);
+  return block_sum_nt<NT>((double)part, red);
+}
+
+// Lossless sibling rule: at each node its children are tested in index order
+// against p_i = max(p - shift_i q, 0) / mass_i (p_0 = p); after a rejection
+// shift_{i+1} = shift_i + mass_i and mass_{i+1} = sum max(p - shift_{i+1} q, 0),
+// the closed form of normalising max(p_i - q, 0).  One vocabulary pass per
+// rejected sibling.  If every child is rejected the draw uses the residual
+// max(p - shift q, 0); a vanished mass falls back to p.
+// CACHE: the rows fit in registers (V % 4 == 0, V <= 4 kCacheVec NT).
+template <typename T, int NT, bool CACHE>
+__device__ void lossless_walk(const SampleArgs& a, int b, Decision& d, SiblingTests& st) {
+  const int N = a.N;
+  const int tid = threadIdx.x;
+  const bool bad = d.bad != 0;
+  int cur = 0, len = 1;
+  if (tid == 0) d.path[0] = 0;
+  bool residual = false;
+  double shift = 0.0;
+  // With CACHE the node's rows stay in registers while its siblings are
+  // tested: one load and one set of exponentials per node.
+  float cpt[CACHE ? 4 * kCacheVec : 1], cpd[CACHE ? 4 * kCacheVec : 1];
+  if (!bad) {
+    while (d.has_child[cur]) {
+      double sh = 0.0, mass = 1.0;
+      int nxt = -1;
+      bool vanished = false, cached = false;
+      // Children of cur in index order: one ballot per 64 candidates.
+      const int lane = tid & 63;
+      for (int base = cur + 1; base < N && nxt < 0 && !vanished; base += kWave) {
+        const int cl = base + lane;
+        unsigned long long kids = __ballot(cl < N && st.par[cl] == cur);
+        while (kids) {
+          const int c = base + __builtin_ctzll(kids);
+          kids &= kids - 1;
+          double ratio;
+          if (sh == 0.0) {
+            ratio = st.ratio0[c];
+          } else if (st.pd[c] == 0.0) {
+            ratio = (st.pt[c] - sh * st.pd[c] > 0.0) ? INFINITY : 0.0;
+          } else {
+            const double pc = st.pt[c] - sh * st.pd[c];
+            ratio = pc > 0.0 ? pc / (mass * st.pd[c]) : 0.0;
+          }
+          if ((double)st.u[c] < ratio) {
+            nxt = c;
+            break;
+          }
+          sh += mass;
+          if constexpr (CACHE) {
+            if (!cached) load_row_probs<T, NT>(a, b, cur, d, cpt, cpd);
+            cached = true;
+            mass = cached_mass<NT>(cpt, cpd, sh, st.red);
+          } else {
+            mass = residual_mass<T, NT>(a, b, cur, d, sh, st.red);
+          }
+          if (!(mass > 0.0)) {
+            vanished = true;
+            break;
+          }
+        }
+      }
+      if (nxt < 0) {
+        residual = !vanished;
+        shift = vanished ? 0.0 : sh;
+        break;
+      }
+      if (tid == 0) {
+        d.acc[nxt] = 1;
+        d.path[len] = nxt;
+      }
+      ++len;
+      cur = nxt;
+    }
+  }
+  if (tid == 0) {
+    d.len = len;
+    d.stop = cur;
+    d.residual = residual;
+    d.shift = shift;
+  }
+  __syncthreads();
+}
+
+// Store one sequence's decision record (group 0 of the residual kernel, or
+// the lossless decide kernel).
+__device__ __forceinline__ void store_decision(const SampleArgs& a, int b, const Decision& d) {
+  const int N = a.N, tid = threadIdx.x;
+  const int r = d.stop;
+  int32_t* dec = a.decision + (size_t)b * a.dec_stride;
+  for (int c = tid; c < N; c += (int)blockDim.x) {
+    dec[4 + c] = c < d.len ? d.path[c] : -1;
+    dec[4 + N + c] = d.acc[c];
+  }
+  if (tid == 0) {
+    dec[0] = d.len;
+    dec[1] = d.bad;
+    dec[2] = d.residual;
+    dec[3] = r;
+    double* st = a.decision_lz + (size_t)b * kDecisionDoubles;
+    st[0] = d.lz[0][r];
+    st[1] = d.residual ? d.lz[1][r] : 0.0;
+    st[2] = d.residual ? d.shift : 0.0;
+    st[3] = d.m[0][r];
+    st[4] = 1.0 / d.s[0][r];
+    st[5] = d.residual ? d.m[1][r] : 0.0;
+    st[6] = d.residual ? 1.0 / d.s[1][r] : 0.0;
+  }
+}
+
+// grid (B): the lossless walk, one work-group per sequence (its vocabulary
+// passes are sequential), stores the decision record.
+template <typename T, bool CACHE>
+__global__ __launch_bounds__(kDecideThreads) void sample_decide_lossless(SampleArgs a) {
+  __shared__ Decision d;
+  __shared__ SiblingTests st;
+  const int b = blockIdx.x;
+  decide_sequence<T, true, kDecideThreads, CACHE>(a, b, d, &st);
+  store_decision(a, b, d);
+}
+
 // Residual (or target) mass of the stop row's 1024-id race chunks q0 .. q1-1
 // of this group.  Every work-group of a sequence derives the same decision;
 // group 0 stores it.
-template <bool VEC4, typename T>
+// With FROM_RECORD the decision comes from the record the lossless decide
+// kernel stored.
+template <bool VEC4, typename T, bool FROM_RECORD = false>
 __global__ __launch_bounds__(kSampleThreads) void sample_resid(SampleArgs a) {
   __shared__ Decision d;
   const int grp = blockIdx.x, b = blockIdx.y;
   const int N = a.N, V = a.V;
   const int tid = threadIdx.x;
-  decide_sequence<T>(a, b, d);
-  const bool bad = d.bad != 0;
-  const bool residual = d.residual;
-  const int r = d.stop;
-  if (grp == 0) {
-    int32_t* dec = a.decision + (size_t)b * a.dec_stride;
-    for (int c = tid; c < N; c += kSampleThreads) {
-      dec[4 + c] = c < d.len ? d.path[c] : -1;
-      dec[4 + N + c] = d.acc[c];
-    }
-    if (tid == 0) {
-      dec[0] = d.len;
-      dec[1] = d.bad;
-      dec[2] = residual;
-      dec[3] = r;
-      double* st = a.decision_lz + (size_t)b * 2;
-      st[0] = d.lz[0][r];
-      st[1] = residual ? d.lz[1][r] : 0.0;
-    }
+  bool bad, residual;
+  int r;
+  float tm, tinv, dm, dinv, shift;
+  if constexpr (FROM_RECORD) {
+    const int32_t* dec = a.decision + (size_t)b * a.dec_stride;
+    const double* st = a.decision_lz + (size_t)b * kDecisionDoubles;
+    bad = dec[1] != 0;
+    residual = dec[2] != 0;
+    r = dec[3];
+    shift = (float)st[2];
+    tm = (float)st[3];
+    tinv = (float)st[4];
+    dm = (float)st[5];
+    dinv = (float)st[6];
+  } else {
+    decide_sequence<T>(a, b, d);
+    if (grp == 0) store_decision(a, b, d);
+    bad = d.bad != 0;
+    residual = d.residual;
+    r = d.stop;
+    shift = 1.f;
+    tm = d.m[0][r];
+    tinv = (float)(1.0 / d.s[0][r]);
+    dm = residual ? d.m[1][r] : 0.f;
+    dinv = residual ? (float)(1.0 / d.s[1][r]) : 0.f;
   }
   const T* trow = static_cast<const T*>(a.target) + ((size_t)b * N + r) * V;
   const T* drow = static_cast<const T*>(a.draft) + ((size_t)b * N + r) * V;
-  const float tm = d.m[0][r];
-  const float tinv = (float)(1.0 / d.s[0][r]);
-  const float dm = residual ? d.m[1][r] : 0.f;
-  const float dinv = residual ? (float)(1.0 / d.s[1][r]) : 0.f;
   const int q0 = (int)((long long)a.n_race * grp / a.n_groups);
   const int q1 = (int)((long long)a.n_race * (grp + 1) / a.n_groups);
   // Per chunk: each wave reduces its lanes with shuffles and parks the two
@@ -410,7 +690,7 @@ __global__ __launch_bounds__(kSampleThreads) void sample_resid(SampleArgs a) {
           const float pt = fast_exp2((tv[k] - tm) * kLog2e) * tinv;
           const float pd = residual ? fast_exp2((dv[k] - dm) * kLog2e) * dinv : 0.f;
           spt += pt;
-          sw += fmaxf(pt - pd, 0.f);
+          sw += fmaxf(pt - shift * pd, 0.f);
         }
       }
       const double tw = wave_sum((double)sw);
@@ -464,8 +744,8 @@ __global__ __launch_bounds__(kSampleThreads) void sample_race(SampleArgs a) {
     return;
   }
   const int r = dec[3];
-  const double* st = a.decision_lz + (size_t)b * 2;
-  const double lzt = st[0], lzd = st[1];
+  const double* st = a.decision_lz + (size_t)b * kDecisionDoubles;
+  const double lzt = st[0], lzd = st[1], shift = st[2];
   const T* trow = static_cast<const T*>(a.target) + ((size_t)b * N + r) * V;
   const T* drow = static_cast<const T*>(a.draft) + ((size_t)b * N + r) * V;
 
@@ -507,7 +787,7 @@ __global__ __launch_bounds__(kSampleThreads) void sample_race(SampleArgs a) {
       wx[k] = pt[k];
       if (use_resid) {
         const double pd = exp((double)ld1(drow, e) - lzd);
-        wx[k] = pt[k] - pd > 0.0 ? pt[k] - pd : 0.0;
+        wx[k] = pt[k] - shift * pd > 0.0 ? pt[k] - shift * pd : 0.0;
       }
     }
   }
@@ -567,7 +847,7 @@ SamplePlan plan_sample(int32_t B, int32_t N, int32_t V) {
   p.off_w = align256(p.off_s + rows * sizeof(double));
   p.off_dec = align256(p.off_w + (size_t)B * p.n_race * 2 * sizeof(double));
   p.off_lz = align256(p.off_dec + (size_t)B * p.dec_stride * sizeof(int32_t));
-  p.bytes = align256(p.off_lz + (size_t)B * 2 * sizeof(double));
+  p.bytes = align256(p.off_lz + (size_t)B * kDecisionDoubles * sizeof(double));
   return p;
 }
 
@@ -575,11 +855,25 @@ template <typename T>
 static hipError_t launch_sample_t(const SampleArgs& a, hipStream_t stream) {
   const bool vec4 = (a.V % 4) == 0;
   dim3 g1(a.n_vchunks, 2 * a.N, a.B), g2(a.n_groups, a.B), g3(a.B), blk(kSampleThreads);
-  if (vec4) {
+  if (vec4)
     hipLaunchKernelGGL((sample_stats<true, T>), g1, blk, 0, stream, a);
+  else
+    hipLaunchKernelGGL((sample_stats<false, T>), g1, blk, 0, stream, a);
+  if (a.lossless) {
+    // The sibling walk needs sequential vocabulary passes: one work-group per
+    // sequence decides, the residual groups read its record.
+    if (vec4 && a.V <= 4 * kCacheVec * kDecideThreads)
+      hipLaunchKernelGGL((sample_decide_lossless<T, true>), g3, dim3(kDecideThreads), 0, stream, a);
+    else
+      hipLaunchKernelGGL((sample_decide_lossless<T, false>), g3, dim3(kDecideThreads), 0, stream,
+                         a);
+    if (vec4)
+      hipLaunchKernelGGL((sample_resid<true, T, true>), g2, blk, 0, stream, a);
+    else
+      hipLaunchKernelGGL((sample_resid<false, T, true>), g2, blk, 0, stream, a);
+  } else if (vec4) {
     hipLaunchKernelGGL((sample_resid<true, T>), g2, blk, 0, stream, a);
   } else {
-    hipLaunchKernelGGL((sample_stats<false, T>), g1, blk, 0, stream, a);
     hipLaunchKernelGGL((sample_resid<false, T>), g2, blk, 0, stream, a);
   }
   hipLaunchKernelGGL((sample_race<T>), g3, blk, 0, stream, a);

@@ -87,15 +87,19 @@ struct SampleArgs {
   double* part_s;          // [B][2N][n_vchunks]
   double* race_w;          // [B][n_race][2]  (residual mass, target mass) per race chunk
   int32_t* decision;       // [B][dec_stride]: len, error, residual flag, -, path[N], accept[N]
-  double* decision_lz;     // [B][2]: log normalisers of the stop row (target, draft)
+  double* decision_lz;     // [B][kDecisionDoubles]: stop row's log normalisers (target,
+                           // draft), residual shift, and (max, 1/sum) of both rows
   int32_t dec_stride;
   int32_t n_vchunks;       // stats chunks per row
   int32_t vchunk;          // ids per stats chunk
   int32_t n_race;          // race chunks per row (1024 ids each)
   int32_t n_groups;        // resample work-groups per sequence
   int32_t logits_bf16;
+  int32_t lossless;        // siblings tested against successively updated residuals
   int32_t* dev_err;
 };
+
+constexpr int kDecisionDoubles = 8;
 
 struct SamplePlan {
   int32_t n_vchunks, vchunk, n_race, n_groups, dec_stride;

@@ -132,6 +132,9 @@ def test_sample_argument_checks():
     assert _sample() == WORKSPACE
     assert L.lib().spec_sample_bf16(P, P, P, NULL, 0, 2, 5, 1000, 1, 0, P, P, NULL, NULL, P, 0,
                                     NULL, NULL) == WORKSPACE
+    for dt, rule, want in [(0, 1, WORKSPACE), (1, 0, WORKSPACE), (2, 0, INVALID), (0, 2, INVALID)]:
+        assert L.lib().spec_sample_ex(P, P, dt, rule, P, NULL, 0, 2, 5, 1000, 1, 0, P, P, NULL,
+                                      NULL, P, 0, NULL, NULL) == want
     assert L.lib().spec_sample_bf16(P_ODD, P, P, NULL, 0, 2, 5, 1000, 1, 0, P, P, NULL, NULL, P,
                                     0, NULL, NULL) == MISALIGNED
 

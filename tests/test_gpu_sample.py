@@ -21,9 +21,10 @@ pytestmark = pytest.mark.gpu
 DEV = "cuda"
 
 
-def _gpu(x, parent, seed, offset):
+def _gpu(x, parent, seed, offset, siblings="first"):
     import long_context_verify_amd as L
-    r = L.spec_sample(x["target"], x["draft"], x["tokens"], parent=parent, seed=seed, offset=offset)
+    r = L.spec_sample(x["target"], x["draft"], x["tokens"], parent=parent, seed=seed, offset=offset,
+                      siblings=siblings)
     torch.cuda.synchronize()
     return {k: v.cpu().numpy() for k, v in r.items()}
 
@@ -123,6 +124,58 @@ def test_sample_full_size_bf16_logits(name):
     g = _gpu(x, parent, seed, 0)
     o = oracle_sample(x["target"], x["draft"], x["tokens"], parent, seed=seed, offset=0)
     _compare(g, o, name)
+
+
+# Lossless sibling rule (spec_sample_ex).  A tree whose rows depend only on depth:
+# the root, three children, two children under each.
+_SIB_PARENT = np.array([-1, 0, 0, 0, 1, 1, 2, 2, 3, 3])
+LOSSLESS_CASES = [
+    # name, B, N, V, parent, dtype
+    ("lossless_tree16_v2048", 48, 16, 2048, "random", torch.float32),
+    ("lossless_siblings_v3001", 64, 10, 3001, "siblings", torch.float32),
+    ("lossless_tree16_bf16_v4096", 32, 16, 4096, "random", torch.bfloat16),
+]
+
+
+@pytest.mark.parametrize("case", LOSSLESS_CASES, ids=[c[0] for c in LOSSLESS_CASES])
+def test_sample_parity_lossless_siblings(case):
+    name, B, N, V, kind, dt = case
+    say(f"sample {name}")
+    parent = (random_tree(N, max_depth=3, max_children=4, seed=17) if kind == "random"
+              else _SIB_PARENT)
+    x = make_sample_inputs(B, N, V, parent, 3.0, draft_noise_std=1.5, seed=sum(map(ord, name)),
+                           device=DEV)
+    x["target"] = x["target"].to(dt)
+    x["draft"] = x["draft"].to(dt)
+    for offset in (0, 5):
+        seed = 0x1055 + offset
+        g = _gpu(x, parent, seed, offset, siblings="lossless")
+        o = oracle_sample(x["target"], x["draft"], x["tokens"], parent, seed=seed, offset=offset,
+                          siblings="lossless")
+        _compare(g, o, f"{name} offset {offset}")
+
+
+def test_sample_lossless_chain_matches_first_rule():
+    say("sample lossless chain = first rule")
+    x = make_sample_inputs(64, 5, 5000, None, 3.0, draft_noise_std=1.0, seed=81, device=DEV)
+    a = _gpu(x, None, 11, 2)
+    b = _gpu(x, None, 11, 2, siblings="lossless")
+    for k in ("out_tokens", "out_count", "out_path"):
+        assert np.array_equal(a[k], b[k]), k
+
+
+def test_sample_full_size_lossless_tree():
+    cfg = CONFIGS["medusa_tree64_8k"]
+    say("sample full-size lossless medusa_tree64_8k")
+    parent = random_tree(cfg.n_nodes)
+    x = make_sample_inputs(cfg.batch, cfg.n_nodes, cfg.vocab, parent, cfg.target_std,
+                           draft_noise_std=cfg.draft_noise_std, draft_std=cfg.draft_std,
+                           seed=cfg.seed, device=DEV)
+    seed = 0x1055 + cfg.seed
+    g = _gpu(x, parent, seed, 0, siblings="lossless")
+    o = oracle_sample(x["target"], x["draft"], x["tokens"], parent, seed=seed, offset=0,
+                      siblings="lossless")
+    _compare(g, o, "medusa_tree64_8k lossless")
 
 
 def test_equal_distributions_accept_all():

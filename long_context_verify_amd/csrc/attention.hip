@@ -509,14 +509,22 @@ __global__ __launch_bounds__(NW * kWave, 8 / NW) void attn_split_mfma(AttnArgs a
 // into a ring of three tiles; one barrier per chunk.  A tile holds
 //   K: 16 operand units of 1 KB in MFMA A-operand order (unit kb*4+s, lane
 //      (h,r) = K[16 kb + r][32 s + 8 h .. +8]) -- read back conflict-free;
-//   V: 64 rows x 256 B, row-major -- each wave reads its 16-byte row pieces
-//      and transposes them in registers as in the streaming kernel.
+//   V: 64 rows x 256 B, 32-byte granules XOR-swizzled by row -- each wave
+//      builds its MFMA operands with gfx950's transposing LDS reads
+//      (ds_read_b64_tr_b16), so no register transpose is needed.
 // A chunk is two 32-key halves; the softmax of a row runs once per chunk over
 // its 16 scores per lane.  The running max is only moved (and O rescaled)
 // when a chunk exceeds it by more than 2^8 (log2 domain); otherwise the
 // exponentials are taken against the old max and stay below 256, which keeps
 // the rescale off the VALU in the common case.
 // ---------------------------------------------------------------------------
+typedef short v4i16 __attribute__((ext_vector_type(4)));
+typedef short v8i16 __attribute__((ext_vector_type(8)));
+
+// XOR applied to the 16-byte piece index of V row `row` in an LDS tile
+// (flips 32-byte granules: granule g of the row is stored at g ^ (row % 8)).
+__device__ __forceinline__ int v_swizzle(int row) { return (row & 7) << 1; }
+
 constexpr int kTreeChunk = 64;        // keys per chunk
 constexpr int kTreeNBuf = 3;          // LDS tiles in the ring
 constexpr float kRescaleTau = 8.0f;   // log2 units
@@ -611,10 +619,14 @@ __global__ __launch_bounds__(WAVES * kWave, 1) void attn_tree_mfma(AttnArgs a) {
         lds_dma16(kc + (size_t)(key - key0) * row_bytes + (32 * s + 8 * h) * 2,
                   tile + unit_id * 1024);
       } else {                // V rows 4 (unit_id - 16) .. +3, 16 lanes per row
-        int key = kbase + 4 * (unit_id - 16) + (lane >> 4);
+        const int vrow = 4 * (unit_id - 16) + (lane >> 4);
+        int key = kbase + vrow;
         key = key < last ? key : last;
-        lds_dma16(vc + (size_t)(key - key0) * row_bytes + (lane & 15) * 16,
-                  tile + unit_id * 1024);
+        // Slot (lane & 15) of the row takes the 16-byte piece whose 32-byte
+        // granule is XOR-swizzled by the row, so transposed reads of 16 rows
+        // spread over all banks.
+        const int piece = (lane & 15) ^ v_swizzle(vrow);
+        lds_dma16(vc + (size_t)(key - key0) * row_bytes + piece * 16, tile + unit_id * 1024);
       }
     }
   };
@@ -718,29 +730,33 @@ __global__ __launch_bounds__(WAVES * kWave, 1) void attn_tree_mfma(AttnArgs a) {
       }
     }
 
+    // O^T += V^T P^T.  The A operand of dim block blk is, in lane (h, r),
+    // V[key(h, t)][16 blk + r] for t = 0..7 (key(h, t) = 16 (t / 4) + 4 h + t % 4
+    // within the half): two transposing LDS reads, each of four keys.  In a
+    // read, lane (h, r) points at 4 dims (16 blk + 4 (r % 4) ..) of key
+    // 4 h + r / 4 (+16 for the second), and the hardware hands lane r the
+    // dim 16 blk + r of all four keys.
 #pragma unroll
     for (int half = 0; half < 2; ++half) {
-      u32x4 vraw[8];
 #pragma unroll
-      for (int t = 0; t < 8; ++t) {
-        const int krow = 32 * half + 16 * (t >> 2) + 4 * h + (t & 3);
-        vraw[t] = *reinterpret_cast<const u32x4*>(tile + 16384 + krow * 256 + r * 16);
-      }
+      for (int blk = 0; blk < 8; ++blk) {
+        v4i16 part[2];
 #pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        u32x4 w;
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const uint32_t lo = vraw[2 * e][j >> 1];
-          const uint32_t hi = vraw[2 * e + 1][j >> 1];
-          // one byte-select per dword: low (even j) or high (odd j) halves of lo, hi
-        w[e] = __builtin_amdgcn_perm(hi, lo, (j & 1) ? 0x07060302u : 0x05040100u);
+        for (int sec = 0; sec < 2; ++sec) {
+          const int vrow = 32 * half + 16 * sec + 4 * h + (r >> 2);
+          const int gp = 2 * blk + ((r & 3) >> 1);          // global 16-byte piece
+          const char* src = tile + 16384 + vrow * 256 + ((gp ^ v_swizzle(vrow)) << 4) +
+                            ((r & 1) << 3);
+          part[sec] = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+              (__attribute__((address_space(3))) v4i16*)(src));
         }
+        const v8i16 w = {part[0][0], part[0][1], part[0][2], part[0][3],
+                         part[1][0], part[1][1], part[1][2], part[1][3]};
         const bf16x8 vop = __builtin_bit_cast(bf16x8, w);
 #pragma unroll
         for (int qb = 0; qb < QB; ++qb)
-          oacc[qb][j] =
-              __builtin_amdgcn_mfma_f32_16x16x32_bf16(vop, pop[qb][half], oacc[qb][j], 0, 0, 0);
+          oacc[qb][blk] =
+              __builtin_amdgcn_mfma_f32_16x16x32_bf16(vop, pop[qb][half], oacc[qb][blk], 0, 0, 0);
       }
     }
   }
@@ -761,16 +777,16 @@ __global__ __launch_bounds__(WAVES * kWave, 1) void attn_tree_mfma(AttnArgs a) {
       const float inv = l > 0.f ? 1.f / l : 0.f;
       __bf16* o = static_cast<__bf16*>(a.out) + (orow0 + row) * D;
 #pragma unroll
-      for (int j = 0; j < 8; ++j)
+      for (int blk = 0; blk < 8; ++blk)
 #pragma unroll
-        for (int e = 0; e < 4; ++e) o[8 * (4 * h + e) + j] = (__bf16)(oacc[qb][j][e] * inv);
+        for (int e = 0; e < 4; ++e) o[16 * blk + 4 * h + e] = (__bf16)(oacc[qb][blk][e] * inv);
       if (h == 0 && a.lse) a.lse[orow0 + row] = l > 0.f ? (m[qb] + __log2f(l)) * kLn2 : -INFINITY;
     } else {
       float* wo = a.ws_o + (part * SR + srow) * D;
 #pragma unroll
-      for (int j = 0; j < 8; ++j)
+      for (int blk = 0; blk < 8; ++blk)
 #pragma unroll
-        for (int e = 0; e < 4; ++e) wo[8 * (4 * h + e) + j] = oacc[qb][j][e];
+        for (int e = 0; e < 4; ++e) wo[16 * blk + 4 * h + e] = oacc[qb][blk][e];
       if (h == 0) {
         float* wml = a.ws_ml + (part * SR + srow) * 2;
         wml[0] = m[qb];

@@ -507,8 +507,9 @@ __global__ __launch_bounds__(NW * kWave, 8 / NW) void attn_split_mfma(AttnArgs a
 // HBM -> LDS with direct-to-LDS loads (global_load_lds_dwordx4: lane l's 16
 // bytes land at base + 16 l), two chunks ahead of the one being computed,
 // into a ring of three tiles; one barrier per chunk.  A tile holds
-//   K: 16 operand units of 1 KB in MFMA A-operand order (unit kb*4+s, lane
-//      (h,r) = K[16 kb + r][32 s + 8 h .. +8]) -- read back conflict-free;
+//   K: 64 rows x 256 B, 16-byte pieces XOR-swizzled by row (loaded as 1 KB
+//      contiguous runs; the A operand of lane (h,r), K[16 kb + r][32 s + 8 h
+//      .. +8], is one conflict-free 16-byte read);
 //   V: 64 rows x 256 B, 32-byte granules XOR-swizzled by row -- each wave
 //      builds its MFMA operands with gfx950's transposing LDS reads
 //      (ds_read_b64_tr_b16), so no register transpose is needed.
@@ -524,6 +525,8 @@ typedef short v8i16 __attribute__((ext_vector_type(8)));
 // XOR applied to the 16-byte piece index of V row `row` in an LDS tile
 // (flips 32-byte granules: granule g of the row is stored at g ^ (row % 8)).
 __device__ __forceinline__ int v_swizzle(int row) { return (row & 7) << 1; }
+// XOR applied to the 16-byte piece index of K row `row` in an LDS tile.
+__device__ __forceinline__ int k_swizzle(int row) { return row & 15; }
 
 constexpr int kTreeChunk = 64;        // keys per chunk
 constexpr int kTreeNBuf = 3;          // LDS tiles in the ring
@@ -612,12 +615,14 @@ __global__ __launch_bounds__(WAVES * kWave, 1) void attn_tree_mfma(AttnArgs a) {
 #pragma unroll
     for (int i = 0; i < UPW; ++i) {
       const int unit_id = wave * UPW + i;
-      if (unit_id < 16) {     // K operand unit (kb, s)
-        const int kb = unit_id >> 2, s = unit_id & 3;
-        int key = kbase + 16 * kb + r;
+      if (unit_id < 16) {     // K rows 4 unit_id .. +3: 1 KB contiguous per instruction
+        const int krow = 4 * unit_id + (lane >> 4);
+        int key = kbase + krow;
         key = key < last ? key : last;
-        lds_dma16(kc + (size_t)(key - key0) * row_bytes + (32 * s + 8 * h) * 2,
-                  tile + unit_id * 1024);
+        // Slot (lane & 15) of the row takes the 16-byte piece (lane & 15) ^ (row % 16),
+        // so the operand reads below (16 rows, same column) hit distinct banks.
+        const int piece = (lane & 15) ^ k_swizzle(krow);
+        lds_dma16(kc + (size_t)(key - key0) * row_bytes + piece * 16, tile + unit_id * 1024);
       } else {                // V rows 4 (unit_id - 16) .. +3, 16 lanes per row
         const int vrow = 4 * (unit_id - 16) + (lane >> 4);
         int key = kbase + vrow;
@@ -666,7 +671,7 @@ __global__ __launch_bounds__(WAVES * kWave, 1) void attn_tree_mfma(AttnArgs a) {
 #pragma unroll
         for (int s = 0; s < DS; ++s)
           kop[kk][s] = *reinterpret_cast<const bf16x8*>(
-              tile + ((2 * half + kk) * 4 + s) * 1024 + lane * 16);
+              tile + (32 * half + 16 * kk + r) * 256 + (((4 * s + h) ^ k_swizzle(r)) << 4));
 #pragma unroll
       for (int qb = 0; qb < QB; ++qb) {
         f32x4 acc0 = {0.f, 0.f, 0.f, 0.f}, acc1 = acc0;

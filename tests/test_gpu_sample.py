@@ -134,6 +134,9 @@ LOSSLESS_CASES = [
     ("lossless_tree16_v2048", 48, 16, 2048, "random", torch.float32),
     ("lossless_siblings_v3001", 64, 10, 3001, "siblings", torch.float32),
     ("lossless_tree16_bf16_v4096", 32, 16, 4096, "random", torch.bfloat16),
+    # vocabularies past the register cache: the streamed residual passes
+    ("lossless_siblings_v40000", 16, 10, 40000, "siblings", torch.float32),
+    ("lossless_siblings_bf16_v40001", 16, 10, 40001, "siblings", torch.bfloat16),
 ]
 
 
@@ -153,6 +156,27 @@ def test_sample_parity_lossless_siblings(case):
         o = oracle_sample(x["target"], x["draft"], x["tokens"], parent, seed=seed, offset=offset,
                           siblings="lossless")
         _compare(g, o, f"{name} offset {offset}")
+
+
+def test_sample_lossless_per_sequence_trees():
+    """A different tree per sequence (parent [B, N])."""
+    say("sample lossless per-sequence trees")
+    B, N, V = 12, 14, 3000
+    parents = np.stack([random_tree(N, max_depth=3, max_children=4, seed=100 + b) for b in range(B)])
+    x = make_sample_inputs(B, N, V, parents[0], 3.0, draft_noise_std=1.5, seed=91, device=DEV)
+    # Redraw the tokens of every sequence from its own tree's parents.
+    g = torch.Generator().manual_seed(92)
+    d = x["draft"].cpu().double()
+    for b in range(B):
+        for c in range(1, N):
+            gum = -torch.log(-torch.log(torch.rand(V, generator=g, dtype=torch.float64)
+                                        .clamp_(min=1e-300)))
+            x["tokens"][b, c] = int(torch.argmax(d[b, int(parents[b, c])] + gum))
+    for rule in ("first", "lossless"):
+        gg = _gpu(x, parents, 77, 4, siblings=rule)
+        o = oracle_sample(x["target"], x["draft"], x["tokens"], parents, seed=77, offset=4,
+                          siblings=rule)
+        _compare(gg, o, f"per-sequence trees {rule}")
 
 
 def test_sample_lossless_chain_matches_first_rule():

@@ -889,26 +889,28 @@ hipError_t launch_sample(const SampleArgs& a, hipStream_t stream) {
 // implementation: softmax of the draft logits, then one multinomial draw).
 // An exponential race over softmax(l): id x scores p_x / E_x with
 // E_x = -ln U_x, the largest score wins (ties: lowest id).  In log2 units the
-// score is l_x log2(e) - log2(-log2 U_x) plus a constant, so the race needs
-// neither the row max nor the normaliser; those are still gathered (per
-// chunk: max and sum of exp2) for the drawn token's log-probability.
+// score ln p_x - ln E_x is l_x - ln(-ln U_x) plus a constant, so the race
+// needs neither the row max nor the normaliser; it is evaluated in fp64, the
+// precision the reference draw decides in.  Max and normaliser are still
+// gathered (per chunk: max and sum of exp2) for the drawn token's
+// log-probability.
 // ---------------------------------------------------------------------------
 // Arg-max of (score, id) with ties to the lowest id, carrying the winner's
 // scaled logit along.
 struct RaceBest {
-  float s;
+  double s;
   int i;
   float x;
 };
 
-__device__ __forceinline__ void better_f(RaceBest& r, float s2, int i2, float x2) {
+__device__ __forceinline__ void better_f(RaceBest& r, double s2, int i2, float x2) {
   if (s2 > r.s || (s2 == r.s && i2 < r.i)) r = RaceBest{s2, i2, x2};
 }
 
 __device__ __forceinline__ void block_argmax_f(RaceBest& r, RaceBest* red) {
 #pragma unroll
   for (int off = 32; off >= 1; off >>= 1) {
-    const float s2 = __shfl_xor(r.s, off);
+    const double s2 = __shfl_xor(r.s, off);
     const int i2 = __shfl_xor(r.i, off);
     const float x2 = __shfl_xor(r.x, off);
     better_f(r, s2, i2, x2);
@@ -935,7 +937,7 @@ __global__ __launch_bounds__(kSampleThreads) void draft_partial(DraftArgs a) {
   const T* row = static_cast<const T*>(a.logits) + (size_t)b * a.row_stride;
   constexpr int GROUPS = kDraftChunk / 4 / kSampleThreads;  // 2
   const int g0 = chunk * (kDraftChunk / 4) + threadIdx.x;
-  float x[4 * GROUPS];
+  float x[4 * GROUPS], lraw[4 * GROUPS];   // logit * log2(e), and the logit
 #pragma unroll
   for (int i = 0; i < GROUPS; ++i) {
     const int e = 4 * (g0 + kSampleThreads * i);
@@ -943,18 +945,24 @@ __global__ __launch_bounds__(kSampleThreads) void draft_partial(DraftArgs a) {
       f32x4 v = {-INFINITY, -INFINITY, -INFINITY, -INFINITY};
       if (e < a.V) v = ld4(row, e);
 #pragma unroll
-      for (int k = 0; k < 4; ++k) x[4 * i + k] = v[k] * kLog2e;
+      for (int k = 0; k < 4; ++k) lraw[4 * i + k] = v[k];
     } else {
 #pragma unroll
-      for (int k = 0; k < 4; ++k) x[4 * i + k] = e + k < a.V ? ld1(row, e + k) * kLog2e : -INFINITY;
+      for (int k = 0; k < 4; ++k) lraw[4 * i + k] = e + k < a.V ? ld1(row, e + k) : -INFINITY;
     }
+#pragma unroll
+    for (int k = 0; k < 4; ++k) x[4 * i + k] = lraw[4 * i + k] * kLog2e;
   }
-  // Race: one Philox block per group of four ids.
-  RaceBest best{-INFINITY, 0x7fffffff, -INFINITY};
+  // Race: one Philox block per group of four ids.  The fp32 score of every
+  // id picks each thread's candidates cheaply; only ids within delta of the
+  // thread's fp32 best get the fp64 score that decides (delta is far above
+  // the fp32 error, so no id left out could win in fp64).
+  float s32[4 * GROUPS];
+  uint32_t word[4 * GROUPS];
+  float m32 = -INFINITY;
 #pragma unroll
   for (int i = 0; i < GROUPS; ++i) {
     const int g = g0 + kSampleThreads * i;
-    if (4 * g >= a.V) break;
     uint32_t c0 = (uint32_t)g, c1 = (uint32_t)a.node, c2 = (uint32_t)b, c3 = a.ctr3;
     philox4x32_10(c0, c1, c2, c3, a.key0, a.key1);
     const uint32_t w[4] = {c0, c1, c2, c3};
@@ -962,8 +970,36 @@ __global__ __launch_bounds__(kSampleThreads) void draft_partial(DraftArgs a) {
     for (int k = 0; k < 4; ++k) {
       // (2 (w >> 9) + 1) 2^-24 is exact in fp32 and lies in (0, 1).
       const float u = (float)(2u * (w[k] >> 9) + 1u) * 5.9604644775390625e-08f;
-      const float s = x[4 * i + k] - __builtin_amdgcn_logf(-__builtin_amdgcn_logf(u));
-      better_f(best, s, 4 * g + k, x[4 * i + k]);   // ids past V carry x = -inf: never beat a real id
+      const float e = -__builtin_amdgcn_logf(u) * 0.6931471805599453f;   // -ln U
+      word[4 * i + k] = w[k];
+      s32[4 * i + k] = lraw[4 * i + k] - __builtin_amdgcn_logf(e) * 0.6931471805599453f;
+      m32 = fmaxf(m32, s32[4 * i + k]);   // ids past V carry -inf
+    }
+  }
+  const float delta = 1e-3f + 1e-6f * fabsf(m32);
+  // Candidate mask; the fp64 scores are taken one candidate per lane per
+  // round (ids in increasing order), so the wave runs as many rounds as its
+  // busiest lane has candidates -- almost always one.
+  uint32_t cand = 0;
+#pragma unroll
+  for (int j = 0; j < 4 * GROUPS; ++j)
+    if (s32[j] != -INFINITY && s32[j] >= m32 - delta) cand |= 1u << j;
+  RaceBest best{-INFINITY, 0x7fffffff, -INFINITY};
+  while (__any(cand != 0)) {
+    if (cand) {
+      const int j = __builtin_ctz(cand);
+      cand &= cand - 1;
+      float l = 0.f, xs = 0.f;
+      uint32_t wj = 0;
+#pragma unroll
+      for (int q = 0; q < 4 * GROUPS; ++q)
+        if (q == j) {
+          l = lraw[q];
+          xs = x[q];
+          wj = word[q];
+        }
+      const double sc = (double)l - log(-log(uniform24(wj)));
+      better_f(best, sc, 4 * (g0 + kSampleThreads * (j >> 2)) + (j & 3), xs);
     }
   }
   block_argmax_f(best, redr);
@@ -1030,7 +1066,7 @@ DraftPlan plan_draft(int32_t B, int32_t V) {
   p.n_chunks = (V + kDraftChunk - 1) / kDraftChunk;
   const size_t n = (size_t)B * p.n_chunks;
   p.off_best = 0;
-  p.off_idx = align256(p.off_best + n * sizeof(float));
+  p.off_idx = align256(p.off_best + n * sizeof(double));
   p.off_x = align256(p.off_idx + n * sizeof(int32_t));
   p.off_m = align256(p.off_x + n * sizeof(float));
   p.off_s = align256(p.off_m + n * sizeof(float));

@@ -135,7 +135,7 @@ struct DraftArgs {
   int32_t* out_token;       // out_token[b * token_stride]
   int32_t token_stride;
   float* out_logprob;       // nullable, [B]
-  float* part_best;         // [B][n_chunks] best race score (log2 units)
+  double* part_best;        // [B][n_chunks] best race score (natural log units)
   int32_t* part_idx;        // [B][n_chunks] its id
   float* part_x;            // [B][n_chunks] its logit * log2(e)
   float* part_m;            // [B][n_chunks] max of logit * log2(e)

@@ -26,7 +26,7 @@ import numpy as np
 from .sample import softmax, uniforms
 
 STREAM_DRAFT = 1
-DRAFT_MARGIN = 1e-5   # best/second race score at or below 1 + this is a near-tie
+DRAFT_MARGIN = 1e-9   # best/second race score at or below 1 + this is a near-tie
 
 
 def draft_sample(logits, seed: int, offset: int, node: int):

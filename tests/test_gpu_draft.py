@@ -1,8 +1,10 @@
 """GPU parity of spec_draft_sample against the fp64 oracle.
 
 Bar: with the same Philox uniforms the drawn ids are bit-exact, except in
-rows where the oracle's two best race scores are within a factor 1 + 1e-5
-(a floating-point near-tie; at most 1% of rows).  The log-probability of the
+rows where the oracle's two best race scores are within a factor 1 + 1e-9
+(a floating-point near-tie; at most 1% of rows).  Both sides decide in fp64:
+the kernel scores l - ln(-ln U), the oracle p / E; the two differ by about
+1e-14 in the score.  The log-probability of the
 drawn id matches to 2e-5 absolute: the kernel rounds l * log2(e) to fp32
 (relative 6e-8, so about 1.2e-6 at |l| = 20) and sums at most 8 exponentials
 per thread in fp32 (relative 2e-6) before the fp64 combine.

@@ -98,3 +98,42 @@ def test_window_bad_total_len_flags_error():
     torch.cuda.synchronize()
     assert int(err.item()) & 0x4
     assert torch.all(out[1] == 0)
+
+
+@pytest.mark.parametrize("dt,tol", [("f32", 1e-6), ("bf16", 8e-3)])
+def test_window_full_ring_rotation_invariance(dt, tol):
+    """With a full ring every slot is attended, so rotating the slots (a permutation
+    of the keys) leaves the output unchanged up to summation order."""
+    import long_context_verify_amd as L
+    say(f"window ring rotation {dt}")
+    B, Hq, Hkv, D, W, S = 3, 16, 4, 128, 96, 4
+    x = make_window_inputs(B, Hq, Hkv, D, W, S, [S + W + 7, 1000, 5 * W], dtype=dt, seed=21,
+                           device=DEV)
+    out, lse = L.window_attention(x["q"], x["k_ring"], x["v_ring"], x["k_sink"], x["v_sink"],
+                                  x["total_len"])
+    kr = torch.roll(x["k_ring"], shifts=37, dims=2).contiguous()
+    vr = torch.roll(x["v_ring"], shifts=37, dims=2).contiguous()
+    out2, lse2 = L.window_attention(x["q"], kr, vr, x["k_sink"], x["v_sink"], x["total_len"])
+    torch.cuda.synchronize()
+    assert (out.float() - out2.float()).abs().max().item() <= tol
+    assert (lse - lse2).abs().max().item() <= 1e-5
+
+
+def test_window_constant_keys_count_the_attended_tokens():
+    """Equal keys: lse - score = ln(min(S, T) + min(W, T - S)) on the GPU too."""
+    import long_context_verify_amd as L
+    say("window constant keys")
+    W, S, D = 64, 4, 128
+    Ts = [1, 3, 4, 5, 40, 68, 69, 500]
+    B = len(Ts)
+    x = make_window_inputs(B, 8, 2, D, W, S, Ts, dtype="f32", seed=5, device=DEV)
+    x["k_ring"][:] = 0.125
+    x["k_sink"][:] = 0.125
+    _, lse = L.window_attention(x["q"], x["k_ring"], x["v_ring"], x["k_sink"], x["v_sink"],
+                                x["total_len"])
+    torch.cuda.synchronize()
+    s = (x["q"][:, :, 0].double() * 0.125).sum(-1) / np.sqrt(D)
+    counts = torch.tensor([min(S, T) + min(W, max(T - S, 0)) for T in Ts], dtype=torch.float64,
+                          device=DEV)
+    err = (lse[:, :, 0].double() - s - torch.log(counts)[:, None]).abs().max().item()
+    assert err <= 1e-5

@@ -233,3 +233,18 @@ def test_paged_equals_contiguous(P, tree):
     for b in range(B):
         need = (kv[b] + P - 1) // P
         assert (bt[b, :need] >= 0).all() and (bt[b, need:] == -1).all()
+
+
+@pytest.mark.parametrize("T", [1, 3, 4, 5, 20, 36, 37, 100])
+def test_window_constant_keys_count_the_attended_tokens(T):
+    """Equal keys: lse - score = ln(min(S, T) + min(W, T - S))."""
+    W, S, D = 32, 4, 8
+    x = make_window_inputs(1, 2, 1, D, W, S, [T], dtype="f32", seed=T)
+    kconst = torch.full((D,), 0.25)
+    for name in ("hist_sink_k", "hist_recent_k"):
+        x[name][:] = kconst
+    _, lse = window_attention(x["q"], x["hist_sink_k"], x["hist_sink_v"], x["hist_recent_k"],
+                              x["hist_recent_v"], x["total_len"], W, S)
+    s = (x["q"][0, :, 0].double() @ kconst.double()).numpy() / np.sqrt(D)
+    count = min(S, T) + min(W, max(T - S, 0))
+    np.testing.assert_allclose(lse[0, :, 0] - s, np.log(count), rtol=0, atol=1e-12)

@@ -35,6 +35,7 @@ import time
 import numpy as np
 
 HBM_PEAK_GBPS = 8000.0      # MI355X HBM3E, vendor figure
+MFMA_BF16_PEAK_TFLOPS = 2500.0   # MI355X dense bf16 matrix rate, vendor figure
 METRIC = "verify-attn KV GB/s (% HBM peak) + verified draft tokens/sec, 1 MI355X"
 
 
@@ -433,6 +434,14 @@ def main():
         },
         "ops": ops_report,
     }
+    if cfg.tree:
+        # Wide query blocks sit near the MFMA ridge: co-report the dense bf16
+        # rate of the same call (Q K^T and P V, 2 flop per multiply-add).
+        flops = 4.0 * B * Hq * nq * Lk * D
+        tflops = flops / (op_us["verify_attn"] * 1e-6) / 1e12
+        res["roofline_mfma"] = {"kernel": "spec_verify_attention", "bound": "mfma",
+                                "achieved": tflops, "peak": MFMA_BF16_PEAK_TFLOPS,
+                                "unit": "TFLOP/s", "frac": tflops / MFMA_BF16_PEAK_TFLOPS}
     if args.cpu_budget > 0:
         log("[bench] timing the oracle on a bounded sample (CPU)")
         res["cpu_baseline"] = cpu_baseline(cfg, att, parent, win, smp, args.cpu_budget)

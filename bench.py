@@ -18,10 +18,13 @@ is verified draft tokens per second (batch * gamma per step).  Per-op times
 come from HIP events recorded on the stream the library launches on (torch's
 current stream); besides the three step ops they cover the calls on either
 side of the step, spec_draft_sample (one draft-step draw) and spec_kv_commit
-(keeping the accepted path), which are not part of the step.  The oracle (fp64 numpy) is timed on a bounded sample of the
-same workload on the host cores and reported as ``cpu_baseline``.
+(keeping the accepted path), which are not part of the step.  The oracle
+(fp64 numpy) is timed on a bounded sample of the same workload on the host
+cores and reported as ``cpu_baseline``.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
+                       [--page-size P] [--logits f32|bf16] [--siblings first|lossless]
+                       [--cpu-budget SECONDS] [--copy-probe-mib MIB]
 """
 
 from __future__ import annotations

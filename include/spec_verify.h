@@ -26,6 +26,13 @@
  *   Pointers    Device pointers unless marked "host".  Tensor pointers must
  *               be 16-byte aligned; workspaces 256-byte aligned.  All tensors
  *               are dense, row-major, in the layouts given per argument.
+ *   Workspace   Scratch the caller owns, sized by the matching *_workspace
+ *               function.  Zero-fill it once before its first use: the
+ *               attention calls keep split-arrival counters in it, and every
+ *               call leaves them at zero again, so the same workspace serves
+ *               any later call (of any entry point) ordered after it on the
+ *               device.  Calls that overlap in time need workspaces of their
+ *               own.  Counters found non-zero set SPEC_DEVERR_WORKSPACE.
  *   Streams     All work is enqueued on `stream` (0 = the null stream); no
  *               call synchronises the host.  Outputs are valid once the
  *               stream reaches the end of the call.
@@ -77,6 +84,7 @@ typedef enum {
 #define SPEC_DEVERR_PATH 0x10     /* commit: count or path entries not a valid accepted path */
 #define SPEC_DEVERR_LOGITS 0x20   /* draft draw: a row with no finite logit */
 #define SPEC_DEVERR_PAGE 0x40     /* paged verify: a block_table entry outside [0, num_pages) */
+#define SPEC_DEVERR_WORKSPACE 0x80 /* a workspace whose arrival counters were not zero-filled */
 
 /* Largest supported query block (one 64-bit ancestor mask per node). */
 #define SPEC_MAX_NQ 64
@@ -114,7 +122,8 @@ typedef enum {
  *   n_q      1 .. SPEC_MAX_NQ;  D in {64, 128};  Hq % Hkv == 0;  L_cap >= n_q.
  *   scale    softmax scale; <= 0 selects 1/sqrt(D).
  *   num_splits  key-range splits per (sequence, kv head); 0 = automatic.
- *   workspace   at least spec_verify_attention_workspace(...) bytes.
+ *   workspace   at least spec_verify_attention_workspace(...) bytes,
+ *               zero-filled before its first use (see Workspace above).
  * Returns SPEC_OK or an error status (nothing launched on error).
  */
 spec_status_t spec_verify_attention(const void* q, const void* k_cache, const void* v_cache,

@@ -115,11 +115,13 @@ def _need_gpu(*ts, strided_ok=()):
 
 
 def _workspace(nbytes: int, device, workspace: Optional[torch.Tensor]):
+    """A caller's workspace (zero-filled before its first use, then reusable
+    by any later call on the same stream), or a fresh zero-filled one."""
     if workspace is not None:
         if workspace.numel() * workspace.element_size() < nbytes:
             raise ValueError("workspace too small")
         return workspace
-    return torch.empty(max(int(nbytes), 256), dtype=torch.uint8, device=device)
+    return torch.zeros(max(int(nbytes), 256), dtype=torch.uint8, device=device)
 
 
 def _parent_arg(parent, B, n, device):

@@ -123,6 +123,16 @@ spec_status_t paging_check(const Paging& pg, int32_t L_max, const int32_t* kv_le
   return SPEC_OK;
 }
 
+// Workspace layout of an attention call: split-arrival counters (used when
+// the plan merges the splits in the last work-group of each unit), then the
+// O and (max, sum) partials.
+void set_workspace(AttnArgs& a, const AttnPlan& p, void* workspace) {
+  char* w = static_cast<char*>(workspace);
+  a.arrive = p.fuse_merge ? reinterpret_cast<uint32_t*>(w) : nullptr;
+  a.ws_o = reinterpret_cast<float*>(w + p.ws_sync_bytes);
+  a.ws_ml = reinterpret_cast<float*>(w + p.ws_sync_bytes + p.ws_o_bytes);
+}
+
 spec_status_t verify_call(const void* q, const void* k_cache, const void* v_cache, void* out,
                           float* lse, const int32_t* kv_len, const int32_t* parent,
                           int32_t parent_batch_stride, int32_t B, int32_t Hq, int32_t Hkv,
@@ -157,8 +167,7 @@ spec_status_t verify_call(const void* q, const void* k_cache, const void* v_cach
     a.page_shift = log2_exact(pg.page_size);
     a.num_pages = pg.num_pages;
   }
-  a.ws_o = static_cast<float*>(workspace);
-  a.ws_ml = reinterpret_cast<float*>(static_cast<char*>(workspace) + p.ws_o_bytes);
+  set_workspace(a, p, workspace);
   a.B = B;
   a.Hq = Hq;
   a.Hkv = Hkv;
@@ -258,8 +267,7 @@ spec_status_t spec_window_attention(const void* q, void* k_ring, void* v_ring, v
   a.k_sink_w = k_sink;
   a.v_sink_w = v_sink;
   a.lens = total_len;
-  a.ws_o = static_cast<float*>(workspace);
-  a.ws_ml = reinterpret_cast<float*>(static_cast<char*>(workspace) + p.ws_o_bytes);
+  set_workspace(a, p, workspace);
   a.B = B;
   a.Hq = Hq;
   a.Hkv = Hkv;

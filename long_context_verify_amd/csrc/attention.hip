@@ -24,11 +24,13 @@
 //     an ancestor of the query's node (a 64-bit mask built from the parent
 //     array);
 //   * the four waves merge through LDS once at the end; the split partials
-//     (unnormalised O, running max, sum) go to the workspace and a second
-//     kernel combines them in a fixed order.
+//     (unnormalised O, running max, sum) go to the workspace and are combined
+//     in a fixed order: by a second kernel for the verify block, and for the
+//     short draft window by the work-group that completes a unit's last split
+//     (an arrival counter per unit in the workspace).
 //
 // The fp32 path is a plain VALU kernel (one wave per query row, lanes over
-// the head dimension) with the same partial format.
+// the head dimension) with the same partial format, merged by the second kernel.
 
 #include <hip/hip_runtime.h>
 
@@ -227,6 +229,42 @@ __device__ __forceinline__ void window_append(const AttnArgs& a, const UnitGeom&
 }
 
 // ---------------------------------------------------------------------------
+// Split merge, separate kernel: output row `row` (0 .. M-1) of a
+// unit, head-dim entries d0 .. d0+3.  Splits are combined in a fixed order,
+// so the result is deterministic.
+// ---------------------------------------------------------------------------
+template <int D, typename OutT>
+__device__ __forceinline__ void merge_item(const MergeArgs& a, int unit, int row, int d0) {
+  const int qs = row / a.slice_rows;
+  const int rr = row - qs * a.slice_rows;
+  const size_t part0 = ((size_t)unit * a.n_qs + qs) * a.n_splits;
+  const size_t pstride = (size_t)a.slice_rows;   // rows between consecutive splits
+
+  // Every split's loads are independent, so they are all in flight together.
+  const float* ml = a.ws_ml + (part0 * a.slice_rows + rr) * 2;
+  const float* src = a.ws_o + (part0 * a.slice_rows + rr) * D + d0;
+  float mx = -INFINITY, l = 0.f;
+  f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll 8
+  for (int s = 0; s < a.n_splits; ++s) {
+    const float ms = ml[s * pstride * 2];
+    const float ls = ml[s * pstride * 2 + 1];
+    const f32x4 v = *reinterpret_cast<const f32x4*>(src + s * pstride * D);
+    float s_old, s_new;
+    merge_scales(mx, ms, s_old, s_new);
+    acc = acc * s_old + v * s_new;
+    l = l * s_old + ls * s_new;
+  }
+  const float inv = l > 0.f ? 1.f / l : 0.f;
+  const int b = unit / a.Hkv, hk = unit - b * a.Hkv;
+  const size_t orow = (size_t)(b * a.Hq + hk * a.g) * a.n_q + row;
+  OutT* out = static_cast<OutT*>(a.out) + orow * D + d0;
+#pragma unroll
+  for (int e = 0; e < 4; ++e) out[e] = (OutT)(acc[e] * inv);
+  if (a.lse && d0 == 0) a.lse[orow] = l > 0.f ? (mx + __log2f(l)) * kLn2 : -INFINITY;
+}
+
+// ---------------------------------------------------------------------------
 // bf16 MFMA split kernel.  QB = MFMA query blocks (16 rows each) per slice.
 // ---------------------------------------------------------------------------
 template <int D, int QB, bool WINDOW, int NW = kWaves, bool PAGED = false>
@@ -250,48 +288,9 @@ __global__ __launch_bounds__(NW * kWave, 8 / NW) void attn_split_mfma(AttnArgs a
   const UnitGeom u = unit_geom<WINDOW>(a, unit, split == 0 && qs == 0 && threadIdx.x == 0);
   window_append<WINDOW>(a, u, split, qs, row_bytes);
 
-  // Query operands (B side of S^T = K Q^T): lane holds Q[row][32 s + 8 h .. +8].
-  // They are loop-invariant; wave 0 stages them in LDS in operand order and
-  // every wave re-reads them per chunk (conflict-free 16-byte reads), which
-  // keeps 32 VGPRs free for the in-flight K/V of the next chunk.
-  const char* qbase = static_cast<const char*>(a.q) +
-                      ((size_t)(u.b * a.Hq + u.hk * a.g) * a.n_q) * row_bytes;
-  uint64_t anc[QB];
-#pragma unroll
-  for (int qb = 0; qb < QB; ++qb) {
-    const int row = qs * SR + qb * 16 + r;
-    const bool live = row < a.M;
-    if (wave == 0) {
-#pragma unroll
-      for (int s = 0; s < DS; ++s)
-        lds_q[qb][s][lane] = live ? *reinterpret_cast<const bf16x8*>(
-                                        qbase + (size_t)row * row_bytes + (32 * s + 8 * h) * 2)
-                                  : bf16x8{};
-    }
-    anc[qb] = (!WINDOW && live) ? ancestor_mask(a, u.b, row % a.n_q) : 1ull;
-  }
-
   int c0, c1;
   chunk_range(u.n_keys, split, a.n_splits, c0, c1);
   int pfirst = 0;
-  if constexpr (PAGED) {
-    // The page-table staging doubles as the barrier after the Q staging.
-    if (!stage_pages<PAGED>(a, u, c0 * kChunk, min(c1 * kChunk, u.n_keys), lds_pages, pfirst))
-      c1 = c0;
-  } else {
-    __syncthreads();
-  }
-
-  float m[QB], lsum[QB];
-  f32x4 oacc[QB][8];
-#pragma unroll
-  for (int qb = 0; qb < QB; ++qb) {
-    m[qb] = -INFINITY;
-    lsum[qb] = 0.f;
-#pragma unroll
-    for (int j = 0; j < 8; ++j) oacc[qb][j] = f32x4{0.f, 0.f, 0.f, 0.f};
-  }
-
   const int last = u.n_keys - 1;
   // K operands (A side): lane holds K[kbase + 16 kb + r][32 s + 8 h .. +8].
   auto row_of = [&](int key, int kv, int kbase) -> const char* {
@@ -330,13 +329,61 @@ __global__ __launch_bounds__(NW * kWave, 8 / NW) void attn_split_mfma(AttnArgs a
     }
   };
 
+  bf16x8 kop[2][DS];
+  u32x4 vraw[8];
+  // The window's waves take one chunk or two: their first K/V loads go out
+  // before the Q staging and its barrier, so the two latencies overlap.
+  if constexpr (WINDOW) {
+    if (c0 + wave < c1) {
+      load_k((c0 + wave) * kChunk, kop);
+      load_v((c0 + wave) * kChunk, vraw);
+    }
+  }
+
+  // Query operands (B side of S^T = K Q^T): lane holds Q[row][32 s + 8 h .. +8].
+  // They are loop-invariant; wave 0 stages them in LDS in operand order and
+  // every wave re-reads them per chunk (conflict-free 16-byte reads), which
+  // keeps 32 VGPRs free for the in-flight K/V of the next chunk.
+  const char* qbase = static_cast<const char*>(a.q) +
+                      ((size_t)(u.b * a.Hq + u.hk * a.g) * a.n_q) * row_bytes;
+  uint64_t anc[QB];
+#pragma unroll
+  for (int qb = 0; qb < QB; ++qb) {
+    const int row = qs * SR + qb * 16 + r;
+    const bool live = row < a.M;
+    if (wave == 0) {
+#pragma unroll
+      for (int s = 0; s < DS; ++s)
+        lds_q[qb][s][lane] = live ? *reinterpret_cast<const bf16x8*>(
+                                        qbase + (size_t)row * row_bytes + (32 * s + 8 * h) * 2)
+                                  : bf16x8{};
+    }
+    anc[qb] = (!WINDOW && live) ? ancestor_mask(a, u.b, row % a.n_q) : 1ull;
+  }
+
+  if constexpr (PAGED) {
+    // The page-table staging doubles as the barrier after the Q staging.
+    if (!stage_pages<PAGED>(a, u, c0 * kChunk, min(c1 * kChunk, u.n_keys), lds_pages, pfirst))
+      c1 = c0;
+  } else {
+    __syncthreads();
+  }
+
+  float m[QB], lsum[QB];
+  f32x4 oacc[QB][8];
+#pragma unroll
+  for (int qb = 0; qb < QB; ++qb) {
+    m[qb] = -INFINITY;
+    lsum[qb] = 0.f;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) oacc[qb][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+  }
+
   // Software pipeline: the loads of the wave's next chunk are issued as soon
   // as the current chunk has consumed the registers they land in (K after the
   // S^T products, V after its transpose), so HBM traffic stays in flight
   // while the wave computes.  The prefetch is never behind a branch, which
   // keeps the compiler's wait counts exact.
-  bf16x8 kop[2][DS];
-  u32x4 vraw[8];
   auto chunk_step = [&](auto prefetch, int kbase, int nbase) {
     constexpr bool kPrefetch = decltype(prefetch)::value;
 
@@ -426,8 +473,10 @@ __global__ __launch_bounds__(NW * kWave, 8 / NW) void attn_split_mfma(AttnArgs a
 
   int c = c0 + wave;
   if (c < c1) {
-    load_k(c * kChunk, kop);
-    load_v(c * kChunk, vraw);
+    if constexpr (!WINDOW) {
+      load_k(c * kChunk, kop);
+      load_v(c * kChunk, vraw);
+    }
     if constexpr (WINDOW) {
       // A few chunks per wave: peel the last one so nothing is read twice.
       for (; c + NW < c1; c += NW)
@@ -460,39 +509,148 @@ __global__ __launch_bounds__(NW * kWave, 8 / NW) void attn_split_mfma(AttnArgs a
   }
   __syncthreads();
 
-  // Merge the four waves.  With a single split per unit this is the final
-  // result (normalised and stored straight to the output); otherwise the
-  // work-group partial goes to the workspace for the split merge.
+  // Merge the waves.  With a single split per unit this is the final result
+  // (normalised and stored straight to the output); otherwise the work-group
+  // partial goes to the workspace for the split merge, which the window
+  // kernel runs in the work-group that completes the unit's last split and
+  // the verify kernel leaves to a second kernel.
   const size_t part = ((size_t)unit * a.n_qs + qs) * a.n_splits + split;
   float* wo = a.ws_o + part * SR * D;
   float* wml = a.ws_ml + part * SR * 2;
   const bool direct = a.n_splits == 1;
   const size_t orow0 = (size_t)(u.b * a.Hq + u.hk * a.g) * a.n_q + (size_t)qs * SR;
-  for (int idx = threadIdx.x; idx < SR * D; idx += NW * kWave) {
-    const int row = idx / D, d = idx - row * D;
+  if constexpr (!WINDOW) {
+    for (int idx = threadIdx.x; idx < SR * D; idx += NW * kWave) {
+      const int row = idx / D, d = idx - row * D;
+      float mx = -INFINITY;
+#pragma unroll
+      for (int w = 0; w < NW; ++w) mx = fmaxf(mx, lds_ml[w][row][0]);
+      const float mu = (mx == -INFINITY) ? 0.f : mx;
+      float o = 0.f, l = 0.f;
+#pragma unroll
+      for (int w = 0; w < NW; ++w) {
+        const float sc = fast_exp2(lds_ml[w][row][0] - mu);
+        o += sc * lds_o[w][row][d];
+        l += sc * lds_ml[w][row][1];
+      }
+      if (direct) {
+        if (qs * SR + row < a.M) {
+          static_cast<__bf16*>(a.out)[(orow0 + row) * D + d] = (__bf16)(l > 0.f ? o / l : 0.f);
+          if (d == 0 && a.lse)
+            a.lse[orow0 + row] = l > 0.f ? (mx + __log2f(l)) * kLn2 : -INFINITY;
+        }
+      } else {
+        wo[idx] = o;
+        if (d == 0) {
+          wml[row * 2 + 0] = mx;
+          wml[row * 2 + 1] = l;
+        }
+      }
+    }
+  } else {
+    // Thread t serves row t / TPR and, with j = t % TPR, the head-dim entries
+    // dim(k) = 4 j + 4 TPR (k / 4) + k % 4, k < PER: each group of four is one
+    // 16-byte piece, and the TPR threads of a row store whole 64-byte runs.
+    constexpr int NT = NW * kWave;
+    constexpr int TPR = NT / SR;
+    constexpr int PER = D / TPR;
+    constexpr bool VEC = PER % 4 == 0;
+    static_assert(TPR * SR == NT && PER * TPR == D, "window epilogue mapping");
+    const int row = threadIdx.x / TPR;
+    const int jr = threadIdx.x - row * TPR;
+    auto dim = [&](int k) { return VEC ? 4 * jr + 4 * TPR * (k >> 2) + (k & 3) : jr * PER + k; };
+    const int d0 = dim(0);
+    const bool live = qs * SR + row < a.M;
     float mx = -INFINITY;
 #pragma unroll
     for (int w = 0; w < NW; ++w) mx = fmaxf(mx, lds_ml[w][row][0]);
     const float mu = (mx == -INFINITY) ? 0.f : mx;
-    float o = 0.f, l = 0.f;
+    float o[PER], l = 0.f;
+#pragma unroll
+    for (int k = 0; k < PER; ++k) o[k] = 0.f;
 #pragma unroll
     for (int w = 0; w < NW; ++w) {
       const float sc = fast_exp2(lds_ml[w][row][0] - mu);
-      o += sc * lds_o[w][row][d];
       l += sc * lds_ml[w][row][1];
+#pragma unroll
+      for (int k = 0; k < PER; ++k) o[k] += sc * lds_o[w][row][dim(k)];
     }
+    __bf16* orow = static_cast<__bf16*>(a.out) + (orow0 + row) * D;
     if (direct) {
-      if (qs * SR + row < a.M) {
-        static_cast<__bf16*>(a.out)[(orow0 + row) * D + d] = (__bf16)(l > 0.f ? o / l : 0.f);
-        if (d == 0 && a.lse)
-          a.lse[orow0 + row] = l > 0.f ? (mx + __log2f(l)) * kLn2 : -INFINITY;
+      if (live) {
+#pragma unroll
+        for (int k = 0; k < PER; ++k) orow[dim(k)] = (__bf16)(l > 0.f ? o[k] / l : 0.f);
+        if (d0 == 0 && a.lse) a.lse[orow0 + row] = l > 0.f ? (mx + __log2f(l)) * kLn2 : -INFINITY;
       }
+      return;
+    }
+    const __amdgpu_buffer_rsrc_t own_o = coherent_view(wo, SR * D * 4);
+    if constexpr (VEC) {
+#pragma unroll
+      for (int k = 0; k < PER; k += 4)
+        store4_coherent(own_o, (row * D + dim(k)) * 4, f32x4{o[k], o[k + 1], o[k + 2], o[k + 3]});
     } else {
-      wo[idx] = o;
-      if (d == 0) {
-        wml[row * 2 + 0] = mx;
-        wml[row * 2 + 1] = l;
+#pragma unroll
+      for (int k = 0; k < PER; ++k) store_coherent(wo + row * D + dim(k), o[k]);
+    }
+    if (d0 == 0) {
+      store_coherent(wml + row * 2 + 0, mx);
+      store_coherent(wml + row * 2 + 1, l);
+    }
+    if (!last_arrival(a.arrive + (size_t)unit * a.n_qs + qs, (uint32_t)a.n_splits, a.dev_err))
+      return;
+
+    // Split merge in split order: this work-group's partial is in registers,
+    // the others' are loaded KS splits at a time (all in flight together).
+    constexpr int KS = PER >= 16 ? 2 : (PER >= 8 ? 4 : 8);
+    const size_t part0 = part - split;
+    float gm = -INFINITY, gl = 0.f, ga[PER];
+#pragma unroll
+    for (int k = 0; k < PER; ++k) ga[k] = 0.f;
+    for (int s0 = 0; s0 < a.n_splits; s0 += KS) {
+      float vo[KS][PER], vm[KS], vl[KS];
+#pragma unroll
+      for (int j = 0; j < KS; ++j) {
+        const int s = s0 + j;
+        const bool other = live && s < a.n_splits && s != split;
+        const size_t ps = part0 + (other ? s : split);
+        const __amdgpu_buffer_rsrc_t vw_o = coherent_view(a.ws_o + ps * SR * D, SR * D * 4);
+        const __amdgpu_buffer_rsrc_t vw_ml = coherent_view(a.ws_ml + ps * SR * 2, SR * 2 * 4);
+        vm[j] = mx;
+        vl[j] = l;
+#pragma unroll
+        for (int k = 0; k < PER; ++k) vo[j][k] = o[k];
+        if (other) {
+          vm[j] = load_coherent(vw_ml, row * 8);
+          vl[j] = load_coherent(vw_ml, row * 8 + 4);
+          if constexpr (VEC) {
+#pragma unroll
+            for (int k = 0; k < PER; k += 4) {
+              const f32x4 v = load4_coherent(vw_o, (row * D + dim(k)) * 4);
+#pragma unroll
+              for (int e = 0; e < 4; ++e) vo[j][k + e] = v[e];
+            }
+          } else {
+#pragma unroll
+            for (int k = 0; k < PER; ++k) vo[j][k] = load_coherent(vw_o, (row * D + dim(k)) * 4);
+          }
+        }
       }
+#pragma unroll
+      for (int j = 0; j < KS; ++j) {
+        if (s0 + j >= a.n_splits) break;
+        float s_old, s_new;
+        merge_scales(gm, vm[j], s_old, s_new);
+        gl = gl * s_old + vl[j] * s_new;
+#pragma unroll
+        for (int k = 0; k < PER; ++k) ga[k] = ga[k] * s_old + vo[j][k] * s_new;
+      }
+    }
+    if (live) {
+      const float inv = gl > 0.f ? 1.f / gl : 0.f;
+#pragma unroll
+      for (int k = 0; k < PER; ++k) orow[dim(k)] = (__bf16)(ga[k] * inv);
+      if (d0 == 0 && a.lse) a.lse[orow0 + row] = gl > 0.f ? (gm + __log2f(gl)) * kLn2 : -INFINITY;
     }
   }
 }
@@ -906,10 +1064,7 @@ __global__ __launch_bounds__(kThreads) void attn_split_valu(AttnArgs a) {
   }
 }
 
-// ---------------------------------------------------------------------------
-// Split merge: one thread per (output row, 4 head-dim entries).  Splits are
-// combined in a fixed order, so the result is deterministic.
-// ---------------------------------------------------------------------------
+// Separate merge kernel: one thread per (output row, 4 head-dim entries).
 template <int D, typename OutT>
 __global__ __launch_bounds__(256) void attn_merge(MergeArgs a) {
   constexpr int TPR = D / 4;  // threads per row
@@ -917,39 +1072,8 @@ __global__ __launch_bounds__(256) void attn_merge(MergeArgs a) {
   const long long total = (long long)a.B * a.Hkv * a.M * TPR;
   if (gid >= total) return;
   const long long grow = gid / TPR;
-  const int d0 = (int)(gid - grow * TPR) * 4;
   const int unit = (int)(grow / a.M);
-  const int row = (int)(grow - (long long)unit * a.M);
-  const int qs = row / a.slice_rows;
-  const int rr = row - qs * a.slice_rows;
-  const size_t part0 = ((size_t)unit * a.n_qs + qs) * a.n_splits;
-  const size_t pstride = (size_t)a.slice_rows;   // rows between consecutive splits
-
-  // Single pass with a running max: every split's loads are independent, so
-  // they are all in flight together.
-  const float* ml = a.ws_ml + (part0 * a.slice_rows + rr) * 2;
-  const float* src = a.ws_o + (part0 * a.slice_rows + rr) * D + d0;
-  float mx = -INFINITY, l = 0.f;
-  f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll 8
-  for (int s = 0; s < a.n_splits; ++s) {
-    const float ms = ml[s * pstride * 2];
-    const float ls = ml[s * pstride * 2 + 1];
-    const f32x4 v = *reinterpret_cast<const f32x4*>(src + s * pstride * D);
-    const float mn = fmaxf(mx, ms);
-    const float mu = (mn == -INFINITY) ? 0.f : mn;
-    const float s_old = fast_exp2(mx - mu), s_new = fast_exp2(ms - mu);
-    acc = acc * s_old + v * s_new;
-    l = l * s_old + ls * s_new;
-    mx = mn;
-  }
-  const float inv = l > 0.f ? 1.f / l : 0.f;
-  const int b = unit / a.Hkv, hk = unit - b * a.Hkv;
-  const size_t orow = (size_t)(b * a.Hq + hk * a.g) * a.n_q + row;
-  OutT* out = static_cast<OutT*>(a.out) + orow * D + d0;
-#pragma unroll
-  for (int e = 0; e < 4; ++e) out[e] = (OutT)(acc[e] * inv);
-  if (a.lse && d0 == 0) a.lse[orow] = l > 0.f ? (mx + __log2f(l)) * kLn2 : -INFINITY;
+  merge_item<D, OutT>(a, unit, (int)(grow - (long long)unit * a.M), (int)(gid - grow * TPR) * 4);
 }
 
 // ---------------------------------------------------------------------------
@@ -997,12 +1121,18 @@ AttnPlan plan_attention(int32_t B, int32_t Hkv, int32_t M, int32_t D, int32_t n_
     const long long smin = (nch + per_split - 1) / per_split;
     if (p.n_splits < smin) p.n_splits = (int)smin;
   }
+  // The draft window (a few hundred keys, latency-bound) merges its splits
+  // in the last work-group of each unit; the verify kernels keep the
+  // separate merge kernel (their tails measured no faster fused, and the
+  // extra epilogue code perturbed the tree kernel's main-loop schedule).
+  p.fuse_merge = mfma && p.n_splits > 1 && window;
   const long long tiles = units * p.n_splits;
   p.grid = (int)(p.n_qs == 1 ? tiles : ((tiles + 7) / 8) * 8 * p.n_qs);
   const size_t parts = (size_t)tiles * p.n_qs;
+  p.ws_sync_bytes = (((size_t)units * p.n_qs * sizeof(uint32_t)) + 255) & ~(size_t)255;
   p.ws_o_bytes = ((parts * p.slice_rows * D * sizeof(float)) + 255) & ~(size_t)255;
   p.ws_ml_bytes = ((parts * p.slice_rows * 2 * sizeof(float)) + 255) & ~(size_t)255;
-  p.ws_bytes = p.ws_o_bytes + p.ws_ml_bytes;
+  p.ws_bytes = p.ws_sync_bytes + p.ws_o_bytes + p.ws_ml_bytes;
   return p;
 }
 
@@ -1055,7 +1185,7 @@ hipError_t launch_attention(const AttnArgs& a, bool window, spec_dtype_t dtype, 
   hipError_t e = window           ? launch_split<true, false>(a, dtype, stream)
                  : a.block_table ? launch_split<false, true>(a, dtype, stream)
                                  : launch_split<false, false>(a, dtype, stream);
-  if (e != hipSuccess || a.n_splits == 1) return e;
+  if (e != hipSuccess || a.n_splits == 1 || a.arrive) return e;
   MergeArgs m;
   m.ws_o = a.ws_o;
   m.ws_ml = a.ws_ml;

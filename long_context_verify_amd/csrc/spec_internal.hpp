@@ -33,6 +33,7 @@ struct AttnArgs {
   int32_t num_pages;      // pages in the pool (bounds check of block_table entries)
   float* ws_o;            // [n_partials][slice_rows][D]
   float* ws_ml;           // [n_partials][slice_rows][2]  (running max in log2 units, sum)
+  uint32_t* arrive;       // [units * n_qs] split arrival counters; NULL: merge kernel
   void* out;              // [B, Hq, n_q, D]: written directly when n_splits == 1
   float* lse;             // nullable
   int32_t B, Hq, Hkv, g, n_q, D, L_cap, M;
@@ -58,7 +59,9 @@ struct MergeArgs {
 
 struct AttnPlan {
   int32_t tree_waves, slice_rows, n_qs, n_splits, grid;
-  size_t ws_o_bytes, ws_ml_bytes, ws_bytes;
+  bool fuse_merge;        // splits merged by the last work-group of each unit
+  // Workspace layout: arrival counters, then the O and (max, sum) partials.
+  size_t ws_sync_bytes, ws_o_bytes, ws_ml_bytes, ws_bytes;
 };
 
 // page_size: keys per page of a paged verify cache (0: contiguous).

@@ -143,6 +143,79 @@ def test_bad_kv_len_sets_error_and_zero_output():
     assert_attention_close(out[:1], lse[:1], o_ref, l_ref, torch.bfloat16, "good sequence")
 
 
+def test_workspace_reuse_across_calls():
+    """The draft-window kernel merges its key-range splits in the work-group
+    that finishes a unit last, counted in the workspace.  One zero-filled
+    workspace serves a run of calls in turn (verify chains and a tree at
+    several split counts, window calls) on inputs that change from round to
+    round, so partials left by an earlier call would show: every result
+    matches the oracle, no call reports an error, and the counters are back
+    at zero afterwards."""
+    from oracle.attention import window_attention as oracle_window
+    from workloads import make_window_inputs
+    say("verify workspace reuse")
+    L = _lib()
+    B, Hq, Hkv, D = 2, 16, 4, 128
+    parent = random_tree(64, seed=12)
+    nbytes = max([L.verify_attention_workspace_bytes(B, Hq, Hkv, 64, D, 3000, torch.bfloat16, s)
+                  for s in (2, 3, 7, 16)] +
+                 [L.window_attention_workspace_bytes(B, Hq, Hkv, D, 256, 4, torch.bfloat16, s)
+                  for s in (0, 3)])
+    ws = torch.zeros(nbytes, dtype=torch.uint8, device=DEV)
+    err = torch.zeros(1, dtype=torch.int32, device=DEV)
+    runs, wruns = [], []
+    for rep in range(3):
+        xs = [make_attention_inputs(B, Hq, Hkv, 5, D, 3000, dtype="bf16", seed=40 + rep,
+                                    device=DEV),
+              make_attention_inputs(B, Hq, Hkv, 64, D, 1500, dtype="bf16", seed=50 + rep,
+                                    device=DEV)]
+        for splits in (7, 3, 16):
+            x = xs[0]
+            runs.append((x, None, L.verify_attention(x["q"], x["k"], x["v"], x["kv_len"],
+                                                     num_splits=splits, workspace=ws,
+                                                     dev_err=err)))
+        x = xs[1]
+        runs.append((x, parent, L.verify_attention(x["q"], x["k"], x["v"], x["kv_len"],
+                                                   parent=parent, num_splits=2 + rep,
+                                                   workspace=ws, dev_err=err)))
+        w = make_window_inputs(B, Hq, Hkv, D, 256, 4, [5000, 77 + rep], dtype="bf16",
+                               seed=60 + rep, device=DEV)
+        wruns.append((w, L.window_attention(w["q"], w["k_ring"], w["v_ring"], w["k_sink"],
+                                            w["v_sink"], w["total_len"], num_splits=3,
+                                            workspace=ws, dev_err=err)))
+    torch.cuda.synchronize()
+    assert int(err.item()) == 0
+    assert int(ws[:256].count_nonzero().item()) == 0
+    refs = {}
+    for x, par, (out, lse) in runs:
+        key = id(x)
+        if key not in refs:
+            refs[key] = oracle_verify(x["q"], x["k"], x["v"], x["kv_len"],
+                                      None if par is None else np.asarray(par))
+        assert_attention_close(out, lse, *refs[key], torch.bfloat16, "reused workspace")
+    for w, wout in wruns:
+        o_ref, l_ref = oracle_window(w["q"], w["hist_sink_k"], w["hist_sink_v"],
+                                     w["hist_recent_k"], w["hist_recent_v"], w["total_len"], 256, 4)
+        assert_attention_close(*wout, o_ref, l_ref, torch.bfloat16, "window, reused workspace")
+
+
+def test_unzeroed_workspace_is_reported():
+    """Arrival counters that were not zero-filled (the draft window, whose
+    splits merge in the last work-group): the call sets SPEC_DEVERR_WORKSPACE
+    and every kernel still runs to completion."""
+    from workloads import make_window_inputs
+    say("window unzeroed workspace")
+    L = _lib()
+    w = make_window_inputs(2, 16, 4, 128, 256, 4, [5000, 77], dtype="bf16", seed=3, device=DEV)
+    nbytes = L.window_attention_workspace_bytes(2, 16, 4, 128, 256, 4, torch.bfloat16, 3)
+    ws = torch.full((nbytes,), 0x7F, dtype=torch.uint8, device=DEV)
+    err = torch.zeros(1, dtype=torch.int32, device=DEV)
+    L.window_attention(w["q"], w["k_ring"], w["v_ring"], w["k_sink"], w["v_sink"],
+                       w["total_len"], num_splits=3, workspace=ws, dev_err=err)
+    torch.cuda.synchronize()
+    assert int(err.item()) == 0x80
+
+
 FULL = ["llama8b_32k_chain", "magicdec_128k_chain", "medusa_tree64_8k", "llama70b_16k_chain_b64"]
 
 

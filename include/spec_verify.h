@@ -27,12 +27,13 @@
  *               be 16-byte aligned; workspaces 256-byte aligned.  All tensors
  *               are dense, row-major, in the layouts given per argument.
  *   Workspace   Scratch the caller owns, sized by the matching *_workspace
- *               function.  Zero-fill it once before its first use: the
- *               attention calls keep split-arrival counters in it, and every
- *               call leaves them at zero again, so the same workspace serves
- *               any later call (of any entry point) ordered after it on the
- *               device.  Calls that overlap in time need workspaces of their
- *               own.  Counters found non-zero set SPEC_DEVERR_WORKSPACE.
+ *               function.  Zero-fill it once before its first use: the window
+ *               attention and sampling calls keep work-group arrival counters
+ *               in it, and every call leaves them at zero again, so the same
+ *               workspace serves any later call (of any entry point) ordered
+ *               after it on the device.  Calls that overlap in time need
+ *               workspaces of their own.  Counters found non-zero set
+ *               SPEC_DEVERR_WORKSPACE.
  *   Streams     All work is enqueued on `stream` (0 = the null stream); no
  *               call synchronises the host.  Outputs are valid once the
  *               stream reaches the end of the call.

@@ -336,6 +336,7 @@ spec_status_t sample_call(const void* target_logits, const void* draft_logits,
   a.out_path = out_path;
   a.out_accept = out_accept;
   char* ws = static_cast<char*>(workspace);
+  a.arrive = reinterpret_cast<uint32_t*>(ws);
   a.part_m = reinterpret_cast<float*>(ws + p.off_m);
   a.part_s = reinterpret_cast<double*>(ws + p.off_s);
   a.race_w = reinterpret_cast<double*>(ws + p.off_w);

@@ -9,8 +9,8 @@
 // the normalised max(p_target - p_draft, 0) (after a rejection) or from
 // p_target (when the walk ends at a leaf: the bonus token).
 //
-// Three kernels, back to back on the caller's stream (the kernel boundaries
-// order the phases; no work-group waits on another):
+// Two kernels, back to back on the caller's stream (no work-group waits on
+// another; the second phase's last work-group of a sequence finishes it):
 //
 //   sample_stats   grid (vocab chunks, 2N rows, B).  Streams the logits once
 //                  (every target row and the draft rows of nodes that have
@@ -21,9 +21,13 @@
 //                  and acceptance test per node, the walk from the root: a few
 //                  hundred scalars, two memory round trips), then the residual
 //                  (or target) mass of its 1024-id race chunks of the stop
-//                  row.  Group 0 stores the decision.
-//   sample_race    grid (B).  The two-level exponential race in fp64 at the
-//                  stop row, and the outputs.
+//                  row.  The group that completes the sequence's masses (an
+//                  arrival counter per sequence in the workspace) runs the
+//                  two-level exponential race in fp64 at the stop row and
+//                  writes the outputs.
+// With the lossless sibling rule a decide kernel (one work-group per
+// sequence) runs between the two and stores the decision record that the
+// residual groups read.
 //
 // Randomness: Philox4x32-10 (Salmon, Moraes, Dror, Shaw, SC'11: four 32-bit
 // counter words, two key words, ten rounds of two 32x32->64 multiplies with
@@ -46,6 +50,9 @@ constexpr int kDecideThreads = 512;    // lossless decide: one work-group stream
 constexpr int kRaceChunk = 1024;
 constexpr int kStatsChunk = 8192;   // ids per stats work-group (32 per thread)
 constexpr int kDraftChunk = 2048;   // ids per draft-draw work-group (8 per thread)
+constexpr int kArriveFan = 16;      // residual groups per first-level arrival counter
+constexpr int kArrivePad = 16;      // counters 64 bytes apart
+constexpr int kArriveStride = kArrivePad * (kArriveFan + 1);   // counters per sequence
 
 __device__ __forceinline__ void philox4x32_10(uint32_t& c0, uint32_t& c1, uint32_t& c2,
                                               uint32_t& c3, uint32_t k0, uint32_t k1) {
@@ -234,6 +241,7 @@ struct Decision {
   uint8_t has_child[SPEC_MAX_SAMPLE_NODES];
   uint8_t acc[SPEC_MAX_SAMPLE_NODES];
   int path[SPEC_MAX_SAMPLE_NODES];
+  int tok[SPEC_MAX_SAMPLE_NODES];         // drafted token of each node
   int len, bad, stop;
   bool residual;
   double shift;                           // residual weights max(pt - shift * pd, 0)
@@ -273,6 +281,7 @@ __device__ void decide_sequence(const SampleArgs& a, int b, Decision& d,
   }
   if (tid == 0) d.bad = 0;
   for (int u = tid; u < N; u += NT) d.has_child[u] = 0;
+  if (c_tok < N) d.tok[c_tok] = x;
   __syncthreads();
   for (int c = 1 + tid; c < N; c += NT) {
     const int pc = parent_of(a, b, c);
@@ -612,6 +621,135 @@ __global__ __launch_bounds__(kDecideThreads) void sample_decide_lossless(SampleA
   store_decision(a, b, d);
 }
 
+// ---------------------------------------------------------------------------
+// The draw at the stop row and the outputs, run by the last residual
+// work-group of a sequence.  The stop node's decision comes from that
+// group's own LDS copy, or from the record the lossless decide kernel stored
+// (path node ids at dec[4 + c], accept flags at dec[4 + N + c]).  The
+// two-level exponential race: chunks race on their masses (level 1), ids
+// race inside the winning chunk on their weights (level 2).
+// ---------------------------------------------------------------------------
+struct StopView {
+  int len, bad, r;
+  bool residual;
+  double lzt, lzd, shift;   // the stop row's fp64 log-normalisers and residual shift
+  const int32_t* dec;       // the record, or NULL
+  const Decision* d;        // the LDS decision when dec is NULL
+};
+
+template <typename T>
+__device__ void race_emit(const SampleArgs& a, int b, const StopView& sv) {
+  __shared__ double redd[4];
+  __shared__ int redi[4];
+  const int N = a.N, V = a.V;
+  const int tid = threadIdx.x;
+  const int len = sv.len;
+  const int bad = sv.bad;
+  const bool residual = sv.residual;
+  int* out_tok = a.out_tokens + (size_t)b * N;
+  if (bad) {
+    for (int c = tid; c < N; c += kSampleThreads) {
+      out_tok[c] = -1;
+      if (a.out_path) a.out_path[(size_t)b * N + c] = -1;
+      if (a.out_accept) a.out_accept[(size_t)b * N + c] = 0;
+    }
+    if (tid == 0) {
+      a.out_count[b] = 0;
+      report_error(a.dev_err, bad == 2 ? SPEC_DEVERR_TOKEN : SPEC_DEVERR_PARENT);
+    }
+    return;
+  }
+  const int r = sv.r;
+
+  // Level 1: chunks race with score W_c / E1_c.  After a rejection the
+  // weights are the residual masses; if they all vanish, the target's.
+  // (The masses were stored by other work-groups of this launch.)
+  const double* rw = a.race_w + (size_t)b * a.n_race * 2;
+  double w_res = 0.0, w_tgt = 0.0;     // this thread's first chunk, q = tid
+  if (tid < a.n_race) {
+    w_res = load_coherent(rw + 2 * tid);
+    w_tgt = load_coherent(rw + 2 * tid + 1);
+  }
+  double tot = w_res;
+  for (int q = tid + kSampleThreads; q < a.n_race; q += kSampleThreads)
+    tot += load_coherent(rw + 2 * q);
+  tot = block_sum(tot, redd);
+  const bool fallback = residual && !(tot > 0.0);
+  const bool use_resid = residual && !fallback;
+  double best = -1.0;
+  int bidx = 0x7fffffff;
+  for (int q = tid; q < a.n_race; q += kSampleThreads) {
+    const double W = q == tid ? (use_resid ? w_res : w_tgt)
+                              : load_coherent(rw + 2 * q + (use_resid ? 0 : 1));
+    if (W > 0.0) {
+      uint32_t c0 = (uint32_t)q, c1 = (uint32_t)r, c2 = (uint32_t)b, c3 = a.ctr3_base + 2u;
+      philox4x32_10(c0, c1, c2, c3, a.key0, a.key1);
+      better(best, bidx, W / -log(uniform24(c0)), q);
+    }
+  }
+  block_argmax(best, bidx, redd, redi);
+  const int cstar = bidx < a.n_race ? bidx : 0;
+
+  // Level 2: ids of the winning chunk race with score w_x / E2_x (fp64 weights).
+  const double lzt = sv.lzt, lzd = sv.lzd, shift = sv.shift;
+  const T* trow = static_cast<const T*>(a.target) + ((size_t)b * N + r) * V;
+  const T* drow = static_cast<const T*>(a.draft) + ((size_t)b * N + r) * V;
+  const int e0 = cstar * kRaceChunk + 4 * tid;
+  uint32_t w0 = (uint32_t)(e0 >> 2), w1 = (uint32_t)r, w2 = (uint32_t)b, w3 = a.ctr3_base + 3u;
+  philox4x32_10(w0, w1, w2, w3, a.key0, a.key1);
+  const uint32_t words[4] = {w0, w1, w2, w3};
+  double pt[4], wx[4];
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    const int e = e0 + k;
+    pt[k] = 0.0;
+    wx[k] = 0.0;
+    if (e < V) {
+      pt[k] = exp((double)ld1(trow, e) - lzt);
+      wx[k] = pt[k];
+      if (use_resid) {
+        const double pd = exp((double)ld1(drow, e) - lzd);
+        wx[k] = pt[k] - shift * pd > 0.0 ? pt[k] - shift * pd : 0.0;
+      }
+    }
+  }
+  double best2 = -1.0;
+  int bidx2 = 0x7fffffff;
+#pragma unroll
+  for (int k = 0; k < 4; ++k)
+    if (wx[k] > 0.0) better(best2, bidx2, wx[k] / -log(uniform24(words[k])), e0 + k);
+  block_argmax(best2, bidx2, redd, redi);
+  if (bidx2 >= V) {
+    // The fp32 chunk mass was positive but no id of the chunk has a positive
+    // fp64 residual (a cancellation at the 1e-7 level): draw from the target.
+    best2 = -1.0;
+    bidx2 = 0x7fffffff;
+#pragma unroll
+    for (int k = 0; k < 4; ++k)
+      if (pt[k] > 0.0) better(best2, bidx2, pt[k] / -log(uniform24(words[k])), e0 + k);
+    block_argmax(best2, bidx2, redd, redi);
+  }
+  const int y = bidx2 < V ? bidx2 : 0;
+
+  auto path_at = [&](int c) -> int {
+    if (sv.dec) return sv.dec[4 + c];
+    return c < sv.d->len ? sv.d->path[c] : -1;
+  };
+  for (int c = tid; c < N; c += kSampleThreads) {
+    int tokv = -1;
+    const int pv = path_at(c);
+    if (c < len - 1)
+      tokv = sv.dec ? a.tokens[(size_t)b * N + path_at(c + 1)] : sv.d->tok[path_at(c + 1)];
+    else if (c == len - 1)
+      tokv = y;
+    out_tok[c] = tokv;
+    if (a.out_path) a.out_path[(size_t)b * N + c] = pv;
+    if (a.out_accept)
+      a.out_accept[(size_t)b * N + c] = (uint8_t)(sv.dec ? sv.dec[4 + N + c] : sv.d->acc[c]);
+  }
+  if (tid == 0) a.out_count[b] = len;
+}
+
 // Residual (or target) mass of the stop row's 1024-id race chunks q0 .. q1-1
 // of this group.  Every work-group of a sequence derives the same decision;
 // group 0 stores it.
@@ -626,12 +764,16 @@ __global__ __launch_bounds__(kSampleThreads) void sample_resid(SampleArgs a) {
   bool bad, residual;
   int r;
   float tm, tinv, dm, dinv, shift;
+  double lzt, lzd, shiftd;   // fp64 log-normalisers and shift of the stop row
   if constexpr (FROM_RECORD) {
     const int32_t* dec = a.decision + (size_t)b * a.dec_stride;
     const double* st = a.decision_lz + (size_t)b * kDecisionDoubles;
     bad = dec[1] != 0;
     residual = dec[2] != 0;
     r = dec[3];
+    lzt = st[0];
+    lzd = st[1];
+    shiftd = st[2];
     shift = (float)st[2];
     tm = (float)st[3];
     tinv = (float)st[4];
@@ -639,10 +781,12 @@ __global__ __launch_bounds__(kSampleThreads) void sample_resid(SampleArgs a) {
     dinv = (float)st[6];
   } else {
     decide_sequence<T>(a, b, d);
-    if (grp == 0) store_decision(a, b, d);
     bad = d.bad != 0;
     residual = d.residual;
     r = d.stop;
+    lzt = d.lz[0][r];
+    lzd = residual ? d.lz[1][r] : 0.0;
+    shiftd = residual ? d.shift : 0.0;
     shift = 1.f;
     tm = d.m[0][r];
     tinv = (float)(1.0 / d.s[0][r]);
@@ -709,119 +853,34 @@ __global__ __launch_bounds__(kSampleThreads) void sample_resid(SampleArgs a) {
         tp += part[w][tid][1];
       }
       double* o = a.race_w + ((size_t)b * a.n_race + qb + tid) * 2;
-      o[0] = tw;
-      o[1] = tp;
+      store_coherent(o, tw);
+      store_coherent(o + 1, tp);
     }
     __syncthreads();
   }
+
+  // The group that completes the sequence's masses runs the draw.
+  // Two-level arrival (fan-in kArriveFan): a hundred groups incrementing one
+  // counter would serialise on it.
+  {
+    uint32_t* ctr = a.arrive + (size_t)b * kArriveStride;
+    const int sub = grp % kArriveFan;
+    const int n_sub = (a.n_groups - 1 - sub) / kArriveFan + 1;
+    if (!last_arrival(ctr + kArrivePad * sub, (uint32_t)n_sub, a.dev_err)) return;
+    if (!last_arrival(ctr + kArrivePad * kArriveFan, (uint32_t)min(kArriveFan, a.n_groups),
+                      a.dev_err))
+      return;
+  }
+  StopView sv;
+  if constexpr (FROM_RECORD) {
+    const int32_t* dec = a.decision + (size_t)b * a.dec_stride;
+    sv = StopView{dec[0], dec[1], r, residual, lzt, lzd, shiftd, dec, nullptr};
+  } else {
+    sv = StopView{d.len, d.bad, r, residual, lzt, lzd, shiftd, nullptr, &d};
+  }
+  race_emit<T>(a, b, sv);
 }
 
-// ---------------------------------------------------------------------------
-// The draw at the stop row and the outputs: one work-group per sequence.
-// ---------------------------------------------------------------------------
-template <typename T>
-__global__ __launch_bounds__(kSampleThreads) void sample_race(SampleArgs a) {
-  __shared__ double redd[4];
-  __shared__ int redi[4];
-  const int b = blockIdx.x;
-  const int N = a.N, V = a.V;
-  const int tid = threadIdx.x;
-  const int32_t* dec = a.decision + (size_t)b * a.dec_stride;
-  const int len = dec[0];
-  const int bad = dec[1];
-  const bool residual = dec[2] != 0;
-  int* out_tok = a.out_tokens + (size_t)b * N;
-  if (bad) {
-    for (int c = tid; c < N; c += kSampleThreads) {
-      out_tok[c] = -1;
-      if (a.out_path) a.out_path[(size_t)b * N + c] = -1;
-      if (a.out_accept) a.out_accept[(size_t)b * N + c] = 0;
-    }
-    if (tid == 0) {
-      a.out_count[b] = 0;
-      report_error(a.dev_err, bad == 2 ? SPEC_DEVERR_TOKEN : SPEC_DEVERR_PARENT);
-    }
-    return;
-  }
-  const int r = dec[3];
-  const double* st = a.decision_lz + (size_t)b * kDecisionDoubles;
-  const double lzt = st[0], lzd = st[1], shift = st[2];
-  const T* trow = static_cast<const T*>(a.target) + ((size_t)b * N + r) * V;
-  const T* drow = static_cast<const T*>(a.draft) + ((size_t)b * N + r) * V;
-
-  // Level 1: chunks race with score W_c / E1_c.  After a rejection the
-  // weights are the residual masses; if they all vanish, the target's.
-  const double* rw = a.race_w + (size_t)b * a.n_race * 2;
-  double tot = 0.0;
-  for (int q = tid; q < a.n_race; q += kSampleThreads) tot += rw[2 * q];
-  tot = block_sum(tot, redd);
-  const bool fallback = residual && !(tot > 0.0);
-  const int col = (residual && !fallback) ? 0 : 1;
-  double best = -1.0;
-  int bidx = 0x7fffffff;
-  for (int q = tid; q < a.n_race; q += kSampleThreads) {
-    const double W = rw[2 * q + col];
-    if (W > 0.0) {
-      uint32_t c0 = (uint32_t)q, c1 = (uint32_t)r, c2 = (uint32_t)b, c3 = a.ctr3_base + 2u;
-      philox4x32_10(c0, c1, c2, c3, a.key0, a.key1);
-      better(best, bidx, W / -log(uniform24(c0)), q);
-    }
-  }
-  block_argmax(best, bidx, redd, redi);
-  const int cstar = bidx < a.n_race ? bidx : 0;
-  const bool use_resid = residual && !fallback;
-
-  // Level 2: ids of the winning chunk race with score w_x / E2_x (fp64 weights).
-  const int e0 = cstar * kRaceChunk + 4 * tid;
-  uint32_t w0 = (uint32_t)(e0 >> 2), w1 = (uint32_t)r, w2 = (uint32_t)b, w3 = a.ctr3_base + 3u;
-  philox4x32_10(w0, w1, w2, w3, a.key0, a.key1);
-  const uint32_t words[4] = {w0, w1, w2, w3};
-  double pt[4], wx[4];
-#pragma unroll
-  for (int k = 0; k < 4; ++k) {
-    const int e = e0 + k;
-    pt[k] = 0.0;
-    wx[k] = 0.0;
-    if (e < V) {
-      pt[k] = exp((double)ld1(trow, e) - lzt);
-      wx[k] = pt[k];
-      if (use_resid) {
-        const double pd = exp((double)ld1(drow, e) - lzd);
-        wx[k] = pt[k] - shift * pd > 0.0 ? pt[k] - shift * pd : 0.0;
-      }
-    }
-  }
-  double best2 = -1.0;
-  int bidx2 = 0x7fffffff;
-#pragma unroll
-  for (int k = 0; k < 4; ++k)
-    if (wx[k] > 0.0) better(best2, bidx2, wx[k] / -log(uniform24(words[k])), e0 + k);
-  block_argmax(best2, bidx2, redd, redi);
-  if (bidx2 >= V) {
-    // The fp32 chunk mass was positive but no id of the chunk has a positive
-    // fp64 residual (a cancellation at the 1e-7 level): draw from the target.
-    best2 = -1.0;
-    bidx2 = 0x7fffffff;
-#pragma unroll
-    for (int k = 0; k < 4; ++k)
-      if (pt[k] > 0.0) better(best2, bidx2, pt[k] / -log(uniform24(words[k])), e0 + k);
-    block_argmax(best2, bidx2, redd, redi);
-  }
-  const int y = bidx2 < V ? bidx2 : 0;
-
-  for (int c = tid; c < N; c += kSampleThreads) {
-    int tokv = -1;
-    const int pv = dec[4 + c];
-    if (c < len - 1)
-      tokv = a.tokens[(size_t)b * N + dec[4 + c + 1]];
-    else if (c == len - 1)
-      tokv = y;
-    out_tok[c] = tokv;
-    if (a.out_path) a.out_path[(size_t)b * N + c] = pv;
-    if (a.out_accept) a.out_accept[(size_t)b * N + c] = (uint8_t)dec[4 + N + c];
-  }
-  if (tid == 0) a.out_count[b] = len;
-}
 
 // ---------------------------------------------------------------------------
 // Host-side planning and launch.
@@ -842,7 +901,7 @@ SamplePlan plan_sample(int32_t B, int32_t N, int32_t V) {
   p.n_groups = (int)groups;
   p.dec_stride = 4 + 2 * N;
   const size_t rows = (size_t)B * 2 * N * p.n_vchunks;
-  p.off_m = 0;
+  p.off_m = align256((size_t)B * kArriveStride * sizeof(uint32_t));
   p.off_s = align256(p.off_m + rows * sizeof(float));
   p.off_w = align256(p.off_s + rows * sizeof(double));
   p.off_dec = align256(p.off_w + (size_t)B * p.n_race * 2 * sizeof(double));
@@ -876,7 +935,6 @@ static hipError_t launch_sample_t(const SampleArgs& a, hipStream_t stream) {
   } else {
     hipLaunchKernelGGL((sample_resid<false, T>), g2, blk, 0, stream, a);
   }
-  hipLaunchKernelGGL((sample_race<T>), g3, blk, 0, stream, a);
   return hipGetLastError();
 }
 

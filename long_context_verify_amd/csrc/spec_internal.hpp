@@ -86,6 +86,7 @@ struct SampleArgs {
   int32_t* out_path;
   uint8_t* out_accept;
   // workspace views
+  uint32_t* arrive;        // [B][..] arrival counters of the residual work-groups
   float* part_m;           // [B][2N][n_vchunks]
   double* part_s;          // [B][2N][n_vchunks]
   double* race_w;          // [B][n_race][2]  (residual mass, target mass) per race chunk
@@ -106,7 +107,7 @@ constexpr int kDecisionDoubles = 8;
 
 struct SamplePlan {
   int32_t n_vchunks, vchunk, n_race, n_groups, dec_stride;
-  size_t off_m, off_s, off_w, off_dec, off_lz, bytes;
+  size_t off_m, off_s, off_w, off_dec, off_lz, bytes;   // arrival counters at offset 0
 };
 
 SamplePlan plan_sample(int32_t B, int32_t N, int32_t V);

@@ -241,6 +241,33 @@ def test_bad_token_flags_error():
     assert torch.all(r["out_count"][[0, 1, 3]] >= 1)
 
 
+def test_workspace_reuse_across_calls():
+    """The draw runs in the residual work-group that completes a sequence's
+    masses, counted in the workspace.  One zero-filled workspace serves a run
+    of calls on changing inputs and both sibling rules: each result equals a
+    call with a fresh workspace, no call reports an error, and the counters
+    are back at zero afterwards."""
+    import long_context_verify_amd as L
+    say("sample workspace reuse")
+    B, N, V = 16, 9, 40000
+    parent = random_tree(N, seed=9)
+    ws = torch.zeros(L.sample_workspace_bytes(B, N, V), dtype=torch.uint8, device=DEV)
+    err = torch.zeros(1, dtype=torch.int32, device=DEV)
+    for rep in range(4):
+        x = make_sample_inputs(B, N, V, parent, 3.0, draft_noise_std=1.0, seed=70 + rep,
+                               device=DEV)
+        rule = "lossless" if rep % 2 else "first"
+        got = L.spec_sample(x["target"], x["draft"], x["tokens"], parent=parent, seed=rep,
+                            offset=rep, siblings=rule, workspace=ws, dev_err=err)
+        ref = L.spec_sample(x["target"], x["draft"], x["tokens"], parent=parent, seed=rep,
+                            offset=rep, siblings=rule)
+        torch.cuda.synchronize()
+        for k in ref:
+            assert torch.equal(got[k], ref[k]), f"rep {rep}: {k}"
+    assert int(err.item()) == 0
+    assert int(ws[:B * 1088].count_nonzero().item()) == 0    # the arrival counters
+
+
 def test_deterministic_bits():
     say("sample determinism")
     x = make_sample_inputs(32, 5, 50000, None, 3.0, draft_noise_std=1.0, seed=6, device=DEV)

@@ -799,49 +799,56 @@ __global__ __launch_bounds__(kSampleThreads) void sample_resid(SampleArgs a) {
   const int q1 = (int)((long long)a.n_race * (grp + 1) / a.n_groups);
   // Per chunk: each wave reduces its lanes with shuffles and parks the two
   // partial sums in LDS; one block pass per batch of chunks adds the waves.
+  // The loads of kU chunks are issued together (a group may own several).
   constexpr int kBatch = 64;
+  constexpr int kU = 4;
   __shared__ double part[kSampleThreads / kWave][kBatch][2];
   const int wave = tid >> 6, lane = tid & 63;
   for (int qb = q0; qb < q1; qb += kBatch) {
     const int nq = min(kBatch, q1 - qb);
-    for (int i = 0; i < nq; ++i) {
-      const int q = qb + i;
-      float sw = 0.f, spt = 0.f;
-      if (!bad) {
-        const int e0 = q * kRaceChunk + 4 * tid;
-        float tv[4], dv[4];
+    for (int i0 = 0; i0 < nq; i0 += kU) {
+      float tv[kU][4], dv[kU][4];
+#pragma unroll
+      for (int u = 0; u < kU; ++u) {
+        const int e0 = (qb + i0 + u) * kRaceChunk + 4 * tid;
+        const bool live = i0 + u < nq && !bad;
         if (VEC4) {
           f32x4 t4 = {-INFINITY, -INFINITY, -INFINITY, -INFINITY}, d4 = t4;
-          if (e0 < V) {
+          if (live && e0 < V) {
             t4 = ld4(trow, e0);
             if (residual) d4 = ld4(drow, e0);
           }
 #pragma unroll
           for (int k = 0; k < 4; ++k) {
-            tv[k] = t4[k];
-            dv[k] = d4[k];
+            tv[u][k] = t4[k];
+            dv[u][k] = d4[k];
           }
         } else {
 #pragma unroll
           for (int k = 0; k < 4; ++k) {
             const int e = e0 + k;
-            tv[k] = e < V ? ld1(trow, e) : -INFINITY;
-            dv[k] = (e < V && residual) ? ld1(drow, e) : -INFINITY;
+            tv[u][k] = (live && e < V) ? ld1(trow, e) : -INFINITY;
+            dv[u][k] = (live && e < V && residual) ? ld1(drow, e) : -INFINITY;
           }
         }
+      }
+#pragma unroll
+      for (int u = 0; u < kU; ++u) {
+        if (i0 + u >= nq) break;
+        float sw = 0.f, spt = 0.f;
 #pragma unroll
         for (int k = 0; k < 4; ++k) {
-          const float pt = fast_exp2((tv[k] - tm) * kLog2e) * tinv;
-          const float pd = residual ? fast_exp2((dv[k] - dm) * kLog2e) * dinv : 0.f;
+          const float pt = fast_exp2((tv[u][k] - tm) * kLog2e) * tinv;
+          const float pd = residual ? fast_exp2((dv[u][k] - dm) * kLog2e) * dinv : 0.f;
           spt += pt;
           sw += fmaxf(pt - shift * pd, 0.f);
         }
-      }
-      const double tw = wave_sum((double)sw);
-      const double tp = wave_sum((double)spt);
-      if (lane == 0) {
-        part[wave][i][0] = tw;
-        part[wave][i][1] = tp;
+        const double tw = wave_sum((double)sw);
+        const double tp = wave_sum((double)spt);
+        if (lane == 0) {
+          part[wave][i0 + u][0] = tw;
+          part[wave][i0 + u][1] = tp;
+        }
       }
     }
     __syncthreads();

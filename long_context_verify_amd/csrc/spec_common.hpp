@@ -63,12 +63,6 @@ __device__ __forceinline__ void store_coherent(double* p, double v) {
 __device__ __forceinline__ double load_coherent(const double* p) {
   return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
-__device__ __forceinline__ void store_coherent(int32_t* p, int32_t v) {
-  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-__device__ __forceinline__ int32_t load_coherent(const int32_t* p) {
-  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
 constexpr int kBufferWord3 = 0x00020000;   // raw buffer descriptor, word 3 (32-bit data format)
 constexpr int kDeviceScope = 16;           // buffer cache policy: sc1
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t coherent_view(const float* base, uint32_t bytes) {

@@ -28,8 +28,8 @@
  *               are dense, row-major, in the layouts given per argument.
  *   Workspace   Scratch the caller owns, sized by the matching *_workspace
  *               function.  Zero-fill it once before its first use: the window
- *               attention and sampling calls keep work-group arrival counters
- *               in it, and every call leaves them at zero again, so the same
+ *               attention, sampling and draft-draw calls keep work-group
+ *               arrival counters in it, and every call leaves them at zero again, so the same
  *               workspace serves any later call (of any entry point) ordered
  *               after it on the device.  Calls that overlap in time need
  *               workspaces of their own.  Counters found non-zero set

@@ -434,6 +434,7 @@ spec_status_t spec_draft_sample(const void* draft_logits, spec_dtype_t dtype, in
   a.token_stride = token_stride ? token_stride : 1;
   a.out_logprob = out_logprob;
   char* ws = static_cast<char*>(workspace);
+  a.arrive = reinterpret_cast<uint32_t*>(ws);
   a.part_best = reinterpret_cast<double*>(ws + p.off_best);
   a.part_idx = reinterpret_cast<int32_t*>(ws + p.off_idx);
   a.part_x = reinterpret_cast<float*>(ws + p.off_x);

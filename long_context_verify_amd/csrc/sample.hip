@@ -54,6 +54,16 @@ constexpr int kArriveFan = 16;      // residual groups per first-level arrival c
 constexpr int kArrivePad = 16;      // counters 64 bytes apart
 constexpr int kArriveStride = kArrivePad * (kArriveFan + 1);   // counters per sequence
 
+// Arrival of member `i` of a group of n work-groups at a two-level tree of
+// counters (kArriveStride of them at ctr): true in the last to arrive.  A
+// hundred work-groups incrementing one counter would serialise on it.
+__device__ __forceinline__ bool last_of_group(uint32_t* ctr, int i, int n, int32_t* dev_err) {
+  const int sub = i % kArriveFan;
+  const int n_sub = (n - 1 - sub) / kArriveFan + 1;
+  if (!last_arrival(ctr + kArrivePad * sub, (uint32_t)n_sub, dev_err)) return false;
+  return last_arrival(ctr + kArrivePad * kArriveFan, (uint32_t)min(kArriveFan, n), dev_err);
+}
+
 __device__ __forceinline__ void philox4x32_10(uint32_t& c0, uint32_t& c1, uint32_t& c2,
                                               uint32_t& c3, uint32_t k0, uint32_t k1) {
 #pragma unroll
@@ -867,17 +877,7 @@ __global__ __launch_bounds__(kSampleThreads) void sample_resid(SampleArgs a) {
   }
 
   // The group that completes the sequence's masses runs the draw.
-  // Two-level arrival (fan-in kArriveFan): a hundred groups incrementing one
-  // counter would serialise on it.
-  {
-    uint32_t* ctr = a.arrive + (size_t)b * kArriveStride;
-    const int sub = grp % kArriveFan;
-    const int n_sub = (a.n_groups - 1 - sub) / kArriveFan + 1;
-    if (!last_arrival(ctr + kArrivePad * sub, (uint32_t)n_sub, a.dev_err)) return;
-    if (!last_arrival(ctr + kArrivePad * kArriveFan, (uint32_t)min(kArriveFan, a.n_groups),
-                      a.dev_err))
-      return;
-  }
+  if (!last_of_group(a.arrive + (size_t)b * kArriveStride, grp, a.n_groups, a.dev_err)) return;
   StopView sv;
   if constexpr (FROM_RECORD) {
     const int32_t* dec = a.decision + (size_t)b * a.dec_stride;
@@ -958,7 +958,8 @@ hipError_t launch_sample(const SampleArgs& a, hipStream_t stream) {
 // needs neither the row max nor the normaliser; it is evaluated in fp64, the
 // precision the reference draw decides in.  Max and normaliser are still
 // gathered (per chunk: max and sum of exp2) for the drawn token's
-// log-probability.
+// log-probability.  One launch: the work-group that completes a row's last
+// chunk (arrival counters in the workspace) combines the chunk partials.
 // ---------------------------------------------------------------------------
 // Arg-max of (score, id) with ties to the lowest id, carrying the winner's
 // scaled logit along.
@@ -987,6 +988,44 @@ __device__ __forceinline__ void block_argmax_f(RaceBest& r, RaceBest* red) {
   r = red[0];
 #pragma unroll
   for (int k = 1; k < 4; ++k) better_f(r, red[k].s, red[k].i, red[k].x);
+}
+
+// Combines the chunk partials of row b: the race winner (chunks are in id
+// order, so ties still go to the lowest id), the fp64 log2 normaliser, and
+// the winner's log-probability.  The partials were stored by other
+// work-groups of this launch.
+__device__ void draft_finish_row(const DraftArgs& a, int b, float* redf, double* redd,
+                                 RaceBest* redr) {
+  const size_t o = (size_t)b * a.n_chunks;
+  float mx = -INFINITY;
+  RaceBest best{-INFINITY, 0x7fffffff, -INFINITY};
+  for (int c = threadIdx.x; c < a.n_chunks; c += kSampleThreads) {
+    better_f(best, load_coherent(a.part_best + o + c),
+             __hip_atomic_load(a.part_idx + o + c, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT),
+             load_coherent(a.part_x + o + c));
+    mx = fmaxf(mx, load_coherent(a.part_m + o + c));
+  }
+  block_argmax_f(best, redr);
+  mx = block_max(mx, redf);
+  double sum = 0.0;
+  if (mx != -INFINITY)
+    for (int c = threadIdx.x; c < a.n_chunks; c += kSampleThreads) {
+      const float m = load_coherent(a.part_m + o + c);
+      if (m != -INFINITY) sum += load_coherent(a.part_s + o + c) * exp2((double)m - (double)mx);
+    }
+  sum = block_sum(sum, redd);
+  if (threadIdx.x == 0) {
+    int tok = best.i;
+    float lp = NAN;
+    if (best.s == -INFINITY || best.s != best.s || tok < 0 || tok >= a.V) {
+      tok = -1;
+      report_error(a.dev_err, SPEC_DEVERR_LOGITS);
+    } else {
+      lp = (float)(((double)best.x - (double)mx - log2(sum)) * 0.6931471805599453);
+    }
+    a.out_token[(size_t)b * a.token_stride] = tok;
+    if (a.out_logprob) a.out_logprob[b] = lp;
+  }
 }
 
 // grid (chunks of 2048 ids, B).  Thread t holds the id groups
@@ -1080,57 +1119,22 @@ __global__ __launch_bounds__(kSampleThreads) void draft_partial(DraftArgs a) {
   const double tot = block_sum((double)sum, redd);
   if (threadIdx.x == 0) {
     const size_t o = (size_t)b * a.n_chunks + chunk;
-    a.part_best[o] = best.s;
-    a.part_idx[o] = best.i;
-    a.part_x[o] = best.x;
-    a.part_m[o] = mx;
-    a.part_s[o] = tot;
+    store_coherent(a.part_best + o, best.s);
+    __hip_atomic_store(a.part_idx + o, best.i, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    store_coherent(a.part_x + o, best.x);
+    store_coherent(a.part_m + o, mx);
+    store_coherent(a.part_s + o, tot);
   }
-}
-
-// grid (B).  Combines the chunk partials of one row: the race winner (chunks
-// are in id order, so ties still go to the lowest id), the fp64 log2
-// normaliser, and the winner's log-probability.
-__global__ __launch_bounds__(kSampleThreads) void draft_finish(DraftArgs a) {
-  __shared__ float redf[4];
-  __shared__ double redd[4];
-  __shared__ RaceBest redr[4];
-  const int b = blockIdx.x;
-  const size_t o = (size_t)b * a.n_chunks;
-  float mx = -INFINITY;
-  RaceBest best{-INFINITY, 0x7fffffff, -INFINITY};
-  for (int c = threadIdx.x; c < a.n_chunks; c += kSampleThreads) {
-    better_f(best, a.part_best[o + c], a.part_idx[o + c], a.part_x[o + c]);
-    mx = fmaxf(mx, a.part_m[o + c]);
-  }
-  block_argmax_f(best, redr);
-  mx = block_max(mx, redf);
-  double sum = 0.0;
-  if (mx != -INFINITY)
-    for (int c = threadIdx.x; c < a.n_chunks; c += kSampleThreads) {
-      const float m = a.part_m[o + c];
-      if (m != -INFINITY) sum += a.part_s[o + c] * exp2((double)m - (double)mx);
-    }
-  sum = block_sum(sum, redd);
-  if (threadIdx.x == 0) {
-    int tok = best.i;
-    float lp = NAN;
-    if (best.s == -INFINITY || best.s != best.s || tok < 0 || tok >= a.V) {
-      tok = -1;
-      report_error(a.dev_err, SPEC_DEVERR_LOGITS);
-    } else {
-      lp = (float)(((double)best.x - (double)mx - log2(sum)) * 0.6931471805599453);
-    }
-    a.out_token[(size_t)b * a.token_stride] = tok;
-    if (a.out_logprob) a.out_logprob[b] = lp;
-  }
+  // The work-group that completes the row's chunks combines them.
+  if (last_of_group(a.arrive + (size_t)b * kArriveStride, chunk, a.n_chunks, a.dev_err))
+    draft_finish_row(a, b, redf, redd, redr);
 }
 
 DraftPlan plan_draft(int32_t B, int32_t V) {
   DraftPlan p{};
   p.n_chunks = (V + kDraftChunk - 1) / kDraftChunk;
   const size_t n = (size_t)B * p.n_chunks;
-  p.off_best = 0;
+  p.off_best = align256((size_t)B * kArriveStride * sizeof(uint32_t));   // arrival counters first
   p.off_idx = align256(p.off_best + n * sizeof(double));
   p.off_x = align256(p.off_idx + n * sizeof(int32_t));
   p.off_m = align256(p.off_x + n * sizeof(float));
@@ -1140,7 +1144,7 @@ DraftPlan plan_draft(int32_t B, int32_t V) {
 }
 
 hipError_t launch_draft(const DraftArgs& a, bool vec4, hipStream_t stream) {
-  dim3 g1(a.n_chunks, a.B), g2(a.B), blk(kSampleThreads);
+  dim3 g1(a.n_chunks, a.B), blk(kSampleThreads);
   if (a.logits_bf16) {
     if (vec4)
       hipLaunchKernelGGL((draft_partial<true, __bf16>), g1, blk, 0, stream, a);
@@ -1152,7 +1156,6 @@ hipError_t launch_draft(const DraftArgs& a, bool vec4, hipStream_t stream) {
     else
       hipLaunchKernelGGL((draft_partial<false, float>), g1, blk, 0, stream, a);
   }
-  hipLaunchKernelGGL(draft_finish, g2, blk, 0, stream, a);
   return hipGetLastError();
 }
 

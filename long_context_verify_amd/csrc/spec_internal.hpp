@@ -139,6 +139,7 @@ struct DraftArgs {
   int32_t* out_token;       // out_token[b * token_stride]
   int32_t token_stride;
   float* out_logprob;       // nullable, [B]
+  uint32_t* arrive;         // [B][..] arrival counters of the chunk work-groups
   double* part_best;        // [B][n_chunks] best race score (natural log units)
   int32_t* part_idx;        // [B][n_chunks] its id
   float* part_x;            // [B][n_chunks] its logit * log2(e)

@@ -24,10 +24,9 @@
 //     an ancestor of the query's node (a 64-bit mask built from the parent
 //     array);
 //   * the four waves merge through LDS once at the end; the split partials
-//     (unnormalised O, running max, sum) go to the workspace and are combined
-//     in a fixed order: by a second kernel for the verify block, and for the
-//     short draft window by the work-group that completes a unit's last split
-//     (an arrival counter per unit in the workspace).
+//     (unnormalised O, running max, sum) go to the workspace and the
+//     work-group that completes a unit's last split (an arrival counter per
+//     unit in the workspace) combines them in a fixed order.
 //
 // The fp32 path is a plain VALU kernel (one wave per query row, lanes over
 // the head dimension) with the same partial format, merged by the second kernel.
@@ -511,147 +510,116 @@ __global__ __launch_bounds__(NW * kWave, 8 / NW) void attn_split_mfma(AttnArgs a
 
   // Merge the waves.  With a single split per unit this is the final result
   // (normalised and stored straight to the output); otherwise the work-group
-  // partial goes to the workspace for the split merge, which the window
-  // kernel runs in the work-group that completes the unit's last split and
-  // the verify kernel leaves to a second kernel.
+  // partial goes to the workspace, and the work-group that completes the
+  // unit's last split merges the splits.
   const size_t part = ((size_t)unit * a.n_qs + qs) * a.n_splits + split;
   float* wo = a.ws_o + part * SR * D;
   float* wml = a.ws_ml + part * SR * 2;
   const bool direct = a.n_splits == 1;
   const size_t orow0 = (size_t)(u.b * a.Hq + u.hk * a.g) * a.n_q + (size_t)qs * SR;
-  if constexpr (!WINDOW) {
-    for (int idx = threadIdx.x; idx < SR * D; idx += NW * kWave) {
-      const int row = idx / D, d = idx - row * D;
-      float mx = -INFINITY;
+  // Thread t serves row t / TPR and, with j = t % TPR, the head-dim entries
+  // dim(k) = 4 j + 4 TPR (k / 4) + k % 4, k < PER: each group of four is one
+  // 16-byte piece, and the TPR threads of a row store whole 64-byte runs.
+  constexpr int NT = NW * kWave;
+  constexpr int TPR = NT / SR;
+  constexpr int PER = D / TPR;
+  constexpr bool VEC = PER % 4 == 0;
+  static_assert(TPR * SR == NT && PER * TPR == D, "epilogue mapping");
+  const int row = threadIdx.x / TPR;
+  const int jr = threadIdx.x - row * TPR;
+  auto dim = [&](int k) { return VEC ? 4 * jr + 4 * TPR * (k >> 2) + (k & 3) : jr * PER + k; };
+  const int d0 = dim(0);
+  const bool live = qs * SR + row < a.M;
+  float mx = -INFINITY;
 #pragma unroll
-      for (int w = 0; w < NW; ++w) mx = fmaxf(mx, lds_ml[w][row][0]);
-      const float mu = (mx == -INFINITY) ? 0.f : mx;
-      float o = 0.f, l = 0.f;
+  for (int w = 0; w < NW; ++w) mx = fmaxf(mx, lds_ml[w][row][0]);
+  const float mu = (mx == -INFINITY) ? 0.f : mx;
+  float o[PER], l = 0.f;
 #pragma unroll
-      for (int w = 0; w < NW; ++w) {
-        const float sc = fast_exp2(lds_ml[w][row][0] - mu);
-        o += sc * lds_o[w][row][d];
-        l += sc * lds_ml[w][row][1];
-      }
-      if (direct) {
-        if (qs * SR + row < a.M) {
-          static_cast<__bf16*>(a.out)[(orow0 + row) * D + d] = (__bf16)(l > 0.f ? o / l : 0.f);
-          if (d == 0 && a.lse)
-            a.lse[orow0 + row] = l > 0.f ? (mx + __log2f(l)) * kLn2 : -INFINITY;
-        }
-      } else {
-        wo[idx] = o;
-        if (d == 0) {
-          wml[row * 2 + 0] = mx;
-          wml[row * 2 + 1] = l;
-        }
-      }
-    }
-  } else {
-    // Thread t serves row t / TPR and, with j = t % TPR, the head-dim entries
-    // dim(k) = 4 j + 4 TPR (k / 4) + k % 4, k < PER: each group of four is one
-    // 16-byte piece, and the TPR threads of a row store whole 64-byte runs.
-    constexpr int NT = NW * kWave;
-    constexpr int TPR = NT / SR;
-    constexpr int PER = D / TPR;
-    constexpr bool VEC = PER % 4 == 0;
-    static_assert(TPR * SR == NT && PER * TPR == D, "window epilogue mapping");
-    const int row = threadIdx.x / TPR;
-    const int jr = threadIdx.x - row * TPR;
-    auto dim = [&](int k) { return VEC ? 4 * jr + 4 * TPR * (k >> 2) + (k & 3) : jr * PER + k; };
-    const int d0 = dim(0);
-    const bool live = qs * SR + row < a.M;
-    float mx = -INFINITY;
+  for (int k = 0; k < PER; ++k) o[k] = 0.f;
 #pragma unroll
-    for (int w = 0; w < NW; ++w) mx = fmaxf(mx, lds_ml[w][row][0]);
-    const float mu = (mx == -INFINITY) ? 0.f : mx;
-    float o[PER], l = 0.f;
+  for (int w = 0; w < NW; ++w) {
+    const float sc = fast_exp2(lds_ml[w][row][0] - mu);
+    l += sc * lds_ml[w][row][1];
 #pragma unroll
-    for (int k = 0; k < PER; ++k) o[k] = 0.f;
-#pragma unroll
-    for (int w = 0; w < NW; ++w) {
-      const float sc = fast_exp2(lds_ml[w][row][0] - mu);
-      l += sc * lds_ml[w][row][1];
-#pragma unroll
-      for (int k = 0; k < PER; ++k) o[k] += sc * lds_o[w][row][dim(k)];
-    }
-    __bf16* orow = static_cast<__bf16*>(a.out) + (orow0 + row) * D;
-    if (direct) {
-      if (live) {
-#pragma unroll
-        for (int k = 0; k < PER; ++k) orow[dim(k)] = (__bf16)(l > 0.f ? o[k] / l : 0.f);
-        if (d0 == 0 && a.lse) a.lse[orow0 + row] = l > 0.f ? (mx + __log2f(l)) * kLn2 : -INFINITY;
-      }
-      return;
-    }
-    const __amdgpu_buffer_rsrc_t own_o = coherent_view(wo, SR * D * 4);
-    if constexpr (VEC) {
-#pragma unroll
-      for (int k = 0; k < PER; k += 4)
-        store4_coherent(own_o, (row * D + dim(k)) * 4, f32x4{o[k], o[k + 1], o[k + 2], o[k + 3]});
-    } else {
-#pragma unroll
-      for (int k = 0; k < PER; ++k) store_coherent(wo + row * D + dim(k), o[k]);
-    }
-    if (d0 == 0) {
-      store_coherent(wml + row * 2 + 0, mx);
-      store_coherent(wml + row * 2 + 1, l);
-    }
-    if (!last_arrival(a.arrive + (size_t)unit * a.n_qs + qs, (uint32_t)a.n_splits, a.dev_err))
-      return;
-
-    // Split merge in split order: this work-group's partial is in registers,
-    // the others' are loaded KS splits at a time (all in flight together).
-    constexpr int KS = PER >= 16 ? 2 : (PER >= 8 ? 4 : 8);
-    const size_t part0 = part - split;
-    float gm = -INFINITY, gl = 0.f, ga[PER];
-#pragma unroll
-    for (int k = 0; k < PER; ++k) ga[k] = 0.f;
-    for (int s0 = 0; s0 < a.n_splits; s0 += KS) {
-      float vo[KS][PER], vm[KS], vl[KS];
-#pragma unroll
-      for (int j = 0; j < KS; ++j) {
-        const int s = s0 + j;
-        const bool other = live && s < a.n_splits && s != split;
-        const size_t ps = part0 + (other ? s : split);
-        const __amdgpu_buffer_rsrc_t vw_o = coherent_view(a.ws_o + ps * SR * D, SR * D * 4);
-        const __amdgpu_buffer_rsrc_t vw_ml = coherent_view(a.ws_ml + ps * SR * 2, SR * 2 * 4);
-        vm[j] = mx;
-        vl[j] = l;
-#pragma unroll
-        for (int k = 0; k < PER; ++k) vo[j][k] = o[k];
-        if (other) {
-          vm[j] = load_coherent(vw_ml, row * 8);
-          vl[j] = load_coherent(vw_ml, row * 8 + 4);
-          if constexpr (VEC) {
-#pragma unroll
-            for (int k = 0; k < PER; k += 4) {
-              const f32x4 v = load4_coherent(vw_o, (row * D + dim(k)) * 4);
-#pragma unroll
-              for (int e = 0; e < 4; ++e) vo[j][k + e] = v[e];
-            }
-          } else {
-#pragma unroll
-            for (int k = 0; k < PER; ++k) vo[j][k] = load_coherent(vw_o, (row * D + dim(k)) * 4);
-          }
-        }
-      }
-#pragma unroll
-      for (int j = 0; j < KS; ++j) {
-        if (s0 + j >= a.n_splits) break;
-        float s_old, s_new;
-        merge_scales(gm, vm[j], s_old, s_new);
-        gl = gl * s_old + vl[j] * s_new;
-#pragma unroll
-        for (int k = 0; k < PER; ++k) ga[k] = ga[k] * s_old + vo[j][k] * s_new;
-      }
-    }
+    for (int k = 0; k < PER; ++k) o[k] += sc * lds_o[w][row][dim(k)];
+  }
+  __bf16* orow = static_cast<__bf16*>(a.out) + (orow0 + row) * D;
+  if (direct) {
     if (live) {
-      const float inv = gl > 0.f ? 1.f / gl : 0.f;
 #pragma unroll
-      for (int k = 0; k < PER; ++k) orow[dim(k)] = (__bf16)(ga[k] * inv);
-      if (d0 == 0 && a.lse) a.lse[orow0 + row] = gl > 0.f ? (gm + __log2f(gl)) * kLn2 : -INFINITY;
+      for (int k = 0; k < PER; ++k) orow[dim(k)] = (__bf16)(l > 0.f ? o[k] / l : 0.f);
+      if (d0 == 0 && a.lse) a.lse[orow0 + row] = l > 0.f ? (mx + __log2f(l)) * kLn2 : -INFINITY;
     }
+    return;
+  }
+  const __amdgpu_buffer_rsrc_t own_o = coherent_view(wo, SR * D * 4);
+  if constexpr (VEC) {
+#pragma unroll
+    for (int k = 0; k < PER; k += 4)
+      store4_coherent(own_o, (row * D + dim(k)) * 4, f32x4{o[k], o[k + 1], o[k + 2], o[k + 3]});
+  } else {
+#pragma unroll
+    for (int k = 0; k < PER; ++k) store_coherent(wo + row * D + dim(k), o[k]);
+  }
+  if (d0 == 0) {
+    store_coherent(wml + row * 2 + 0, mx);
+    store_coherent(wml + row * 2 + 1, l);
+  }
+  if (!last_arrival(a.arrive + (size_t)unit * a.n_qs + qs, (uint32_t)a.n_splits, a.dev_err))
+    return;
+
+  // Split merge in split order: this work-group's partial is in registers,
+  // the others' are loaded KS splits at a time (all in flight together).
+  constexpr int KS = PER >= 16 ? 2 : (PER >= 8 ? 4 : 8);
+  const size_t part0 = part - split;
+  float gm = -INFINITY, gl = 0.f, ga[PER];
+#pragma unroll
+  for (int k = 0; k < PER; ++k) ga[k] = 0.f;
+  for (int s0 = 0; s0 < a.n_splits; s0 += KS) {
+    float vo[KS][PER], vm[KS], vl[KS];
+#pragma unroll
+    for (int j = 0; j < KS; ++j) {
+      const int s = s0 + j;
+      const bool other = live && s < a.n_splits && s != split;
+      const size_t ps = part0 + (other ? s : split);
+      const __amdgpu_buffer_rsrc_t vw_o = coherent_view(a.ws_o + ps * SR * D, SR * D * 4);
+      const __amdgpu_buffer_rsrc_t vw_ml = coherent_view(a.ws_ml + ps * SR * 2, SR * 2 * 4);
+      vm[j] = mx;
+      vl[j] = l;
+#pragma unroll
+      for (int k = 0; k < PER; ++k) vo[j][k] = o[k];
+      if (other) {
+        vm[j] = load_coherent(vw_ml, row * 8);
+        vl[j] = load_coherent(vw_ml, row * 8 + 4);
+        if constexpr (VEC) {
+#pragma unroll
+          for (int k = 0; k < PER; k += 4) {
+            const f32x4 v = load4_coherent(vw_o, (row * D + dim(k)) * 4);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) vo[j][k + e] = v[e];
+          }
+        } else {
+#pragma unroll
+          for (int k = 0; k < PER; ++k) vo[j][k] = load_coherent(vw_o, (row * D + dim(k)) * 4);
+        }
+      }
+    }
+#pragma unroll
+    for (int j = 0; j < KS; ++j) {
+      if (s0 + j >= a.n_splits) break;
+      float s_old, s_new;
+      merge_scales(gm, vm[j], s_old, s_new);
+      gl = gl * s_old + vl[j] * s_new;
+#pragma unroll
+      for (int k = 0; k < PER; ++k) ga[k] = ga[k] * s_old + vo[j][k] * s_new;
+    }
+  }
+  if (live) {
+    const float inv = gl > 0.f ? 1.f / gl : 0.f;
+#pragma unroll
+    for (int k = 0; k < PER; ++k) orow[dim(k)] = (__bf16)(ga[k] * inv);
+    if (d0 == 0 && a.lse) a.lse[orow0 + row] = gl > 0.f ? (gm + __log2f(gl)) * kLn2 : -INFINITY;
   }
 }
 
@@ -1121,11 +1089,11 @@ AttnPlan plan_attention(int32_t B, int32_t Hkv, int32_t M, int32_t D, int32_t n_
     const long long smin = (nch + per_split - 1) / per_split;
     if (p.n_splits < smin) p.n_splits = (int)smin;
   }
-  // The draft window (a few hundred keys, latency-bound) merges its splits
-  // in the last work-group of each unit; the verify kernels keep the
-  // separate merge kernel (their tails measured no faster fused, and the
-  // extra epilogue code perturbed the tree kernel's main-loop schedule).
-  p.fuse_merge = mfma && p.n_splits > 1 && window;
+  // The streaming kernel (chains, the draft window) merges its splits in the
+  // last work-group of each unit: one launch, 4 us less per 8B/32K call than
+  // the merge kernel.  The tree kernel keeps the merge kernel: the fused
+  // epilogue moved its main-loop schedule (296 -> 354 us at one split).
+  p.fuse_merge = mfma && p.n_splits > 1 && p.tree_waves == 0;
   const long long tiles = units * p.n_splits;
   p.grid = (int)(p.n_qs == 1 ? tiles : ((tiles + 7) / 8) * 8 * p.n_qs);
   const size_t parts = (size_t)tiles * p.n_qs;

@@ -144,13 +144,13 @@ def test_bad_kv_len_sets_error_and_zero_output():
 
 
 def test_workspace_reuse_across_calls():
-    """The draft-window kernel merges its key-range splits in the work-group
-    that finishes a unit last, counted in the workspace.  One zero-filled
-    workspace serves a run of calls in turn (verify chains and a tree at
-    several split counts, window calls) on inputs that change from round to
-    round, so partials left by an earlier call would show: every result
-    matches the oracle, no call reports an error, and the counters are back
-    at zero afterwards."""
+    """The streaming kernel (chains, the draft window) merges its key-range
+    splits in the work-group that finishes a unit last, counted in the
+    workspace.  One zero-filled workspace serves a run of calls in turn
+    (verify chains at several split counts, a tree, window calls) on inputs
+    that change from round to round, so partials left by an earlier call
+    would show: every result matches the oracle, no call reports an error,
+    and the counters are back at zero afterwards."""
     from oracle.attention import window_attention as oracle_window
     from workloads import make_window_inputs
     say("verify workspace reuse")

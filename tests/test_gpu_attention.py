@@ -199,6 +199,29 @@ def test_workspace_reuse_across_calls():
         assert_attention_close(*wout, o_ref, l_ref, torch.bfloat16, "window, reused workspace")
 
 
+def test_interleaved_calls_on_one_workspace_are_bit_stable():
+    """Two inputs alternate for 24 calls on one workspace (the chain call
+    merges its splits through it): every call reproduces, bit for bit, the
+    result of the first call on the same input, so no partial of the other
+    input is ever read."""
+    say("verify interleaved calls on one workspace")
+    L = _lib()
+    B, Hq, Hkv, n_q, D, Lk = 4, 32, 8, 5, 128, 6000
+    xs = [make_attention_inputs(B, Hq, Hkv, n_q, D, Lk, dtype="bf16", seed=90 + i, device=DEV)
+          for i in range(2)]
+    ws = torch.zeros(L.verify_attention_workspace_bytes(B, Hq, Hkv, n_q, D, Lk, torch.bfloat16, 6),
+                     dtype=torch.uint8, device=DEV)
+    err = torch.zeros(1, dtype=torch.int32, device=DEV)
+    outs = [L.verify_attention(x["q"], x["k"], x["v"], x["kv_len"], num_splits=6, workspace=ws,
+                               dev_err=err) for x in xs * 12]
+    torch.cuda.synchronize()
+    assert int(err.item()) == 0
+    for i, (o, l) in enumerate(outs):
+        o0, l0 = outs[i % 2]
+        assert torch.equal(o, o0) and torch.equal(l, l0), f"call {i}"
+    assert not torch.equal(outs[0][0], outs[1][0])
+
+
 def test_unzeroed_workspace_is_reported():
     """Arrival counters that were not zero-filled (the draft window, whose
     splits merge in the last work-group): the call sets SPEC_DEVERR_WORKSPACE

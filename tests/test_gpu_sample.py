@@ -50,6 +50,10 @@ CASES = [
     ("chain_v4096_close", 48, 4, 4096, False, 3.0, 0.05, None),
     ("single_node_bonus", 16, 1, 3000, False, 3.0, 1.0, None),
     ("tree16_v2048", 24, 16, 2048, True, 3.0, 1.0, None),
+    # one sequence, 126 residual groups (two-level arrival, 16 first-level counters)
+    ("b1_chain_v128256", 1, 5, 128256, False, 3.0, 1.0, None),
+    # many sequences, few groups each owning several chunks
+    ("b300_chain_v20000", 300, 3, 20000, False, 3.0, 1.0, None),
 ]
 
 

@@ -631,6 +631,80 @@ __global__ __launch_bounds__(kDecideThreads) void sample_decide_lossless(SampleA
   store_decision(a, b, d);
 }
 
+// E = -ln U of a race uniform in fp32, within 2e-6 relative: the series of
+// -ln(1 - d) near U = 1 (where a logarithm's last-place error would be a
+// large relative error), the hardware logarithm elsewhere.  U is exact in
+// fp32 (a 24-bit odd numerator over 2^24), and so is d = 1 - U.
+__device__ __forceinline__ float race_e32(uint32_t w) {
+  const float u = (float)(2u * (w >> 9) + 1u) * 5.9604644775390625e-08f;
+  const float d = 1.0f - u;
+  if (d < 0.015625f) return d * (1.0f + d * (0.5f + d * (1.0f / 3.0f)));
+  return -__builtin_amdgcn_logf(u) * kLn2;
+}
+
+// The level-2 race among this thread's ids e0 .. e0+3 (logits lt, ld): id x
+// scores w_x / E_x in fp64, with w_x = max(pt - shift pd, 0) when resid, else
+// pt, where pt = exp(lt - lzt), pd = exp(ld - lzd); the block's best goes to
+// (best, bidx), ties to the lowest id.  The fp64 score is taken only for ids
+// whose fp32 upper bound reaches the best fp32 lower bound in the block: the
+// bounds carry the fp32 rounding of the exponent (2e-7 of |logit| + |log
+// normaliser|, plus 2e-6) on pt and pd, of E (2e-6) and of the quotient, ten
+// times over, and 1e-30 for fp32 underflow, so no id left out can win or tie
+// in fp64.  Usually one id per block is scored in fp64.
+__device__ void race_ids(const float (&lt)[4], const float (&ld)[4], const uint32_t (&words)[4],
+                         int e0, int V, double lzt, double lzd, double shift, bool resid,
+                         double& best, int& bidx, double* redd, int* redi) {
+  __shared__ float redf[4];
+  const float lzt_f = (float)lzt, lzd_f = (float)lzd, sh_f = (float)shift;
+  float hi[4], lo_max = 0.f;
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    hi[k] = -1.f;
+    if (e0 + k >= V || lt[k] == -INFINITY) continue;
+    const float pt = fast_exp2((lt[k] - lzt_f) * kLog2e);
+    const float et = 2e-6f * (fabsf(lt[k]) + fabsf(lzt_f)) + 2e-5f;
+    float w = pt, eps = et * pt + 1e-30f;
+    if (resid) {
+      const float pd = ld[k] == -INFINITY ? 0.f : fast_exp2((ld[k] - lzd_f) * kLog2e);
+      const float ed = 2e-6f * (fabsf(ld[k]) + fabsf(lzd_f)) + 2e-5f;
+      w = pt - sh_f * pd;
+      eps += ed * sh_f * pd;
+    }
+    if (!(w + eps > 0.f)) continue;   // no positive weight in fp64 either
+    const float e = race_e32(words[k]);
+    hi[k] = (w + eps) / e * (1.f + 1e-4f);
+    if (w - eps > 0.f) lo_max = fmaxf(lo_max, (w - eps) / e * (1.f - 1e-4f));
+  }
+  const float floor_lo = block_max(lo_max, redf);
+  uint32_t cand = 0;
+#pragma unroll
+  for (int k = 0; k < 4; ++k)
+    if (hi[k] > 0.f && hi[k] >= floor_lo) cand |= 1u << k;
+  while (__any(cand != 0)) {
+    if (cand) {
+      const int k = __builtin_ctz(cand);
+      cand &= cand - 1;
+      float ltk = 0.f, ldk = 0.f;
+      uint32_t wk = 0;
+#pragma unroll
+      for (int q = 0; q < 4; ++q)
+        if (q == k) {
+          ltk = lt[q];
+          ldk = ld[q];
+          wk = words[q];
+        }
+      const double pt = exp((double)ltk - lzt);
+      double wx = pt;
+      if (resid) {
+        const double pd = exp((double)ldk - lzd);
+        wx = pt - shift * pd > 0.0 ? pt - shift * pd : 0.0;
+      }
+      if (wx > 0.0) better(best, bidx, wx / -log(uniform24(wk)), e0 + k);
+    }
+  }
+  block_argmax(best, bidx, redd, redi);
+}
+
 // ---------------------------------------------------------------------------
 // The draw at the stop row and the outputs, run by the last residual
 // work-group of a sequence.  The stop node's decision comes from that
@@ -708,36 +782,23 @@ __device__ void race_emit(const SampleArgs& a, int b, const StopView& sv) {
   uint32_t w0 = (uint32_t)(e0 >> 2), w1 = (uint32_t)r, w2 = (uint32_t)b, w3 = a.ctr3_base + 3u;
   philox4x32_10(w0, w1, w2, w3, a.key0, a.key1);
   const uint32_t words[4] = {w0, w1, w2, w3};
-  double pt[4], wx[4];
+  float lt[4], ld[4];
 #pragma unroll
   for (int k = 0; k < 4; ++k) {
     const int e = e0 + k;
-    pt[k] = 0.0;
-    wx[k] = 0.0;
-    if (e < V) {
-      pt[k] = exp((double)ld1(trow, e) - lzt);
-      wx[k] = pt[k];
-      if (use_resid) {
-        const double pd = exp((double)ld1(drow, e) - lzd);
-        wx[k] = pt[k] - shift * pd > 0.0 ? pt[k] - shift * pd : 0.0;
-      }
-    }
+    lt[k] = e < V ? ld1(trow, e) : -INFINITY;
+    ld[k] = (e < V && use_resid) ? ld1(drow, e) : -INFINITY;
   }
   double best2 = -1.0;
   int bidx2 = 0x7fffffff;
-#pragma unroll
-  for (int k = 0; k < 4; ++k)
-    if (wx[k] > 0.0) better(best2, bidx2, wx[k] / -log(uniform24(words[k])), e0 + k);
-  block_argmax(best2, bidx2, redd, redi);
-  if (bidx2 >= V) {
+  race_ids(lt, ld, words, e0, V, lzt, lzd, use_resid ? shift : 0.0, use_resid, best2, bidx2,
+           redd, redi);
+  if (bidx2 >= V && use_resid) {
     // The fp32 chunk mass was positive but no id of the chunk has a positive
     // fp64 residual (a cancellation at the 1e-7 level): draw from the target.
     best2 = -1.0;
     bidx2 = 0x7fffffff;
-#pragma unroll
-    for (int k = 0; k < 4; ++k)
-      if (pt[k] > 0.0) better(best2, bidx2, pt[k] / -log(uniform24(words[k])), e0 + k);
-    block_argmax(best2, bidx2, redd, redi);
+    race_ids(lt, ld, words, e0, V, lzt, lzd, 0.0, false, best2, bidx2, redd, redi);
   }
   const int y = bidx2 < V ? bidx2 : 0;
 

@@ -54,6 +54,10 @@ CASES = [
     ("b1_chain_v128256", 1, 5, 128256, False, 3.0, 1.0, None),
     # many sequences, few groups each owning several chunks
     ("b300_chain_v20000", 300, 3, 20000, False, 3.0, 1.0, None),
+    # large logits and a draft within 1% of the target: residuals cancel, the
+    # draw's fp32 screen works at its widest error bounds
+    ("chain_sharp_close", 64, 5, 30000, False, 40.0, 0.01, None),
+    ("chain_sharp", 64, 5, 30000, False, 40.0, 2.0, None),
 ]
 
 

@@ -24,6 +24,12 @@ float resolve_scale(float scale, int32_t D) {
   return s * 1.4426950408889634f;  // log2(e): the kernels run their softmax in base 2
 }
 
+// Launch size of an attention plan: at most 2^22 work-groups (of up to 512
+// threads), which keeps every grid and tile index in 32 bits.
+bool grid_fits(int32_t B, int32_t Hkv, const AttnPlan& p) {
+  return (long long)B * Hkv * p.n_splits * p.n_qs <= (1ll << 22);
+}
+
 spec_status_t check_attn_shape(int32_t B, int32_t Hq, int32_t Hkv, int32_t D, spec_dtype_t dtype,
                                int32_t num_splits) {
   if (B < 0 || Hq < 1 || Hkv < 1 || Hq % Hkv) return SPEC_ERR_INVALID_ARG;
@@ -96,7 +102,8 @@ size_t spec_verify_attention_workspace(int32_t B, int32_t Hq, int32_t Hkv, int32
                                        int32_t L_cap, spec_dtype_t dtype, int32_t num_splits) {
   if (verify_shape(B, Hq, Hkv, n_q, D, L_cap, dtype, num_splits) != SPEC_OK) return 0;
   if (B == 0) return 0;
-  return plan_attention(B, Hkv, (Hq / Hkv) * n_q, D, L_cap, dtype, num_splits, false).ws_bytes;
+  const AttnPlan p = plan_attention(B, Hkv, (Hq / Hkv) * n_q, D, L_cap, dtype, num_splits, false);
+  return grid_fits(B, Hkv, p) ? p.ws_bytes : 0;
 }
 
 }  // extern "C"
@@ -151,6 +158,7 @@ spec_status_t verify_call(const void* q, const void* k_cache, const void* v_cach
   const int32_t g = Hq / Hkv;
   const AttnPlan p =
       plan_attention(B, Hkv, g * n_q, D, L_cap, dtype, num_splits, false, pg.page_size);
+  if (!grid_fits(B, Hkv, p)) return SPEC_ERR_UNSUPPORTED;
   if (!aligned(workspace, 256) || workspace_bytes < p.ws_bytes) return SPEC_ERR_WORKSPACE;
 
   AttnArgs a;
@@ -210,8 +218,9 @@ size_t spec_verify_attention_paged_workspace(int32_t B, int32_t Hq, int32_t Hkv,
                                              spec_dtype_t dtype, int32_t num_splits) {
   if (verify_shape(B, Hq, Hkv, n_q, D, L_max, dtype, num_splits) != SPEC_OK || B == 0) return 0;
   if (page_size > (1 << 20) || log2_exact(page_size) < 6) return 0;
-  return plan_attention(B, Hkv, (Hq / Hkv) * n_q, D, L_max, dtype, num_splits, false, page_size)
-      .ws_bytes;
+  const AttnPlan p =
+      plan_attention(B, Hkv, (Hq / Hkv) * n_q, D, L_max, dtype, num_splits, false, page_size);
+  return grid_fits(B, Hkv, p) ? p.ws_bytes : 0;
 }
 
 spec_status_t spec_verify_attention_paged(
@@ -230,7 +239,8 @@ spec_status_t spec_verify_attention_paged(
 size_t spec_window_attention_workspace(int32_t B, int32_t Hq, int32_t Hkv, int32_t D, int32_t W,
                                        int32_t S, spec_dtype_t dtype, int32_t num_splits) {
   if (window_shape(B, Hq, Hkv, D, W, S, dtype, num_splits) != SPEC_OK || B == 0) return 0;
-  return plan_attention(B, Hkv, Hq / Hkv, D, W + S, dtype, num_splits, true).ws_bytes;
+  const AttnPlan p = plan_attention(B, Hkv, Hq / Hkv, D, W + S, dtype, num_splits, true);
+  return grid_fits(B, Hkv, p) ? p.ws_bytes : 0;
 }
 
 spec_status_t spec_window_attention(const void* q, void* k_ring, void* v_ring, void* k_sink,
@@ -251,6 +261,7 @@ spec_status_t spec_window_attention(const void* q, void* k_ring, void* v_ring, v
   if (S > 0 && (!aligned(k_sink, 16) || !aligned(v_sink, 16))) return SPEC_ERR_MISALIGNED;
   const int32_t g = Hq / Hkv;
   const AttnPlan p = plan_attention(B, Hkv, g, D, W + S, dtype, num_splits, true);
+  if (!grid_fits(B, Hkv, p)) return SPEC_ERR_UNSUPPORTED;
   if (!aligned(workspace, 256) || workspace_bytes < p.ws_bytes) return SPEC_ERR_WORKSPACE;
 
   AttnArgs a;

@@ -64,6 +64,8 @@ def test_verify_attention_argument_checks():
     assert _verify(k=NULL) == MISALIGNED
     assert _verify(ws_bytes=16) == WORKSPACE       # far below the planned workspace
     assert _verify(ws=P_ODD, ws_bytes=1 << 40) == WORKSPACE
+    # more than 2^22 work-groups: refused before the workspace is looked at
+    assert _verify(B=4096, Hq=64, Hkv=64, L_cap=1 << 20, splits=65536) == UNSUPPORTED
 
 
 def test_workspace_queries():
@@ -77,6 +79,11 @@ def test_workspace_queries():
     assert L.window_attention_workspace_bytes(8, 32, 8, 128, 512, 4, bf16) > 0
     assert L.sample_workspace_bytes(8, 5, 128256) > 0
     assert L.sample_workspace_bytes(8, 0, 128256) == 0
+    # More than 2^22 work-groups: refused (a zero size here, UNSUPPORTED at the call).
+    assert L.verify_attention_workspace_bytes(4096, 64, 64, 5, 128, 1 << 20, bf16,
+                                              num_splits=65536) == 0
+    assert L.window_attention_workspace_bytes(8192, 64, 64, 128, 512, 4, bf16,
+                                              num_splits=65536) == 0
 
 
 def _paged(B=2, P_size=64, stride=16, num_pages=40, bt=P, kv_len=P, L_max=1000, ws_bytes=0):

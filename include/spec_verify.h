@@ -122,7 +122,9 @@ typedef enum {
  *            forests are allowed.
  *   n_q      1 .. SPEC_MAX_NQ;  D in {64, 128};  Hq % Hkv == 0;  L_cap >= n_q.
  *   scale    softmax scale; <= 0 selects 1/sqrt(D).
- *   num_splits  key-range splits per (sequence, kv head); 0 = automatic.
+ *   num_splits  key-range splits per (sequence, kv head); 0 = automatic.  A
+ *               launch of more than 2^22 work-groups (B * Hkv * splits * row
+ *               slices) returns SPEC_ERR_UNSUPPORTED.
  *   workspace   at least spec_verify_attention_workspace(...) bytes,
  *               zero-filled before its first use (see Workspace above).
  * Returns SPEC_OK or an error status (nothing launched on error).
@@ -206,6 +208,7 @@ size_t spec_verify_attention_paged_workspace(int32_t B, int32_t Hq, int32_t Hkv,
  *   total_len [B] int32 (>= 1)
  *   out      [B, Hq, 1, D] dtype;  lse [B, Hq, 1] f32 nullable
  *   W >= 1, S >= 0, D in {64, 128}, Hq % Hkv == 0.
+ *   num_splits, workspace: as in spec_verify_attention.
  */
 spec_status_t spec_window_attention(const void* q, void* k_ring, void* v_ring, void* k_sink,
                                     void* v_sink, const void* k_new, const void* v_new,

@@ -74,6 +74,18 @@ def test_tree_parity(dt):
     assert_attention_close(out, lse, o_ref, l_ref, x["q"].dtype, f"tree {dt}")
 
 
+@pytest.mark.parametrize("Hq,Hkv,n_q,D", [(64, 2, 1, 128), (32, 8, 4, 64), (64, 8, 4, 64),
+                                           (16, 16, 3, 128)])
+def test_chain_split_merge_shapes(Hq, Hkv, n_q, D):
+    """The chain kernel's in-kernel split merge at every epilogue shape:
+    16- and 32-row slices, head dim 64 and 128, several splits."""
+    say(f"verify merge shapes Hq={Hq} Hkv={Hkv} n_q={n_q} D={D}")
+    x = make_attention_inputs(2, Hq, Hkv, n_q, D, 2500, dtype="bf16", seed=Hq + n_q + D,
+                              device=DEV, kv_len=[2500, 1111])
+    out, lse, o_ref, l_ref = _gpu_and_oracle(x, num_splits=5)
+    assert_attention_close(out, lse, o_ref, l_ref, torch.bfloat16, f"{Hq}/{Hkv}/{n_q}/{D}")
+
+
 def test_tree_per_sequence_parent_and_forest():
     say("verify per-sequence parents incl. forest")
     n = 17

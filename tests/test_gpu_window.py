@@ -87,6 +87,18 @@ def test_window_split_independence(splits):
     assert_attention_close(out, lse, o_ref, l_ref, torch.bfloat16, f"splits={splits}")
 
 
+@pytest.mark.parametrize("Hq,Hkv,D", [(64, 2, 128), (64, 2, 64), (16, 4, 64), (8, 8, 128)])
+def test_window_split_merge_shapes(Hq, Hkv, D):
+    """Every epilogue shape of the in-kernel split merge: 16- and 32-row query
+    slices (g <= 16 and g = 32), head dim 64 and 128, three splits."""
+    say(f"window merge shapes Hq={Hq} Hkv={Hkv} D={D}")
+    B, W, S = 3, 200, 4
+    x = make_window_inputs(B, Hq, Hkv, D, W, S, [1000, 150, 2], dtype="bf16",
+                           seed=Hq * 1000 + Hkv * 10 + D, device=DEV)
+    out, lse, o_ref, l_ref = _run(x, B, Hq, Hkv, D, W, S, num_splits=3)
+    assert_attention_close(out, lse, o_ref, l_ref, torch.bfloat16, f"{Hq}/{Hkv}/{D}")
+
+
 def test_window_bad_total_len_flags_error():
     import long_context_verify_amd as L
     say("window total_len 0")

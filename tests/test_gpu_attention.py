@@ -86,6 +86,33 @@ def test_chain_split_merge_shapes(Hq, Hkv, n_q, D):
     assert_attention_close(out, lse, o_ref, l_ref, torch.bfloat16, f"{Hq}/{Hkv}/{n_q}/{D}")
 
 
+WIDE = [
+    # name, B, Hq, Hkv, n_q, D, L, tree, splits, kv_len
+    # two 256-row slices of the LDS-shared kernel (g = 8, 64 nodes)
+    ("tree64_g8_two_slices", 2, 64, 8, 64, 128, 1500, True, 0, [1500, 700]),
+    ("tree64_g8_two_slices_s3", 2, 64, 8, 64, 128, 1500, True, 3, [1500, 64]),
+    # the longest chain (n_q = 64, g = 1): two live waves of the wide kernel
+    ("chain_nq64_g1", 2, 8, 8, 64, 128, 2000, False, 0, [2000, 90]),
+    # a wide block at D = 64 goes to the streaming kernel, eight 32-row slices
+    ("tree64_d64_eight_slices", 2, 32, 8, 64, 64, 1200, True, 0, [1200, 333]),
+    # a row count that leaves the last wave partly empty
+    ("tree50_g4_M200", 3, 4, 1, 50, 128, 900, True, 2, [900, 50, 51]),
+]
+
+
+@pytest.mark.parametrize("case", WIDE, ids=[c[0] for c in WIDE])
+def test_wide_query_blocks(case):
+    """Query blocks at and past one wide slice: every row of every slice
+    against the oracle, ragged lengths down to the block itself."""
+    name, B, Hq, Hkv, n_q, D, L, tree, splits, kv_len = case
+    say(f"verify wide {name}")
+    parent = random_tree(n_q, seed=n_q + Hq) if tree else None
+    x = make_attention_inputs(B, Hq, Hkv, n_q, D, L, dtype="bf16", seed=sum(map(ord, name)),
+                              device=DEV, kv_len=kv_len)
+    out, lse, o_ref, l_ref = _gpu_and_oracle(x, parent=parent, num_splits=splits)
+    assert_attention_close(out, lse, o_ref, l_ref, torch.bfloat16, name)
+
+
 def test_tree_per_sequence_parent_and_forest():
     say("verify per-sequence parents incl. forest")
     n = 17

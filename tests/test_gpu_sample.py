@@ -210,6 +210,27 @@ def test_sample_full_size_lossless_tree():
     _compare(g, o, "medusa_tree64_8k lossless")
 
 
+@pytest.mark.parametrize("rule", ["first", "lossless"])
+def test_sample_max_nodes(rule):
+    """The node limit: a 256-node tree (depth 8, up to 8 children), and a
+    256-node chain whose drafts track the target closely, so accepted paths
+    run long."""
+    N = 256
+    say(f"sample max nodes {rule}")
+    parent = random_tree(N, max_depth=8, max_children=8, seed=256)
+    x = make_sample_inputs(6, N, 3000, parent, 3.0, draft_noise_std=0.3, seed=2560, device=DEV)
+    g = _gpu(x, parent, 0xA11, 1, siblings=rule)
+    o = oracle_sample(x["target"], x["draft"], x["tokens"], parent, seed=0xA11, offset=1,
+                      siblings=rule)
+    _compare(g, o, f"tree {N} {rule}")
+    x = make_sample_inputs(4, N, 2000, None, 3.0, draft_noise_std=0.02, seed=2561, device=DEV)
+    g = _gpu(x, None, 0xA12, 2, siblings=rule)
+    o = oracle_sample(x["target"], x["draft"], x["tokens"], None, seed=0xA12, offset=2,
+                      siblings=rule)
+    _compare(g, o, f"chain {N} {rule}")
+    assert g["out_count"].max() > 8
+
+
 def test_equal_distributions_accept_all():
     say("sample equal distributions")
     B, N, V = 64, 5, 3000

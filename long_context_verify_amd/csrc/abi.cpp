@@ -350,6 +350,7 @@ spec_status_t sample_call(const void* target_logits, const void* draft_logits,
   a.arrive = reinterpret_cast<uint32_t*>(ws);
   a.part_m = reinterpret_cast<float*>(ws + p.off_m);
   a.part_s = reinterpret_cast<double*>(ws + p.off_s);
+  a.tok_logit = reinterpret_cast<float*>(ws + p.off_g);
   a.race_w = reinterpret_cast<double*>(ws + p.off_w);
   a.decision = reinterpret_cast<int32_t*>(ws + p.off_dec);
   a.decision_lz = reinterpret_cast<double*>(ws + p.off_lz);

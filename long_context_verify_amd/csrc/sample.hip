@@ -191,6 +191,18 @@ __global__ __launch_bounds__(kSampleThreads) void sample_stats(SampleArgs a) {
   }
   const T* row = static_cast<const T*>(kind ? a.draft : a.target) + ((size_t)b * a.N + u) * a.V;
   const int x0 = chunk * a.vchunk;
+  // The drafted tokens of u's children that fall in this chunk: their logits
+  // in this row go to the workspace, so the decision reads them in the same
+  // round as the row statistics (N <= threads: one child per thread).
+  static_assert(SPEC_MAX_SAMPLE_NODES <= kSampleThreads + 1, "one child per thread");
+  {
+    const int c = 1 + threadIdx.x;
+    if (c < a.N && parent_of(a, b, c) == u) {
+      const int xc = a.tokens[(size_t)b * a.N + c];
+      if (xc >= x0 && xc < x0 + a.vchunk && xc < a.V)
+        a.tok_logit[((size_t)b * 2 + kind) * a.N + c] = ld1(row, xc);
+    }
+  }
   constexpr int PER = kStatsChunk / kSampleThreads;  // 32
   float x[PER];
   if (VEC4) {
@@ -277,17 +289,27 @@ __device__ void decide_sequence(const SampleArgs& a, int b, Decision& d,
   const int N = a.N, V = a.V;
   const int tid = threadIdx.x;
 
-  // Drafted-token logits at each node's parent: issue these loads first.
+  // One round of loads: the drafted tokens, their logits at the parent
+  // (gathered by the stats kernel; valid wherever the token and parent are),
+  // and this thread's first row partial of the fold below.
+  const int nv = a.n_vchunks;
+  const int GL = nv >= 64 ? 64 : (nv > 32 ? 64 : nv > 16 ? 32 : nv > 8 ? 16 : nv > 4 ? 8 : 4);
+  const int rows_per_pass = NT / GL;
+  float pm0 = -INFINITY;
+  double ps0 = 0.0;
+  if (tid / GL < 2 * N && tid % GL < nv) {
+    const size_t o = ((size_t)b * 2 * N + tid / GL) * nv + tid % GL;
+    pm0 = a.part_m[o];
+    ps0 = a.part_s[o];
+  }
   float tl = 0.f, dl = 0.f;
   int x = 0, p = -1;
   const int c_tok = 1 + tid;
   if (c_tok < N) {
     p = parent_of(a, b, c_tok);
     x = a.tokens[(size_t)b * N + c_tok];
-    if (p >= 0 && p < c_tok && x >= 0 && x < V) {
-      tl = ld1(static_cast<const T*>(a.target), ((size_t)b * N + p) * V + x);
-      dl = ld1(static_cast<const T*>(a.draft), ((size_t)b * N + p) * V + x);
-    }
+    tl = a.tok_logit[(size_t)b * 2 * N + c_tok];
+    dl = a.tok_logit[((size_t)b * 2 + 1) * N + c_tok];
   }
   if (tid == 0) d.bad = 0;
   for (int u = tid; u < N; u += NT) d.has_child[u] = 0;
@@ -305,10 +327,7 @@ __device__ void decide_sequence(const SampleArgs& a, int b, Decision& d,
   const bool bad_tree = d.bad != 0;
 
   // Fold the per-chunk partials of every needed row: GL lanes per row, all
-  // rows side by side, so the partials arrive in one round.
-  const int nv = a.n_vchunks;
-  const int GL = nv >= 64 ? 64 : (nv > 32 ? 64 : nv > 16 ? 32 : nv > 8 ? 16 : nv > 4 ? 8 : 4);
-  const int rows_per_pass = NT / GL;
+  // rows side by side (the first partial of each lane was loaded above).
   for (int base = 0; base < 2 * N; base += rows_per_pass) {
     const int rs = base + tid / GL;
     const int k0 = tid % GL;
@@ -320,13 +339,14 @@ __device__ void decide_sequence(const SampleArgs& a, int b, Decision& d,
     double sk = 0.0;
     float m = -INFINITY;
     if (need)
-      for (int k = k0; k < nv; k += GL) m = fmaxf(m, a.part_m[o + k]);
+      for (int k = k0; k < nv; k += GL) m = fmaxf(m, (base == 0 && k == k0) ? pm0 : a.part_m[o + k]);
     for (int off = GL >> 1; off >= 1; off >>= 1) m = fmaxf(m, __shfl_xor(m, off));
     double sum = 0.0;
     if (need && m != -INFINITY)
       for (int k = k0; k < nv; k += GL) {
-        mk = a.part_m[o + k];
-        sk = a.part_s[o + k];
+        const bool first = base == 0 && k == k0;
+        mk = first ? pm0 : a.part_m[o + k];
+        sk = first ? ps0 : a.part_s[o + k];
         if (mk != -INFINITY) sum += sk * exp((double)mk - (double)m);
       }
     for (int off = GL >> 1; off >= 1; off >>= 1) sum += __shfl_xor(sum, off);
@@ -971,7 +991,8 @@ SamplePlan plan_sample(int32_t B, int32_t N, int32_t V) {
   const size_t rows = (size_t)B * 2 * N * p.n_vchunks;
   p.off_m = align256((size_t)B * kArriveStride * sizeof(uint32_t));
   p.off_s = align256(p.off_m + rows * sizeof(float));
-  p.off_w = align256(p.off_s + rows * sizeof(double));
+  p.off_g = align256(p.off_s + rows * sizeof(double));
+  p.off_w = align256(p.off_g + (size_t)B * 2 * N * sizeof(float));
   p.off_dec = align256(p.off_w + (size_t)B * p.n_race * 2 * sizeof(double));
   p.off_lz = align256(p.off_dec + (size_t)B * p.dec_stride * sizeof(int32_t));
   p.bytes = align256(p.off_lz + (size_t)B * kDecisionDoubles * sizeof(double));

@@ -89,6 +89,8 @@ struct SampleArgs {
   uint32_t* arrive;        // [B][..] arrival counters of the residual work-groups
   float* part_m;           // [B][2N][n_vchunks]
   double* part_s;          // [B][2N][n_vchunks]
+  float* tok_logit;        // [B][2][N]: logit of node c's drafted token in its parent's
+                           // target (0) and draft (1) row, gathered by the stats kernel
   double* race_w;          // [B][n_race][2]  (residual mass, target mass) per race chunk
   int32_t* decision;       // [B][dec_stride]: len, error, residual flag, -, path[N], accept[N]
   double* decision_lz;     // [B][kDecisionDoubles]: stop row's log normalisers (target,
@@ -107,7 +109,7 @@ constexpr int kDecisionDoubles = 8;
 
 struct SamplePlan {
   int32_t n_vchunks, vchunk, n_race, n_groups, dec_stride;
-  size_t off_m, off_s, off_w, off_dec, off_lz, bytes;   // arrival counters at offset 0
+  size_t off_m, off_s, off_g, off_w, off_dec, off_lz, bytes;   // arrival counters at offset 0
 };
 
 SamplePlan plan_sample(int32_t B, int32_t N, int32_t V);

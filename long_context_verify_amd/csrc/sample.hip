@@ -191,17 +191,14 @@ __global__ __launch_bounds__(kSampleThreads) void sample_stats(SampleArgs a) {
   }
   const T* row = static_cast<const T*>(kind ? a.draft : a.target) + ((size_t)b * a.N + u) * a.V;
   const int x0 = chunk * a.vchunk;
-  // The drafted tokens of u's children that fall in this chunk: their logits
-  // in this row go to the workspace, so the decision reads them in the same
-  // round as the row statistics (N <= threads: one child per thread).
+  // Node c = 1 + thread (N <= threads): its parent and drafted token, loaded
+  // ahead of the row so that their use below waits for nothing else.
   static_assert(SPEC_MAX_SAMPLE_NODES <= kSampleThreads + 1, "one child per thread");
-  {
-    const int c = 1 + threadIdx.x;
-    if (c < a.N && parent_of(a, b, c) == u) {
-      const int xc = a.tokens[(size_t)b * a.N + c];
-      if (xc >= x0 && xc < x0 + a.vchunk && xc < a.V)
-        a.tok_logit[((size_t)b * 2 + kind) * a.N + c] = ld1(row, xc);
-    }
+  const int c = 1 + threadIdx.x;
+  int pc = -1, xc = -1;
+  if (c < a.N) {
+    pc = parent_of(a, b, c);
+    xc = a.tokens[(size_t)b * a.N + c];
   }
   constexpr int PER = kStatsChunk / kSampleThreads;  // 32
   float x[PER];
@@ -221,6 +218,12 @@ __global__ __launch_bounds__(kSampleThreads) void sample_stats(SampleArgs a) {
       x[i] = e < a.V ? ld1(row, e) : -INFINITY;
     }
   }
+  // The drafted tokens of u's children that fall in this chunk: their logits
+  // in this row go to the workspace (stored at the end, so the load is not
+  // waited for), and the decision reads them in the same round as the row
+  // statistics.
+  const bool gather = pc == u && xc >= x0 && xc < x0 + a.vchunk && xc < a.V;
+  const float xlogit = gather ? ld1(row, xc) : 0.f;
   float mx = x[0];
 #pragma unroll
   for (int i = 1; i < PER; ++i) mx = fmaxf(mx, x[i]);
@@ -236,6 +239,7 @@ __global__ __launch_bounds__(kSampleThreads) void sample_stats(SampleArgs a) {
     a.part_m[o] = mx;
     a.part_s[o] = tot;
   }
+  if (gather) a.tok_logit[((size_t)b * 2 + kind) * a.N + c] = xlogit;
 }
 
 // ---------------------------------------------------------------------------

@@ -118,10 +118,16 @@ def _workspace(nbytes: int, device, workspace: Optional[torch.Tensor]):
     """A caller's workspace (zero-filled before its first use, then reusable
     by any later call on the same stream), or a fresh zero-filled one."""
     if workspace is not None:
-        if workspace.numel() * workspace.element_size() < nbytes:
+        if not workspace.is_cuda or not workspace.is_contiguous():
+            raise ValueError("workspace must be a contiguous tensor on a HIP device")
+        if _nbytes(workspace) < nbytes:
             raise ValueError("workspace too small")
         return workspace
     return torch.zeros(max(int(nbytes), 256), dtype=torch.uint8, device=device)
+
+
+def _nbytes(t: torch.Tensor) -> int:
+    return t.numel() * t.element_size()
 
 
 def _parent_arg(parent, B, n, device):
@@ -168,7 +174,7 @@ def verify_attention(q, k_cache, v_cache, kv_len=None, parent=None, scale: float
     st = lib().spec_verify_attention(
         _p(q), _p(k_cache), _p(v_cache), _p(out), _p(lse), _p(kv_len), _p(par), pstride,
         B, Hq, Hkv, n_q, D, L_cap, _DTYPES[q.dtype], float(scale), int(num_splits), _p(ws),
-        ws.numel(), _p(dev_err), _stream(dev))
+        _nbytes(ws), _p(dev_err), _stream(dev))
     _check(st, "spec_verify_attention")
     return out, lse
 
@@ -207,7 +213,7 @@ def verify_attention_paged(q, k_pages, v_pages, block_table, kv_len, L_max: int,
     st = lib().spec_verify_attention_paged(
         _p(q), _p(k_pages), _p(v_pages), _p(block_table), int(block_table.shape[1]), num_pages, P,
         _p(out), _p(lse), _p(kv_len), _p(par), pstride, B, Hq, Hkv, n_q, D, int(L_max),
-        _DTYPES[q.dtype], float(scale), int(num_splits), _p(ws), ws.numel(), _p(dev_err),
+        _DTYPES[q.dtype], float(scale), int(num_splits), _p(ws), _nbytes(ws), _p(dev_err),
         _stream(dev))
     _check(st, "spec_verify_attention_paged")
     return out, lse
@@ -237,7 +243,7 @@ def window_attention(q, k_ring, v_ring, k_sink, v_sink, total_len, k_new=None, v
     st = lib().spec_window_attention(
         _p(q), _p(k_ring), _p(v_ring), _p(k_sink), _p(v_sink), _p(k_new), _p(v_new), _p(tl),
         _p(out), _p(lse), B, Hq, Hkv, D, W, S, _DTYPES[q.dtype], float(scale), int(num_splits),
-        _p(ws), ws.numel(), _p(dev_err), _stream(dev))
+        _p(ws), _nbytes(ws), _p(dev_err), _stream(dev))
     _check(st, "spec_window_attention")
     return out, lse
 
@@ -275,7 +281,7 @@ def spec_sample(target_logits, draft_logits, tokens, parent=None, seed: int = 0,
     par, pstride = _parent_arg(parent, B, N, dev)
     ws = _workspace(sample_workspace_bytes(B, N, V), dev, workspace)
     args = (_p(tokens), _p(par), pstride, B, N, V, int(seed) & (2**64 - 1), int(offset),
-            _p(out_tokens), _p(out_count), _p(out_path), _p(out_accept), _p(ws), ws.numel(),
+            _p(out_tokens), _p(out_count), _p(out_path), _p(out_accept), _p(ws), _nbytes(ws),
             _p(dev_err), _stream(dev))
     if siblings == "lossless":
         st = lib().spec_sample_ex(_p(target_logits), _p(draft_logits),
@@ -320,7 +326,7 @@ def draft_sample(draft_logits, node: int, seed: int = 0, offset: int = 0, out_to
         _p(draft_logits), _DTYPES[draft_logits.dtype], int(draft_logits.stride(0)) if B > 1 else V,
         B, V,
         int(seed) & (2**64 - 1), int(offset), int(node), _p(out_token),
-        int(out_token.stride(0)) if B > 1 else 1, _p(out_logprob), _p(ws), ws.numel(),
+        int(out_token.stride(0)) if B > 1 else 1, _p(out_logprob), _p(ws), _nbytes(ws),
         _p(dev_err), _stream(dev))
     _check(st, "spec_draft_sample")
     return out_token, out_logprob

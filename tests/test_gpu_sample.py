@@ -231,6 +231,26 @@ def test_sample_max_nodes(rule):
     assert g["out_count"].max() > 8
 
 
+@pytest.mark.parametrize("V", [1, 2, 3])
+def test_sample_tiny_vocabularies(V):
+    """V = 1: both distributions are the same point mass, so every draft is
+    accepted and every token is 0.  V = 2, 3: parity with the oracle, chain
+    and tree."""
+    say(f"sample V={V}")
+    for parent, N in ((None, 5), (random_tree(9, max_depth=3, max_children=3, seed=3), 9)):
+        x = make_sample_inputs(32, N, V, parent, 2.0, draft_noise_std=1.0, seed=V * 7 + N,
+                               device=DEV)
+        for rule in ("first", "lossless"):
+            g = _gpu(x, parent, 0xABC + V, 1, siblings=rule)
+            o = oracle_sample(x["target"], x["draft"], x["tokens"], parent, seed=0xABC + V,
+                              offset=1, siblings=rule)
+            _compare(g, o, f"V={V} N={N} {rule}")
+            if V == 1:
+                assert np.all(g["out_tokens"][g["out_tokens"] >= 0] == 0)
+                if parent is None:
+                    assert np.all(g["out_count"] == N)
+
+
 def test_equal_distributions_accept_all():
     say("sample equal distributions")
     B, N, V = 64, 5, 3000

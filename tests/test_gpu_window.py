@@ -99,6 +99,23 @@ def test_window_split_merge_shapes(Hq, Hkv, D):
     assert_attention_close(out, lse, o_ref, l_ref, torch.bfloat16, f"{Hq}/{Hkv}/{D}")
 
 
+@pytest.mark.parametrize("dt", ["bf16", "f32"])
+@pytest.mark.parametrize("W,S", [(1, 0), (1, 4), (2, 1)])
+def test_window_degenerate_sizes(dt, W, S):
+    """A one- or two-slot ring, with and without sinks, from the first token
+    to well past the wrap-around, plain and with the fused append."""
+    name = f"W{W}_S{S}_{dt}"
+    say(f"window degenerate {name}")
+    T = [1, 2, 3, 5, 6, 37]
+    x = make_window_inputs(len(T), 8, 2, 64, W, S, T, dtype=dt, seed=W * 10 + S, device=DEV)
+    out, lse, o_ref, l_ref = _run(x, len(T), 8, 2, 64, W, S)
+    assert_attention_close(out, lse, o_ref, l_ref, x["q"].dtype, name)
+    x = make_window_inputs(len(T), 8, 2, 64, W, S, T, dtype=dt, seed=W * 10 + S + 1, device=DEV,
+                           fused_append=True)
+    out, lse, o_ref, l_ref = _run(x, len(T), 8, 2, 64, W, S, fused=True)
+    assert_attention_close(out, lse, o_ref, l_ref, x["q"].dtype, name + " fused")
+
+
 def test_window_bad_total_len_flags_error():
     import long_context_verify_amd as L
     say("window total_len 0")

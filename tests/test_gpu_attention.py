@@ -278,6 +278,25 @@ def test_unzeroed_workspace_is_reported():
     assert int(err.item()) == 0x80
 
 
+@pytest.mark.parametrize("L,n_q,tree", [(262144, 5, False), (65536, 64, True)])
+def test_longest_contexts(L, n_q, tree):
+    """256K keys (a 512 MB unit stride, 32 splits per unit) and a 64-node tree
+    at 64K, one sequence, ragged against the capacity: every unit against the
+    oracle."""
+    say(f"verify long context L={L} n_q={n_q}")
+    B, Hq, Hkv, D = 1, 32, 8, 128
+    x = make_attention_inputs(B, Hq, Hkv, n_q, D, L - 123, dtype="bf16", seed=L % 997 + n_q,
+                              device=DEV, L_cap=L)
+    parent = random_tree(n_q, seed=64) if tree else None
+    out, lse = _lib().verify_attention(x["q"], x["k"], x["v"], x["kv_len"], parent=parent)
+    torch.cuda.synchronize()
+    g = Hq // Hkv
+    for hk in range(Hkv):
+        o_ref, l_ref = oracle_unit(x["q"], x["k"], x["v"], x["kv_len"], parent, 0, hk, g)
+        assert_attention_close(out[:, hk * g:(hk + 1) * g], lse[:, hk * g:(hk + 1) * g], o_ref,
+                               l_ref, torch.bfloat16, f"L={L} unit {hk}")
+
+
 FULL = ["llama8b_32k_chain", "magicdec_128k_chain", "medusa_tree64_8k", "llama70b_16k_chain_b64"]
 
 

@@ -58,6 +58,8 @@ CASES = [
     # draw's fp32 screen works at its widest error bounds
     ("chain_sharp_close", 64, 5, 30000, False, 40.0, 0.01, None),
     ("chain_sharp", 64, 5, 30000, False, 40.0, 2.0, None),
+    # a vocabulary one id past a multiple of four at full size: the scalar paths
+    ("b8_chain_v128257_scalar", 8, 5, 128257, False, 3.0, 1.0, None),
 ]
 
 

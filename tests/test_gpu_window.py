@@ -116,6 +116,16 @@ def test_window_degenerate_sizes(dt, W, S):
     assert_attention_close(out, lse, o_ref, l_ref, x["q"].dtype, name + " fused")
 
 
+def test_window_wide_ring():
+    """A 4096-slot ring (129 chunks: many splits per unit) at 100K tokens."""
+    say("window W=4096")
+    B, Hq, Hkv, D, W, S = 2, 32, 8, 128, 4096, 4
+    x = make_window_inputs(B, Hq, Hkv, D, W, S, [100000, 2000], dtype="bf16", seed=4096,
+                           device=DEV)
+    out, lse, o_ref, l_ref = _run(x, B, Hq, Hkv, D, W, S)
+    assert_attention_close(out, lse, o_ref, l_ref, torch.bfloat16, "W=4096")
+
+
 def test_window_bad_total_len_flags_error():
     import long_context_verify_amd as L
     say("window total_len 0")

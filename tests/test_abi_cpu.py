@@ -204,3 +204,33 @@ def test_validate_tree(parent, single, expect):
 
 def test_validate_tree_null():
     assert L.lib().spec_validate_tree(NULL, 3, 1) == INVALID
+
+
+def test_binding_refuses_host_tensors():
+    """No CPU fallback: every entry point refuses tensors that are not on a
+    HIP device before any library call."""
+    q = torch.zeros(1, 4, 5, 64, dtype=torch.bfloat16)
+    k = torch.zeros(1, 1, 64, 64, dtype=torch.bfloat16)
+    with pytest.raises(ValueError, match="HIP device"):
+        L.verify_attention(q, k, k)
+    with pytest.raises(ValueError, match="HIP device"):
+        L.window_attention(q[:, :, :1], k, k, k[:, :, :4], k[:, :, :4], [10])
+    logits = torch.zeros(2, 5, 100)
+    with pytest.raises(ValueError, match="HIP device"):
+        L.spec_sample(logits, logits, torch.zeros(2, 5, dtype=torch.int32))
+    with pytest.raises(ValueError, match="HIP device"):
+        L.draft_sample(logits[:, 0], node=1)
+    with pytest.raises(ValueError, match="HIP device"):
+        L.kv_commit(k, k, torch.zeros(1, dtype=torch.int32), torch.ones(1, dtype=torch.int32), 5)
+
+
+def test_bench_refuses_more_than_one_gpu():
+    """The measured path is one GPU's: --gpus N > 1 exits with a message and
+    touches no device."""
+    import subprocess
+    import sys
+    root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+    r = subprocess.run([sys.executable, os.path.join(root, "bench.py"), "--gpus", "2"],
+                       capture_output=True, text=True, timeout=120, cwd=root)
+    assert r.returncode != 0
+    assert "one GPU" in (r.stdout + r.stderr)

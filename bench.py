@@ -1,30 +1,46 @@
 #!/usr/bin/env python3
 """Benchmark of one speculative verification step on one MI355X.
 
-A step is one pass of the whole hot path over one batch of synthetic input,
-shaped like an 8B-class GQA layer at 32K context (batch 8, 32 query heads,
-8 KV heads, head dim 128, bf16, gamma = 4):
+A step is one pass of the whole hot path over one batch of synthetic input.
+The default workload is the largest one that fits one GPU, a 70B-class GQA
+layer at high batch (batch 64, 64 query heads, 8 KV heads, head dim 128,
+bf16, 16384-token context, gamma = 3; 4 GiB of K/V):
 
-  1. spec_verify_attention  the gamma+1 = 5 block queries of every sequence
-                            against its 32768-token KV cache (causal chain);
+  1. spec_verify_attention  the gamma+1 = 4 block queries of every sequence
+                            against its KV cache (causal chain);
   2. spec_window_attention  one draft-step query against 4 sink tokens and a
-                            512-slot ring (the MagicDec bounded draft cache);
+                            W-slot ring (only workloads that have a draft
+                            window: the 8B/32K and 128K shapes);
   3. spec_sample            acceptance test + residual/bonus draw over a
-                            128256-token vocabulary (5 target rows, 4 draft rows
-                            per sequence).
+                            128256-token vocabulary (4 target rows and 3 draft
+                            rows per sequence at the default).
 
-All inputs are resident in HBM before the timed region.  The printed value
-is verified draft tokens per second (batch * gamma per step).  Per-op times
-come from HIP events recorded on the stream the library launches on (torch's
-current stream); besides the three step ops they cover the calls on either
-side of the step, spec_draft_sample (one draft-step draw) and spec_kv_commit
-(keeping the accepted path), which are not part of the step.  The oracle
-(fp64 numpy) is timed on a bounded sample of the same workload on the host
-cores and reported as ``cpu_baseline``.
+All inputs are resident in HBM before the timed region.  The printed value is
+verified draft tokens per second (batch * gamma per step, host clock around K
+back-to-back steps).  Each step's verify call streams more than the 256 MB
+Infinity Cache (537 MB to 4 GiB of K/V), so every step meets its sampling
+logits in HBM, not in the cache.
+
+Per-op device times come from HIP events on the stream the library launches
+on (torch's current stream), with all calls queued behind a GPU sleep so host
+launch latency cannot leak in:
+
+* ops whose inputs exceed 768 MB: K back-to-back calls between one pair of
+  events;
+* smaller ops: K calls back to back (``us_warm``: their inputs may sit in the
+  Infinity Cache), and K calls each preceded by a 512 MB read of an unrelated
+  buffer, minus K such reads alone (``us``: inputs from HBM).
+
+Also reported: the fraction of a stream-copy rate measured in the same run,
+the other workloads' verify and sampling figures (``workloads``), the draft
+window's cost against the context length next to full-cache n_q = 1 attention
+(``window_scaling``), and the fp64 oracle timed on a bounded sample of the
+headline workload on the host cores (``cpu_baseline``).
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
                        [--page-size P] [--logits f32|bf16] [--siblings first|lossless]
                        [--cpu-budget SECONDS] [--copy-probe-mib MIB]
+                       [--no-others] [--no-window-scaling] [--window-scaling-only]
 """
 
 from __future__ import annotations
@@ -40,13 +56,14 @@ import numpy as np
 HBM_PEAK_GBPS = 8000.0      # MI355X HBM3E, vendor figure
 MFMA_BF16_PEAK_TFLOPS = 2500.0   # MI355X dense bf16 matrix rate, vendor figure
 METRIC = "verify-attn KV GB/s (% HBM peak) + verified draft tokens/sec, 1 MI355X"
+DEFAULT_WORKLOAD = "llama70b_16k_chain_b64"
+BIG_OP_BYTES = 768 << 20    # inputs above this cannot stay in the 256 MB Infinity Cache
 
 
 ROOT = os.path.dirname(os.path.abspath(__file__))
 KERNEL_SOURCES = ["long_context_verify_amd/csrc/attention.hip",
                   "long_context_verify_amd/csrc/spec_common.hpp",
                   "long_context_verify_amd/csrc/spec_internal.hpp"]
-TRAFFIC_FILE = os.path.join(ROOT, "profiles", "verify_attn_llama8b_32k_hbm_counters.txt")
 
 
 def log(*a):
@@ -69,9 +86,10 @@ def recorded_traffic(workload: str):
     sources they were taken with; if the sources changed since, the figure no
     longer describes this kernel and None is returned.
     """
+    path = os.path.join(ROOT, "profiles", f"verify_attn_{workload}_hbm_counters.txt")
     try:
         fields = {}
-        with open(TRAFFIC_FILE) as f:
+        with open(path) as f:
             for line in f:
                 if ":" in line and not line.startswith("#"):
                     k, v = line.split(":", 1)
@@ -88,7 +106,7 @@ def parse():
     p.add_argument("--gpus", type=int, default=1)
     p.add_argument("--steps", type=int, default=50)
     p.add_argument("--warmup", type=int, default=10)
-    p.add_argument("--workload", default="llama8b_32k_chain")
+    p.add_argument("--workload", default=DEFAULT_WORKLOAD)
     p.add_argument("--cpu-budget", type=float, default=12.0,
                    help="seconds of oracle work for the CPU baseline (0 disables it)")
     p.add_argument("--page-size", type=int, default=0,
@@ -101,17 +119,135 @@ def parse():
     p.add_argument("--copy-probe-mib", type=int, default=0,
                    help="also run plain device copies of this many MiB (calibrates HBM "
                         "byte counters: the copy reads and writes exactly this much)")
+    p.add_argument("--no-others", action="store_true",
+                   help="skip the verify and sampling figures of the other workloads")
+    p.add_argument("--no-window-scaling", action="store_true",
+                   help="skip the window-vs-context scaling run")
+    p.add_argument("--window-scaling-only", action="store_true",
+                   help="run only the window-vs-context scaling run and print its JSON")
     return p.parse_args()
 
 
-def build_inputs(cfg, dev):
-    from workloads import (chain_parent, make_attention_inputs, make_sample_inputs,
-                           make_window_inputs, random_tree)
+# ---------------------------------------------------------------------------
+# Device timing
+# ---------------------------------------------------------------------------
+class Timer:
+    """Mean device time per call, from HIP events on the library's stream."""
+
+    def __init__(self, dev):
+        import torch
+        self.torch = torch
+        self.stream = torch.cuda.current_stream(dev)
+        # 512 MB of unrelated data: reading it evicts the 256 MB Infinity Cache.
+        self.flush_buf = torch.ones(128 << 20, dtype=torch.float32, device=dev)
+
+    def flush(self):
+        self.flush_buf.amax()
+
+    def _bracket(self, body, n):
+        torch = self.torch
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        torch.cuda._sleep(int(2.4e9 * 0.05))   # ~50 ms of GPU spin while the calls queue up
+        e0.record(self.stream)
+        for i in range(n):
+            body(i)
+        e1.record(self.stream)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) * 1e3 / n   # us per call
+
+    def back_to_back(self, fn, n):
+        return self._bracket(fn, n)
+
+    def cold(self, fn, n, prep=None):
+        """Per-call time with a cache flush (and an optional prep) before every
+        call: (flush; prep; call) x n minus (flush; prep) x n."""
+        def with_call(i):
+            self.flush()
+            if prep:
+                prep()
+            fn(i)
+
+        def without(i):
+            self.flush()
+            if prep:
+                prep()
+        t_all = self._bracket(with_call, n)
+        t_base = self._bracket(without, n)
+        return max(t_all - t_base, 0.0)
+
+
+def stream_rates(dev, timer, mib=2048, reps=10):
+    """The device's practical streaming rates, measured now with the plain
+    read and copy kernels of libstreamprobe.so (GB/s of bytes moved; the best
+    of a few launch shapes), plus the rate of re-reading 64 MB that was just
+    read (served by the Infinity Cache when it holds it)."""
+    import ctypes
+    import torch
+    from long_context_verify_amd.build import PROBE_LIB_PATH
+    lib = ctypes.CDLL(PROBE_LIB_PATH)
+    lib.probe_stream_read.restype = ctypes.c_int
+    lib.probe_stream_read.argtypes = [ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p,
+                                      ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_void_p]
+    lib.probe_stream_copy.restype = ctypes.c_int
+    lib.probe_stream_copy.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_size_t,
+                                      ctypes.c_int, ctypes.c_int, ctypes.c_void_p]
+    stream = ctypes.c_void_p(torch.cuda.current_stream(dev).cuda_stream)
+    n = mib << 20
+    src = torch.ones(n // 4, dtype=torch.float32, device=dev)
+    dst = torch.empty_like(src)
+    sink = torch.zeros(1, dtype=torch.float32, device=dev)
+
+    def read(nbytes, grid, unroll, nt):
+        def f(i):
+            if lib.probe_stream_read(src.data_ptr(), nbytes, sink.data_ptr(), grid, unroll, nt,
+                                     stream) != 0:
+                raise RuntimeError("probe_stream_read failed")
+        f(0)
+        return f
+
+    def copy(grid, unroll):
+        def f(i):
+            if lib.probe_stream_copy(src.data_ptr(), dst.data_ptr(), n, grid, unroll,
+                                     stream) != 0:
+                raise RuntimeError("probe_stream_copy failed")
+        f(0)
+        return f
+    best_r, cfg_r = 0.0, None
+    for grid in (1024, 2048, 4096):
+        for unroll in (8, 16):
+            for nt in (0, 1):
+                t = timer.back_to_back(read(n, grid, unroll, nt), reps)
+                if n / t / 1e3 > best_r:
+                    best_r, cfg_r = n / t / 1e3, (grid, unroll, nt)
+    best_c, cfg_c = 0.0, None
+    for grid in (1024, 2048, 4096):
+        for unroll in (4, 8):
+            t = timer.back_to_back(copy(grid, unroll), reps)
+            if 2 * n / t / 1e3 > best_c:
+                best_c, cfg_c = 2 * n / t / 1e3, (grid, unroll)
+    small = 64 << 20
+    t_small = timer.back_to_back(read(small, cfg_r[0], cfg_r[1], 0), reps * 5)
+    del src, dst
+    return {"read_GBps": best_r, "copy_GBps": best_c, "bytes": n,
+            "cache_reread_GBps": small / t_small / 1e3,
+            "how": (f"libstreamprobe.so plain read / copy kernels over {mib} MiB, best of "
+                    f"launch shapes (read: {cfg_r[0]} work-groups x {cfg_r[1]} 4-KB steps, "
+                    f"{'non-temporal' if cfg_r[2] else 'plain'} loads; copy: {cfg_c[0]} x "
+                    f"{cfg_c[1]}), {reps} back-to-back calls between HIP events; "
+                    f"cache_reread: the same read kernel over 64 MiB read just before")}
+
+
+# ---------------------------------------------------------------------------
+# Inputs
+# ---------------------------------------------------------------------------
+def build_inputs(cfg, dev, with_window=True):
+    from workloads import make_attention_inputs, make_sample_inputs, make_window_inputs, random_tree
     att = make_attention_inputs(cfg.batch, cfg.hq, cfg.hkv, cfg.n_q, cfg.head_dim, cfg.kv_len,
                                 dtype=cfg.dtype, seed=cfg.seed, device=dev)
     parent = random_tree(cfg.n_q) if cfg.tree else None
     win = None
-    if cfg.window is not None:
+    if cfg.window is not None and with_window:
         win = make_window_inputs(cfg.batch, cfg.hq, cfg.hkv, cfg.head_dim, cfg.window, cfg.sinks,
                                  [cfg.kv_len] * cfg.batch, dtype=cfg.dtype, seed=cfg.seed + 1,
                                  device=dev)
@@ -131,16 +267,45 @@ def sample_rows_read(n_nodes, parent):
     return n_nodes + n_int
 
 
-def cpu_baseline(cfg, att, parent, win, smp, budget_s):
-    """Time the fp64 oracle on a bounded sample of the step and scale it to the whole step."""
-    import torch
-    from oracle.attention import verify_attention, window_attention
-    from oracle.sample import spec_sample
+def verify_bytes(cfg, esz):
+    kv = 2 * cfg.batch * cfg.hkv * cfg.kv_len * cfg.head_dim * esz
+    qo = 2 * cfg.batch * cfg.hq * cfg.n_q * cfg.head_dim * esz
+    return kv + qo
+
+
+# ---------------------------------------------------------------------------
+# CPU baseline
+# ---------------------------------------------------------------------------
+def cpu_info():
+    model = "unknown"
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    blas = "unknown"
+    threads = 1
     try:
         from threadpoolctl import threadpool_info
-        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+        info = [i for i in threadpool_info() if i.get("user_api") == "blas"]
+        if info:
+            i = info[0]
+            blas = f"{i.get('internal_api', '?')} {i.get('version', '?')} " \
+                   f"({os.path.basename(i.get('filepath', '?'))})"
+            threads = max(int(x.get("num_threads", 1)) for x in info)
     except Exception:  # pragma: no cover
-        threads = 1
+        pass
+    return model, blas, threads
+
+
+def cpu_baseline(cfg, att, parent, win, smp, budget_s):
+    """Time the fp64 oracle on a bounded sample of the step and scale it to the whole step."""
+    from oracle.attention import verify_attention, window_attention
+    from oracle.sample import spec_sample
+    model, blas, threads = cpu_info()
     g = cfg.hq // cfg.hkv
     units = cfg.batch * cfg.hkv
     share = budget_s / 3.0
@@ -184,12 +349,160 @@ def cpu_baseline(cfg, att, parent, win, smp, budget_s):
     drafts = cfg.batch * (cfg.n_nodes - 1)
     return {
         "value": drafts / t_step, "unit": "verified draft tokens/s", "cores": int(threads),
-        "kind": "oracle",
+        "kind": "oracle", "cpu_model": model, "blas": blas,
         "sample": (f"{n_unit}/{units} verify units (sequence x kv head), {n_win}/{cfg.batch} "
-                   f"window sequences, {n_seq}/{cfg.batch} sampling sequences; fp64 numpy, "
-                   f"scaled to the whole step ({t_step:.2f} s/step)"),
+                   f"window sequences, {n_seq}/{cfg.batch} sampling sequences of {cfg.name}; "
+                   f"fp64 numpy, scaled to the whole step ({t_step:.2f} s/step)"),
         "ms_per_step": t_step * 1e3,
     }
+
+
+# ---------------------------------------------------------------------------
+# One workload's ops
+# ---------------------------------------------------------------------------
+class WorkloadOps:
+    """Preallocated outputs and workspaces of one workload: the timed calls allocate nothing."""
+
+    def __init__(self, L, cfg, dev, att, parent, win, smp, seed, page_size=0, siblings="first"):
+        import torch
+        self.L, self.cfg, self.att, self.parent, self.win, self.smp = L, cfg, att, parent, win, smp
+        self.seed, self.page_size, self.siblings = seed, page_size, siblings
+        B, Hq, Hkv, D, Lk, nq = cfg.batch, cfg.hq, cfg.hkv, cfg.head_dim, cfg.kv_len, cfg.n_q
+        dt = att["q"].dtype
+        self.out = torch.empty_like(att["q"])
+        self.lse = torch.empty(B, Hq, nq, dtype=torch.float32, device=dev)
+        self.ws_v = torch.zeros(max(L.verify_attention_workspace_bytes(B, Hq, Hkv, nq, D, Lk, dt),
+                                    256), dtype=torch.uint8, device=dev)
+        self.par_t = None if parent is None else torch.as_tensor(parent, dtype=torch.int32,
+                                                                  device=dev)
+        if win is not None:
+            self.wout = torch.empty_like(win["q"])
+            self.wlse = torch.empty(B, Hq, 1, dtype=torch.float32, device=dev)
+            self.ws_w = torch.zeros(max(L.window_attention_workspace_bytes(
+                B, Hq, Hkv, D, cfg.window, cfg.sinks, dt), 256), dtype=torch.uint8, device=dev)
+        N, V = cfg.n_nodes, cfg.vocab
+        self.s_out = {"out_tokens": torch.empty(B, N, dtype=torch.int32, device=dev),
+                      "out_count": torch.empty(B, dtype=torch.int32, device=dev),
+                      "out_path": torch.empty(B, N, dtype=torch.int32, device=dev),
+                      "out_accept": torch.empty(B, N, dtype=torch.uint8, device=dev)}
+        self.ws_s = torch.zeros(max(L.sample_workspace_bytes(B, N, V), 256), dtype=torch.uint8,
+                                device=dev)
+        if page_size:
+            from workloads import make_paged_inputs
+            self.pg = make_paged_inputs(att["k"], att["v"], att["kv_len"], page_size,
+                                        seed=cfg.seed)
+            self.ws_v = torch.zeros(max(L.verify_attention_paged_workspace_bytes(
+                B, Hq, Hkv, nq, D, Lk, page_size, dt), 256), dtype=torch.uint8, device=dev)
+
+    def verify(self, i=0):
+        a, L = self.att, self.L
+        if self.page_size:
+            L.verify_attention_paged(a["q"], self.pg["k_pages"], self.pg["v_pages"],
+                                     self.pg["block_table"], a["kv_len"], self.cfg.kv_len,
+                                     parent=self.par_t, out=self.out, lse=self.lse,
+                                     workspace=self.ws_v)
+        else:
+            L.verify_attention(a["q"], a["k"], a["v"], a["kv_len"], parent=self.par_t,
+                               out=self.out, lse=self.lse, workspace=self.ws_v)
+
+    def window(self, i=0):
+        w = self.win
+        self.L.window_attention(w["q"], w["k_ring"], w["v_ring"], w["k_sink"], w["v_sink"],
+                                w["total_len"], out=self.wout, lse=self.wlse, workspace=self.ws_w)
+
+    def sample(self, i=0):
+        s = self.smp
+        self.L.spec_sample(s["target"], s["draft"], s["tokens"],
+                           parent=self.par_t if self.cfg.tree else None, seed=self.seed,
+                           offset=i % (1 << 20), workspace=self.ws_s, siblings=self.siblings,
+                           **self.s_out)
+
+    def step_ops(self):
+        ops = [("verify_attn", self.verify)]
+        if self.win is not None:
+            ops.append(("window_attn", self.window))
+        ops.append(("sample", self.sample))
+        return ops
+
+    def verify_bytes(self):
+        return verify_bytes(self.cfg, self.att["q"].element_size())
+
+    def sample_bytes(self):
+        rows = sample_rows_read(self.cfg.n_nodes, self.parent if self.cfg.tree else None)
+        return self.cfg.batch * rows * self.cfg.vocab * self.smp["target"].element_size()
+
+
+def op_figures(timer, ops, steps):
+    """us / GB/s of the verify and sampling calls of one workload."""
+    rep = {}
+    t_v = timer.back_to_back(ops.verify, steps)
+    vb = ops.verify_bytes()
+    rep["verify_attn"] = {"us": t_v, "bytes": vb, "GBps": vb / t_v / 1e3,
+                          "hbm_frac": vb / t_v / 1e3 / HBM_PEAK_GBPS,
+                          "timing": "events around K back-to-back calls"
+                          if vb >= BIG_OP_BYTES else
+                          "events around K back-to-back calls (K/V partly cache-resident)"}
+    sb = ops.sample_bytes()
+    t_s = timer.cold(ops.sample, steps)
+    t_sw = timer.back_to_back(ops.sample, steps)
+    rep["sample"] = {"us": t_s, "us_warm": t_sw, "bytes": sb, "GBps": sb / t_s / 1e3,
+                     "hbm_frac": sb / t_s / 1e3 / HBM_PEAK_GBPS,
+                     "drafts_per_call": ops.cfg.batch * (ops.cfg.n_nodes - 1),
+                     "timing": "K x (cache flush; call) minus K x flush, one event pair each; "
+                               "us_warm: K back-to-back calls"}
+    if ops.cfg.tree:
+        flops = 4.0 * ops.cfg.batch * ops.cfg.hq * ops.cfg.n_q * ops.cfg.kv_len * ops.cfg.head_dim
+        rep["verify_attn"]["mfma_TFLOPs"] = flops / (t_v * 1e-6) / 1e12
+        rep["verify_attn"]["mfma_frac"] = rep["verify_attn"]["mfma_TFLOPs"] / MFMA_BF16_PEAK_TFLOPS
+    return rep
+
+
+def window_scaling(L, dev, timer, steps):
+    """Draft window attention vs full-cache n_q = 1 attention as the context grows.
+
+    The 8B/32K layer shape (batch 8, 32 q heads, 8 kv heads, head dim 128,
+    bf16) with a 512-slot ring + 4 sinks: the window's cost stays flat while
+    attention of one query over the whole cache grows with T.
+    """
+    import torch
+    from workloads import make_attention_inputs, make_window_inputs
+    B, Hq, Hkv, D, W, S = 8, 32, 8, 128, 512, 4
+    rows = []
+    win = make_window_inputs(B, Hq, Hkv, D, W, S, [W + S] * B, dtype="bf16", seed=77, device=dev)
+    wout = torch.empty_like(win["q"])
+    ws_w = torch.zeros(max(L.window_attention_workspace_bytes(B, Hq, Hkv, D, W, S,
+                                                              torch.bfloat16), 256),
+                       dtype=torch.uint8, device=dev)
+    for T in (1024, 8192, 32768, 131072):
+        tl = torch.full((B,), T, dtype=torch.int32, device=dev)
+
+        def fwin(i):
+            L.window_attention(win["q"], win["k_ring"], win["v_ring"], win["k_sink"],
+                               win["v_sink"], tl, out=wout, workspace=ws_w, want_lse=False)
+        fwin(0)
+        t_w = timer.cold(fwin, steps)
+        t_ww = timer.back_to_back(fwin, steps)
+        att = make_attention_inputs(B, Hq, Hkv, 1, D, T, dtype="bf16", seed=78, device=dev)
+        out = torch.empty_like(att["q"])
+        ws_v = torch.zeros(max(L.verify_attention_workspace_bytes(B, Hq, Hkv, 1, D, T,
+                                                                  torch.bfloat16), 256),
+                           dtype=torch.uint8, device=dev)
+
+        def ffull(i):
+            L.verify_attention(att["q"], att["k"], att["v"], att["kv_len"], out=out,
+                               workspace=ws_v, want_lse=False)
+        ffull(0)
+        kvb = 2 * B * Hkv * T * D * 2
+        t_f = timer.back_to_back(ffull, steps) if kvb >= BIG_OP_BYTES else timer.cold(ffull, steps)
+        rows.append({"T": T, "window_us": t_w, "window_us_warm": t_ww, "full_us": t_f,
+                     "full_kv_bytes": kvb,
+                     "window_kv_bytes": 2 * B * Hkv * min(T, W + S) * D * 2})
+        del att, out, ws_v
+        torch.cuda.empty_cache()
+    return {"shape": "batch 8, 32 q heads / 8 kv heads, head dim 128, bf16; window 512 + 4 sinks",
+            "timing": "window: K x (cache flush; call) minus K x flush; full: K back-to-back "
+                      "calls when the cache exceeds 768 MB, else flushed like the window",
+            "rows": rows}
 
 
 def main():
@@ -210,89 +523,23 @@ def main():
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     L.lib()  # fail loudly if the library is missing
+    timer = Timer(dev)
+    if args.window_scaling_only:
+        print(json.dumps({"window_scaling": window_scaling(L, dev, timer, min(args.steps, 30))}),
+              flush=True)
+        return
     log(f"[bench] building inputs for {cfg.name}")
     att, parent, win, smp = build_inputs(cfg, dev)
     if args.logits == "bf16":
         smp["target"] = smp["target"].to(torch.bfloat16)
         smp["draft"] = smp["draft"].to(torch.bfloat16)
-    lsz = smp["target"].element_size()
+    seed = 0x5EED0000 + cfg.seed
+    ops = WorkloadOps(L, cfg, dev, att, parent, win, smp, seed, args.page_size, args.siblings)
     B, Hq, Hkv, D, Lk, nq = cfg.batch, cfg.hq, cfg.hkv, cfg.head_dim, cfg.kv_len, cfg.n_q
+    N, V = cfg.n_nodes, cfg.vocab
     dt = att["q"].dtype
     esz = att["q"].element_size()
-
-    # Preallocated outputs and workspaces: the timed loop allocates nothing.
-    out = torch.empty_like(att["q"])
-    lse = torch.empty(B, Hq, nq, dtype=torch.float32, device=dev)
-    ws_v = torch.zeros(max(L.verify_attention_workspace_bytes(B, Hq, Hkv, nq, D, Lk, dt), 256),
-                       dtype=torch.uint8, device=dev)
-    par_t = None if parent is None else torch.as_tensor(parent, dtype=torch.int32, device=dev)
-    if win is not None:
-        wout = torch.empty_like(win["q"])
-        wlse = torch.empty(B, Hq, 1, dtype=torch.float32, device=dev)
-        ws_w = torch.zeros(max(L.window_attention_workspace_bytes(B, Hq, Hkv, D, cfg.window,
-                                                                  cfg.sinks, dt), 256),
-                           dtype=torch.uint8, device=dev)
-    N, V = cfg.n_nodes, cfg.vocab
-    s_out = {"out_tokens": torch.empty(B, N, dtype=torch.int32, device=dev),
-             "out_count": torch.empty(B, dtype=torch.int32, device=dev),
-             "out_path": torch.empty(B, N, dtype=torch.int32, device=dev),
-             "out_accept": torch.empty(B, N, dtype=torch.uint8, device=dev)}
-    ws_s = torch.zeros(max(L.sample_workspace_bytes(B, N, V), 256), dtype=torch.uint8, device=dev)
-    seed = 0x5EED0000 + cfg.seed
-
-    if args.page_size:
-        from workloads import make_paged_inputs
-        pg = make_paged_inputs(att["k"], att["v"], att["kv_len"], args.page_size, seed=cfg.seed)
-        ws_v = torch.zeros(max(L.verify_attention_paged_workspace_bytes(
-            B, Hq, Hkv, nq, D, Lk, args.page_size, dt), 256), dtype=torch.uint8, device=dev)
-
-    def op_verify():
-        if args.page_size:
-            L.verify_attention_paged(att["q"], pg["k_pages"], pg["v_pages"], pg["block_table"],
-                                     att["kv_len"], Lk, parent=par_t, out=out, lse=lse,
-                                     workspace=ws_v)
-        else:
-            L.verify_attention(att["q"], att["k"], att["v"], att["kv_len"], parent=par_t,
-                               out=out, lse=lse, workspace=ws_v)
-
-    def op_window():
-        L.window_attention(win["q"], win["k_ring"], win["v_ring"], win["k_sink"], win["v_sink"],
-                           win["total_len"], out=wout, lse=wlse, workspace=ws_w)
-
-    def op_sample(i):
-        L.spec_sample(smp["target"], smp["draft"], smp["tokens"], parent=par_t if cfg.tree else None,
-                      seed=seed, offset=i, workspace=ws_s, siblings=args.siblings, **s_out)
-
-    ops = [("verify_attn", lambda i: op_verify())]
-    if win is not None:
-        ops.append(("window_attn", lambda i: op_window()))
-    ops.append(("sample", op_sample))
-
-    # The commit after sampling updates lengths in place, so it is timed on
-    # its own (not part of the step) with the lengths restored before each
-    # call, outside the timed bracket.
-    kl_c = att["kv_len"].clone()
-    tl_c = None if win is None else win["total_len"].clone()
-
-    def prep_commit():
-        kl_c.copy_(att["kv_len"])
-        if tl_c is not None:
-            tl_c.copy_(win["total_len"])
-
-    d_tok = torch.empty(B, dtype=torch.int32, device=dev)
-    d_lp = torch.empty(B, dtype=torch.float32, device=dev)
-    ws_d = torch.zeros(max(L.draft_sample_workspace_bytes(B, V), 256), dtype=torch.uint8,
-                       device=dev)
-
-    def op_draft(i):
-        # One draft step: the draw of node 1 from draft row 0 of every sequence.
-        L.draft_sample(smp["draft"][:, 0], 1, seed=seed, offset=i, out_token=d_tok,
-                       out_logprob=d_lp, workspace=ws_d)
-
-    def op_commit(i):
-        L.kv_commit(att["k"], att["v"], kl_c, s_out["out_count"], nq,
-                    path=s_out["out_path"] if cfg.tree else None, draft_total_len=tl_c,
-                    draft_appended=nq - 1 if tl_c is not None else 0)
+    step_ops = ops.step_ops()
 
     if args.copy_probe_mib > 0:
         n = args.copy_probe_mib << 20
@@ -306,105 +553,84 @@ def main():
 
     log(f"[bench] warmup {args.warmup}")
     for i in range(args.warmup):
-        for _, f in ops:
+        for _, f in step_ops:
             f(i)
     torch.cuda.synchronize()
 
     # (A) Headline: K whole steps back to back, host clock around a device sync.
     log(f"[bench] timing {args.steps} steps")
+    torch.cuda.synchronize()
     t0 = time.perf_counter()
     for i in range(args.steps):
-        for _, f in ops:
+        for _, f in step_ops:
             f(args.warmup + i)
     torch.cuda.synchronize()
     t1 = time.perf_counter()
     ms_step = (t1 - t0) * 1e3 / args.steps
 
-    # (B) Per-op device time from HIP events on the stream the library launches
-    # on (torch's current stream).  Everything is queued behind a GPU sleep so
-    # host launch latency cannot leak into the bracketed time.  An op whose
-    # inputs exceed the 256 MB Infinity Cache runs K times back to back between
-    # one pair of events (its inputs come from HBM every time).  Smaller ops
-    # get one pair per call, with a 512 MB read of an unrelated buffer between
-    # calls (outside the brackets) so every call reads its inputs from HBM and
-    # leaves no dirty lines to write back.
-    stream = torch.cuda.current_stream(dev)
-    flush = torch.ones(128 << 20, dtype=torch.float32, device=dev)
-    op_bytes_in = {"verify_attn": att["k"].numel() * esz * 2,
-                   "window_attn": 0 if win is None else
-                   (win["k_ring"].numel() + win["k_sink"].numel()) * esz * 2,
-                   "sample": smp["target"].numel() * 2 * lsz,
-                   "draft_sample": B * V * lsz,
-                   "kv_commit": 0}
-    op_us = {}
-    preps = {"kv_commit": prep_commit}
-    for name, f in ops + [("draft_sample", op_draft), ("kv_commit", op_commit)]:
-        big = op_bytes_in[name] >= (768 << 20)
-        n_pairs = 1 if big else args.steps
-        pairs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-                 for _ in range(n_pairs)]
-        torch.cuda.synchronize()
-        torch.cuda._sleep(int(2.4e9 * 0.05))           # ~50 ms of GPU spin while we enqueue
-        if big:
-            pairs[0][0].record(stream)
-            for i in range(args.steps):
-                f(args.warmup + args.steps + i)
-            pairs[0][1].record(stream)
-        else:
-            for i, (e0, e1) in enumerate(pairs):
-                flush.amax()
-                if name in preps:
-                    preps[name]()
-                e0.record(stream)
-                f(args.warmup + args.steps + i)
-                e1.record(stream)
-        torch.cuda.synchronize()
-        per_call = [a.elapsed_time(b) * 1e3 for a, b in pairs]
-        op_us[name] = float(np.sum(per_call) / args.steps)
-    log(f"[bench] per-op mean us: {op_us}")
-
-    # Algorithmic bytes per call.
-    kv_bytes = 2 * B * Hkv * Lk * D * esz
-    qo_bytes = 2 * B * Hq * nq * D * esz
-    verify_bytes = kv_bytes + qo_bytes
-    ops_report = {"verify_attn": {
-        "us": op_us["verify_attn"], "bytes": verify_bytes,
-        "GBps": verify_bytes / op_us["verify_attn"] / 1e3,
-    }}
-    ops_report["verify_attn"]["hbm_frac"] = ops_report["verify_attn"]["GBps"] / HBM_PEAK_GBPS
+    # (B) Per-op device times.
+    op_rep = op_figures(timer, ops, args.steps)
     if win is not None:
         keys = cfg.sinks + cfg.window
         wbytes = 2 * B * Hkv * keys * D * esz + 2 * B * Hq * D * esz
-        ops_report["window_attn"] = {"us": op_us["window_attn"], "bytes": wbytes,
-                                     "GBps": wbytes / op_us["window_attn"] / 1e3}
-    srows = sample_rows_read(N, parent if cfg.tree else None)
-    sbytes = B * srows * V * lsz
-    ops_report["sample"] = {"us": op_us["sample"], "bytes": sbytes,
-                            "GBps": sbytes / op_us["sample"] / 1e3}
-    ops_report["sample"]["hbm_frac"] = ops_report["sample"]["GBps"] / HBM_PEAK_GBPS
-    dbytes = B * V * lsz
-    ops_report["draft_sample"] = {"us": op_us["draft_sample"], "bytes": dbytes,
-                                  "GBps": dbytes / op_us["draft_sample"] / 1e3}
-    # Commit: K and V rows of the accepted path read and written back, from the
-    # first node that is not already in place (a chain moves nothing).
-    counts = s_out["out_count"].cpu().numpy()
+        t_w = timer.cold(ops.window, args.steps)
+        op_rep["window_attn"] = {"us": t_w, "us_warm": timer.back_to_back(ops.window, args.steps),
+                                 "bytes": wbytes, "GBps": wbytes / t_w / 1e3,
+                                 "timing": op_rep["sample"]["timing"]}
+
+    # Calls on either side of the step: the draft-step draw and the commit.
+    d_tok = torch.empty(B, dtype=torch.int32, device=dev)
+    d_lp = torch.empty(B, dtype=torch.float32, device=dev)
+    ws_d = torch.zeros(max(L.draft_sample_workspace_bytes(B, V), 256), dtype=torch.uint8,
+                       device=dev)
+
+    def op_draft(i):
+        # One draft step: the draw of node 1 from draft row 0 of every sequence.
+        L.draft_sample(smp["draft"][:, 0], 1, seed=seed, offset=i, out_token=d_tok,
+                       out_logprob=d_lp, workspace=ws_d)
+    t_d = timer.cold(op_draft, args.steps)
+    dbytes = B * V * smp["target"].element_size()
+    op_rep["draft_sample"] = {"us": t_d, "us_warm": timer.back_to_back(op_draft, args.steps),
+                              "bytes": dbytes, "GBps": dbytes / t_d / 1e3,
+                              "timing": op_rep["sample"]["timing"]}
+
+    # The commit updates lengths in place: each call is preceded by a restore
+    # of the lengths, which the subtraction removes with the flush.
+    kl_c = att["kv_len"].clone()
+    tl_c = None if win is None else win["total_len"].clone()
+
+    def prep_commit():
+        kl_c.copy_(att["kv_len"])
+        if tl_c is not None:
+            tl_c.copy_(win["total_len"])
+
+    def op_commit(i):
+        L.kv_commit(att["k"], att["v"], kl_c, ops.s_out["out_count"], nq,
+                    path=ops.s_out["out_path"] if cfg.tree else None, draft_total_len=tl_c,
+                    draft_appended=nq - 1 if tl_c is not None else 0)
+    ops.sample(0)
+    t_c = timer.cold(op_commit, args.steps, prep=prep_commit)
+    counts = ops.s_out["out_count"].cpu().numpy()
     moved = 0
     if cfg.tree:
-        paths = s_out["out_path"].cpu().numpy()
+        paths = ops.s_out["out_path"].cpu().numpy()
         for b in range(B):
             c = int(counts[b])
             j0 = next((j for j in range(c) if paths[b, j] != j), c)
             moved += c - j0
-    cbytes = 2 * 2 * moved * Hkv * D * esz
-    ops_report["kv_commit"] = {"us": op_us["kv_commit"], "bytes": cbytes,
-                               "rows_moved": moved, "accepted_mean": float(counts.mean())}
-    for name, rep in ops_report.items():
-        rep["timing"] = ("events around K back-to-back calls"
-                         if op_bytes_in[name] >= (768 << 20) else
-                         "events around each call, cache flushed between calls")
+    op_rep["kv_commit"] = {"us": t_c, "bytes": 2 * 2 * moved * Hkv * D * esz,
+                           "rows_moved": moved, "accepted_mean": float(counts.mean()),
+                           "timing": "K x (cache flush; length restore; call) minus "
+                                     "K x (flush; restore)"}
+    log(f"[bench] per-op us: " + ", ".join(f"{k} {v['us']:.2f}" for k, v in op_rep.items()))
+
+    rates = stream_rates(dev, timer)
+    log(f"[bench] stream read {rates['read_GBps']:.0f} GB/s, copy {rates['copy_GBps']:.0f} GB/s, "
+        f"64 MB re-read {rates['cache_reread_GBps']:.0f} GB/s")
 
     drafts = B * (N - 1)
     value = drafts / (ms_step / 1e3)
+    v_rep = op_rep["verify_attn"]
     res = {
         "metric": METRIC,
         "value": value,
@@ -420,34 +646,68 @@ def main():
         "data": "synthetic",
         "config": {"workload": cfg.name, "batch": B, "q_heads": Hq, "kv_heads": Hkv,
                    "head_dim": D, "kv_len": Lk, "block": "tree" if cfg.tree else "chain",
-                   "gamma": nq - 1, "draft_window": cfg.window, "sinks": cfg.sinks,
-                   "vocab": V, "logits": args.logits, "siblings": args.siblings, "kv_layout": (f"paged, {args.page_size} keys per page"
-                                             if args.page_size else "contiguous"),
+                   "gamma": nq - 1, "draft_window": cfg.window,
+                   "sinks": cfg.sinks if cfg.window is not None else None,
+                   "vocab": V, "logits": args.logits, "siblings": args.siblings,
+                   "kv_layout": (f"paged, {args.page_size} keys per page"
+                                 if args.page_size else "contiguous"),
                    "parallelism": "single-gpu"},
-        "verify_attn_GBps": ops_report["verify_attn"]["GBps"],
-        "verify_attn_hbm_frac": ops_report["verify_attn"]["hbm_frac"],
+        "verify_attn_GBps": v_rep["GBps"],
+        "verify_attn_hbm_frac": v_rep["hbm_frac"],
         "roofline": {
             "kernel": "spec_verify_attention",
             "bound": "hbm",
-            "achieved": ops_report["verify_attn"]["GBps"],
+            "achieved": v_rep["GBps"],
             "peak": HBM_PEAK_GBPS,
             "unit": "GB/s",
-            "frac": ops_report["verify_attn"]["hbm_frac"],
+            "frac": v_rep["hbm_frac"],
             "traffic": recorded_traffic(cfg.name),
+            "frac_measured_peak": v_rep["GBps"] / rates["read_GBps"],
+            "measured_peak": rates,
         },
-        "ops": ops_report,
+        "roofline_sample": {
+            "kernel": "spec_sample", "bound": "hbm", "achieved": op_rep["sample"]["GBps"],
+            "peak": HBM_PEAK_GBPS, "unit": "GB/s", "frac": op_rep["sample"]["hbm_frac"],
+            "frac_measured_peak": op_rep["sample"]["GBps"] / rates["read_GBps"],
+            "verified_drafts_per_s": op_rep["sample"]["drafts_per_call"]
+            / (op_rep["sample"]["us"] * 1e-6),
+        },
+        "ops": op_rep,
     }
     if cfg.tree:
         # Wide query blocks sit near the MFMA ridge: co-report the dense bf16
         # rate of the same call (Q K^T and P V, 2 flop per multiply-add).
-        flops = 4.0 * B * Hq * nq * Lk * D
-        tflops = flops / (op_us["verify_attn"] * 1e-6) / 1e12
         res["roofline_mfma"] = {"kernel": "spec_verify_attention", "bound": "mfma",
-                                "achieved": tflops, "peak": MFMA_BF16_PEAK_TFLOPS,
-                                "unit": "TFLOP/s", "frac": tflops / MFMA_BF16_PEAK_TFLOPS}
+                                "achieved": v_rep["mfma_TFLOPs"], "peak": MFMA_BF16_PEAK_TFLOPS,
+                                "unit": "TFLOP/s", "frac": v_rep["mfma_frac"]}
+    cpu = None
     if args.cpu_budget > 0:
         log("[bench] timing the oracle on a bounded sample (CPU)")
-        res["cpu_baseline"] = cpu_baseline(cfg, att, parent, win, smp, args.cpu_budget)
+        cpu = cpu_baseline(cfg, att, parent, win, smp, args.cpu_budget)
+
+    # Free the headline inputs before the extra runs.
+    del ops, att, win, smp, step_ops
+    torch.cuda.empty_cache()
+
+    if not args.no_others:
+        others = {}
+        for name, ocfg in CONFIGS.items():
+            if name == cfg.name or ocfg.dtype != "bf16":
+                continue
+            log(f"[bench] other workload {name}")
+            oatt, opar, _, osmp = build_inputs(ocfg, dev, with_window=False)
+            oops = WorkloadOps(L, ocfg, dev, oatt, opar, None, osmp, 0x5EED0000 + ocfg.seed)
+            oops.verify(0)
+            oops.sample(0)
+            others[name] = op_figures(timer, oops, args.steps)
+            del oops, oatt, osmp
+            torch.cuda.empty_cache()
+        res["workloads"] = others
+    if not args.no_window_scaling:
+        log("[bench] window scaling")
+        res["window_scaling"] = window_scaling(L, dev, timer, min(args.steps, 30))
+    if cpu is not None:
+        res["cpu_baseline"] = cpu
     print(json.dumps(res), flush=True)
 
 

@@ -15,6 +15,7 @@ import os
 import re
 from typing import Optional
 
+import numpy as np
 import torch
 
 HERE = os.path.dirname(os.path.abspath(__file__))
@@ -130,17 +131,46 @@ def _nbytes(t: torch.Tensor) -> int:
     return t.numel() * t.element_size()
 
 
+def _expect(t, name: str, shape=None, dtype=None, min_numel: int = 0):
+    """Shape and dtype check of one tensor argument (None passes).  The C ABI
+    sees raw pointers only, so every size the kernels will index with is
+    checked here against the sizes derived from the call's primary inputs."""
+    if t is None:
+        return
+    if not isinstance(t, torch.Tensor):
+        raise ValueError(f"{name} must be a torch tensor")
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
+    if dtype is not None and t.dtype != dtype:
+        raise ValueError(f"{name} has dtype {t.dtype}, expected {dtype}")
+    if t.numel() < min_numel:
+        raise ValueError(f"{name} needs at least {min_numel} elements")
+
+
+def _expect_dev_err(dev_err):
+    _expect(dev_err, "dev_err", dtype=torch.int32, min_numel=1)
+
+
+def _expect_dims(t, name: str, ndim: int):
+    if not isinstance(t, torch.Tensor) or t.dim() != ndim:
+        raise ValueError(f"{name} must be a {ndim}-d tensor")
+
+
+def _check_parent(parent, B, n):
+    """A parent array is [n] (shared) or [B, n] (per sequence)."""
+    if parent is None:
+        return
+    shape = tuple(parent.shape) if hasattr(parent, "shape") else tuple(np.shape(parent))
+    if shape != (n,) and shape != (B, n):
+        raise ValueError(f"parent has shape {shape}, expected ({n},) or ({B}, {n})")
+
+
 def _parent_arg(parent, B, n, device):
     if parent is None:
         return None, 0
+    _check_parent(parent, B, n)
     pt = torch.as_tensor(parent, dtype=torch.int32, device=device).contiguous()
-    if pt.dim() == 1:
-        if pt.numel() != n:
-            raise ValueError("parent must have n entries")
-        return pt, 0
-    if tuple(pt.shape) != (B, n):
-        raise ValueError("parent must be [n] or [B, n]")
-    return pt, n
+    return (pt, 0) if pt.dim() == 1 else (pt, n)
 
 
 def verify_attention_workspace_bytes(B, Hq, Hkv, n_q, D, L_cap, dtype, num_splits=0) -> int:
@@ -156,11 +186,24 @@ def verify_attention(q, k_cache, v_cache, kv_len=None, parent=None, scale: float
                      num_splits: int = 0, out=None, lse=None, workspace=None, dev_err=None,
                      want_lse: bool = True):
     """spec_verify_attention on torch tensors.  Returns (out, lse or None)."""
-    _need_gpu(q, k_cache, v_cache, kv_len, out, lse, dev_err)
+    _expect_dims(q, "q", 4)
+    _expect_dims(k_cache, "k_cache", 4)
     if q.dtype not in _DTYPES or k_cache.dtype != q.dtype or v_cache.dtype != q.dtype:
         raise ValueError("q, k, v must share dtype float32 or bfloat16")
     B, Hq, n_q, D = q.shape
-    _, Hkv, L_cap, _ = k_cache.shape
+    Hkv, L_cap = k_cache.shape[1], k_cache.shape[2]
+    _expect(k_cache, "k_cache", (B, Hkv, L_cap, D))
+    _expect(v_cache, "v_cache", (B, Hkv, L_cap, D))
+    if isinstance(kv_len, torch.Tensor):
+        _expect(kv_len, "kv_len", (B,))
+    elif kv_len is not None and len(kv_len) != B:
+        raise ValueError("kv_len must have B entries")
+    _expect(out, "out", q.shape, q.dtype)
+    _expect(lse, "lse", (B, Hq, n_q), torch.float32)
+    _expect_dev_err(dev_err)
+    _check_parent(parent, B, n_q)
+    _need_gpu(q, k_cache, v_cache, kv_len if isinstance(kv_len, torch.Tensor) else None, out, lse,
+              dev_err)
     dev = q.device
     if out is None:
         out = torch.empty_like(q)
@@ -192,15 +235,22 @@ def verify_attention_paged(q, k_pages, v_pages, block_table, kv_len, L_max: int,
 
     k_pages, v_pages: [num_pages, Hkv, P, D]; block_table: [B, stride] int32;
     kv_len: [B] int32 (required).  Returns (out, lse or None)."""
-    _need_gpu(q, k_pages, v_pages, block_table, kv_len, out, lse, dev_err)
+    _expect_dims(q, "q", 4)
+    _expect_dims(k_pages, "k_pages", 4)
+    _expect_dims(block_table, "block_table", 2)
     if q.dtype not in _DTYPES or k_pages.dtype != q.dtype or v_pages.dtype != q.dtype:
         raise ValueError("q, k, v must share dtype float32 or bfloat16")
-    if k_pages.shape != v_pages.shape:
-        raise ValueError("k_pages and v_pages must match")
-    if block_table.dtype != torch.int32 or kv_len.dtype != torch.int32:
-        raise ValueError("block_table and kv_len must be int32")
     B, Hq, n_q, D = q.shape
-    num_pages, Hkv, P, _ = k_pages.shape
+    num_pages, Hkv, P = k_pages.shape[0], k_pages.shape[1], k_pages.shape[2]
+    _expect(k_pages, "k_pages", (num_pages, Hkv, P, D))
+    _expect(v_pages, "v_pages", (num_pages, Hkv, P, D))
+    _expect(block_table, "block_table", (B, block_table.shape[1]), torch.int32)
+    _expect(kv_len, "kv_len", (B,), torch.int32)
+    _expect(out, "out", q.shape, q.dtype)
+    _expect(lse, "lse", (B, Hq, n_q), torch.float32)
+    _expect_dev_err(dev_err)
+    _check_parent(parent, B, n_q)
+    _need_gpu(q, k_pages, v_pages, block_table, kv_len, out, lse, dev_err)
     dev = q.device
     if out is None:
         out = torch.empty_like(q)
@@ -228,10 +278,35 @@ def window_attention(q, k_ring, v_ring, k_sink, v_sink, total_len, k_new=None, v
                      scale: float = 0.0, num_splits: int = 0, out=None, lse=None,
                      workspace=None, dev_err=None, want_lse: bool = True):
     """spec_window_attention on torch tensors.  Returns (out, lse or None)."""
-    _need_gpu(q, k_ring, v_ring, k_sink, v_sink, k_new, v_new, total_len, out, lse, dev_err)
+    _expect_dims(q, "q", 4)
+    _expect_dims(k_ring, "k_ring", 4)
+    if q.dtype not in _DTYPES:
+        raise ValueError("q must be float32 or bfloat16")
     B, Hq, _, D = q.shape
-    _, Hkv, W, _ = k_ring.shape
+    Hkv, W = k_ring.shape[1], k_ring.shape[2]
+    _expect(q, "q", (B, Hq, 1, D))
+    _expect(k_ring, "k_ring", (B, Hkv, W, D), q.dtype)
+    _expect(v_ring, "v_ring", (B, Hkv, W, D), q.dtype)
+    if (k_sink is None) != (v_sink is None):
+        raise ValueError("k_sink and v_sink must both be given or both be None")
+    if k_sink is not None:
+        _expect_dims(k_sink, "k_sink", 4)
     S = 0 if k_sink is None else k_sink.shape[2]
+    _expect(k_sink, "k_sink", (B, Hkv, S, D), q.dtype)
+    _expect(v_sink, "v_sink", (B, Hkv, S, D), q.dtype)
+    if (k_new is None) != (v_new is None):
+        raise ValueError("k_new and v_new must both be given or both be None")
+    _expect(k_new, "k_new", (B, Hkv, 1, D), q.dtype)
+    _expect(v_new, "v_new", (B, Hkv, 1, D), q.dtype)
+    if isinstance(total_len, torch.Tensor):
+        _expect(total_len, "total_len", (B,))
+    elif len(total_len) != B:
+        raise ValueError("total_len must have B entries")
+    _expect(out, "out", q.shape, q.dtype)
+    _expect(lse, "lse", (B, Hq, 1), torch.float32)
+    _expect_dev_err(dev_err)
+    _need_gpu(q, k_ring, v_ring, k_sink, v_sink, k_new, v_new,
+              total_len if isinstance(total_len, torch.Tensor) else None, out, lse, dev_err)
     dev = q.device
     if out is None:
         out = torch.empty_like(q)
@@ -262,13 +337,20 @@ def spec_sample(target_logits, draft_logits, tokens, parent=None, seed: int = 0,
     selects spec_sample_ex's lossless sibling rule."""
     if siblings not in ("first", "lossless"):
         raise ValueError("siblings must be 'first' or 'lossless'")
-    _need_gpu(target_logits, draft_logits, tokens, out_tokens, out_count, out_path, out_accept,
-              dev_err)
+    _expect_dims(target_logits, "target_logits", 3)
     if target_logits.dtype not in _DTYPES or draft_logits.dtype != target_logits.dtype:
         raise ValueError("logits must be float32 or bfloat16 (both the same)")
-    if tokens.dtype != torch.int32:
-        raise ValueError("tokens must be int32")
     B, N, V = target_logits.shape
+    _expect(draft_logits, "draft_logits", (B, N, V))
+    _expect(tokens, "tokens", (B, N), torch.int32)
+    _expect(out_tokens, "out_tokens", (B, N), torch.int32)
+    _expect(out_count, "out_count", (B,), torch.int32)
+    _expect(out_path, "out_path", (B, N), torch.int32)
+    _expect(out_accept, "out_accept", (B, N), torch.uint8)
+    _expect_dev_err(dev_err)
+    _check_parent(parent, B, N)
+    _need_gpu(target_logits, draft_logits, tokens, out_tokens, out_count, out_path, out_accept,
+              dev_err)
     dev = target_logits.device
     if out_tokens is None:
         out_tokens = torch.empty(B, N, dtype=torch.int32, device=dev)
@@ -306,17 +388,20 @@ def draft_sample(draft_logits, node: int, seed: int = 0, offset: int = 0, out_to
     ``draft_logits`` is [B, V] fp32 whose rows may be strided (e.g. ``x[:, u]``
     of a [B, N, V] tensor); ``out_token`` may be a strided column of a [B, N]
     int32 tensor.  Returns (out_token, out_logprob)."""
-    _need_gpu(draft_logits, out_token, out_logprob, dev_err, strided_ok=(0, 1))
     if draft_logits.dtype not in _DTYPES or draft_logits.dim() != 2:
         raise ValueError("draft_logits must be a [B, V] float32 or bfloat16 tensor")
     if draft_logits.stride(1) != 1:
         raise ValueError("draft_logits rows must be contiguous")
     B, V = draft_logits.shape
+    if out_token is not None and (out_token.dtype != torch.int32 or out_token.dim() != 1
+                                  or out_token.numel() != B):
+        raise ValueError("out_token must be [B] int32")
+    _expect(out_logprob, "out_logprob", (B,), torch.float32)
+    _expect_dev_err(dev_err)
+    _need_gpu(draft_logits, out_token, out_logprob, dev_err, strided_ok=(0, 1))
     dev = draft_logits.device
     if out_token is None:
         out_token = torch.empty(B, dtype=torch.int32, device=dev)
-    if out_token.dtype != torch.int32 or out_token.dim() != 1 or out_token.numel() != B:
-        raise ValueError("out_token must be [B] int32")
     if B > 1 and (draft_logits.stride(0) < V or out_token.stride(0) < 1):
         raise ValueError("rows of draft_logits and entries of out_token must not overlap")
     if out_logprob is None and want_logprob:
@@ -337,18 +422,20 @@ def kv_commit(k_cache, v_cache, kv_len, count, n_q: int, path=None, draft_total_
     """spec_kv_commit on torch tensors; updates k_cache, v_cache, kv_len (and
     draft_total_len) in place.  ``path`` is [B, n_q] (spec_sample's out_path)
     or None for a chain."""
-    _need_gpu(k_cache, v_cache, kv_len, count, path, draft_total_len, dev_err)
+    _expect_dims(k_cache, "k_cache", 4)
     if k_cache.shape != v_cache.shape or k_cache.dtype != v_cache.dtype:
         raise ValueError("k_cache and v_cache must match")
-    if not (k_cache.is_contiguous() and v_cache.is_contiguous()):
-        raise ValueError("caches must be contiguous")
-    for name, t in (("kv_len", kv_len), ("count", count), ("path", path),
-                    ("draft_total_len", draft_total_len)):
-        if t is not None and (t.dtype != torch.int32 or not t.is_contiguous()):
-            raise ValueError(f"{name} must be contiguous int32")
+    if k_cache.dtype not in _DTYPES:
+        raise ValueError("caches must be float32 or bfloat16")
     B, Hkv, L_cap, D = k_cache.shape
-    if path is not None and tuple(path.shape) != (B, n_q):
-        raise ValueError("path must be [B, n_q]")
+    if kv_len is None or count is None:
+        raise ValueError("kv_len and count are required")
+    _expect(kv_len, "kv_len", (B,), torch.int32)
+    _expect(count, "count", (B,), torch.int32)
+    _expect(path, "path", (B, n_q), torch.int32)
+    _expect(draft_total_len, "draft_total_len", (B,), torch.int32)
+    _expect_dev_err(dev_err)
+    _need_gpu(k_cache, v_cache, kv_len, count, path, draft_total_len, dev_err)
     st = lib().spec_kv_commit(
         _p(k_cache), _p(v_cache), _p(kv_len), _p(path), _p(count), B, Hkv, int(n_q), D, L_cap,
         _DTYPES[k_cache.dtype], _p(draft_total_len), int(draft_appended), _p(dev_err),

@@ -234,3 +234,102 @@ def test_bench_refuses_more_than_one_gpu():
                        capture_output=True, text=True, timeout=120, cwd=root)
     assert r.returncode != 0
     assert "one GPU" in (r.stdout + r.stderr)
+
+
+def _bf(*shape):
+    return torch.zeros(*shape, dtype=torch.bfloat16)
+
+
+def _i32(*shape):
+    return torch.zeros(*shape, dtype=torch.int32)
+
+
+# Each case: a call whose tensors disagree with the sizes the call derives
+# from its primary inputs.  The binding must refuse it (ValueError naming the
+# argument) before the device check and before any library call, since the
+# C ABI sees only raw pointers.
+_Q, _K = _bf(2, 8, 5, 64), _bf(2, 2, 100, 64)
+_WQ, _RING, _SINK = _bf(2, 8, 1, 64), _bf(2, 2, 16, 64), _bf(2, 2, 4, 64)
+_LOG, _TOK = torch.zeros(2, 5, 100), _i32(2, 5)
+SHAPE_CASES = [
+    ("verify v_cache", lambda: L.verify_attention(_Q, _K, _bf(2, 2, 99, 64)), "v_cache"),
+    ("verify k batch", lambda: L.verify_attention(_Q, _bf(3, 2, 100, 64), _bf(3, 2, 100, 64)),
+     "k_cache"),
+    ("verify k head dim", lambda: L.verify_attention(_Q, _bf(2, 2, 100, 128),
+                                                     _bf(2, 2, 100, 128)), "k_cache"),
+    ("verify dtype", lambda: L.verify_attention(_Q, _K.float(), _K.float()), "dtype"),
+    ("verify kv_len", lambda: L.verify_attention(_Q, _K, _K, kv_len=_i32(3)), "kv_len"),
+    ("verify kv_len list", lambda: L.verify_attention(_Q, _K, _K, kv_len=[5, 5, 5]), "kv_len"),
+    ("verify out", lambda: L.verify_attention(_Q, _K, _K, out=_bf(2, 8, 5, 32)), "out"),
+    ("verify out dtype", lambda: L.verify_attention(_Q, _K, _K, out=_Q.float()), "out"),
+    ("verify lse", lambda: L.verify_attention(_Q, _K, _K, lse=torch.zeros(2, 8, 4)), "lse"),
+    ("verify dev_err", lambda: L.verify_attention(_Q, _K, _K,
+                                                  dev_err=torch.zeros(1, dtype=torch.int64)),
+     "dev_err"),
+    ("verify dev_err empty", lambda: L.verify_attention(_Q, _K, _K, dev_err=_i32(0)), "dev_err"),
+    ("verify parent", lambda: L.verify_attention(_Q, _K, _K, parent=[-1, 0, 1]), "parent"),
+    ("paged v_pages", lambda: L.verify_attention_paged(_Q, _bf(9, 2, 64, 64), _bf(9, 2, 64, 32),
+                                                       _i32(2, 2), _i32(2), 100), "v_pages"),
+    ("paged kv_len", lambda: L.verify_attention_paged(_Q, _bf(9, 2, 64, 64), _bf(9, 2, 64, 64),
+                                                      _i32(2, 2), _i32(4), 100), "kv_len"),
+    ("paged table rows", lambda: L.verify_attention_paged(_Q, _bf(9, 2, 64, 64),
+                                                          _bf(9, 2, 64, 64), _i32(3, 2),
+                                                          _i32(2), 100), "block_table"),
+    ("paged table dtype", lambda: L.verify_attention_paged(
+        _Q, _bf(9, 2, 64, 64), _bf(9, 2, 64, 64), torch.zeros(2, 2, dtype=torch.int64), _i32(2),
+        100), "block_table"),
+    ("window q rows", lambda: L.window_attention(_bf(2, 8, 2, 64), _RING, _RING, _SINK, _SINK,
+                                                 [20, 20]), "q"),
+    ("window ring dtype", lambda: L.window_attention(_WQ.float(), _RING, _RING, _SINK, _SINK,
+                                                     [20, 20]), "k_ring"),
+    ("window v_ring", lambda: L.window_attention(_WQ, _RING, _bf(2, 2, 8, 64), _SINK, _SINK,
+                                                 [20, 20]), "v_ring"),
+    ("window sink", lambda: L.window_attention(_WQ, _RING, _RING, _SINK, _bf(2, 2, 3, 64),
+                                               [20, 20]), "v_sink"),
+    ("window sink pair", lambda: L.window_attention(_WQ, _RING, _RING, _SINK, None, [20, 20]),
+     "v_sink"),
+    ("window new", lambda: L.window_attention(_WQ, _RING, _RING, _SINK, _SINK, [20, 20],
+                                              k_new=_bf(2, 2, 2, 64), v_new=_bf(2, 2, 2, 64)),
+     "k_new"),
+    ("window new pair", lambda: L.window_attention(_WQ, _RING, _RING, _SINK, _SINK, [20, 20],
+                                                   k_new=_bf(2, 2, 1, 64)), "v_new"),
+    ("window total_len", lambda: L.window_attention(_WQ, _RING, _RING, _SINK, _SINK, _i32(3)),
+     "total_len"),
+    ("window out", lambda: L.window_attention(_WQ, _RING, _RING, _SINK, _SINK, [20, 20],
+                                              out=_bf(2, 8, 1, 32)), "out"),
+    ("window lse", lambda: L.window_attention(_WQ, _RING, _RING, _SINK, _SINK, [20, 20],
+                                              lse=torch.zeros(2, 8)), "lse"),
+    ("sample draft", lambda: L.spec_sample(_LOG, torch.zeros(2, 5, 99), _TOK), "draft_logits"),
+    ("sample tokens", lambda: L.spec_sample(_LOG, _LOG, _i32(2, 4)), "tokens"),
+    ("sample tokens dtype", lambda: L.spec_sample(_LOG, _LOG, _TOK.long()), "tokens"),
+    ("sample out_tokens", lambda: L.spec_sample(_LOG, _LOG, _TOK, out_tokens=_i32(2, 6)),
+     "out_tokens"),
+    ("sample out_count", lambda: L.spec_sample(_LOG, _LOG, _TOK, out_count=_i32(1)),
+     "out_count"),
+    ("sample out_path", lambda: L.spec_sample(_LOG, _LOG, _TOK, out_path=_i32(5, 2)),
+     "out_path"),
+    ("sample out_accept", lambda: L.spec_sample(_LOG, _LOG, _TOK, out_accept=_i32(2, 5)),
+     "out_accept"),
+    ("sample dev_err", lambda: L.spec_sample(_LOG, _LOG, _TOK, dev_err=torch.zeros(1)),
+     "dev_err"),
+    ("sample parent", lambda: L.spec_sample(_LOG, _LOG, _TOK, parent=[-1, 0, 0]), "parent"),
+    ("draft out_token", lambda: L.draft_sample(_LOG[:, 0], 1, out_token=_i32(3)), "out_token"),
+    ("draft out_logprob", lambda: L.draft_sample(_LOG[:, 0], 1, out_logprob=torch.zeros(3)),
+     "out_logprob"),
+    ("commit v", lambda: L.kv_commit(_K, _bf(2, 2, 100, 32), _i32(2), _i32(2), 5), "v_cache"),
+    ("commit kv_len", lambda: L.kv_commit(_K, _K, _i32(3), _i32(2), 5), "kv_len"),
+    ("commit count", lambda: L.kv_commit(_K, _K, _i32(2), _i32(1), 5), "count"),
+    ("commit path", lambda: L.kv_commit(_K, _K, _i32(2), _i32(2), 5, path=_i32(2, 4)), "path"),
+    ("commit total", lambda: L.kv_commit(_K, _K, _i32(2), _i32(2), 5,
+                                         draft_total_len=_i32(2, 1)), "draft_total_len"),
+]
+
+
+@pytest.mark.parametrize("case", SHAPE_CASES, ids=[c[0] for c in SHAPE_CASES])
+def test_binding_refuses_mismatched_shapes(case):
+    _, call, word = case
+    with pytest.raises(ValueError) as e:
+        call()
+    msg = str(e.value)
+    assert "HIP device" not in msg, f"shape mismatch not caught before the device check: {msg}"
+    assert word.split("_")[0] in msg or word in msg, msg

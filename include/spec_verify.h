@@ -91,6 +91,9 @@ typedef enum {
 #define SPEC_MAX_NQ 64
 /* Largest supported number of nodes per sequence in spec_sample. */
 #define SPEC_MAX_SAMPLE_NODES 256
+/* Size of the library-owned device scratch array that spec_sample_noalloc
+   uses on each GPU (one array per device, held until the process ends). */
+#define SPEC_NOALLOC_SCRATCH_BYTES (4u << 20)
 
 /*
  * spec_verify_attention -- verification attention of the drafted block.
@@ -392,6 +395,35 @@ spec_status_t spec_sample_ex(const void* target_logits, const void* draft_logits
                              int32_t* out_count, int32_t* out_path, uint8_t* out_accept,
                              void* workspace, size_t workspace_bytes, int32_t* dev_err,
                              hipStream_t stream);
+
+/*
+ * spec_sample_noalloc -- spec_sample_ex without a workspace: allocates nothing.
+ *
+ * For callers that cannot allocate device memory or pass a workspace: code
+ * under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc.  Same computation, arguments (minus workspace/workspace_bytes),
+ * layouts and outputs as spec_sample_ex, with the same kernels.  Instead of a
+ * caller workspace the call uses a library-owned device array of
+ * SPEC_NOALLOC_SCRATCH_BYTES bytes per GPU (a static device variable: no
+ * hipMalloc, hipFree or allocating library routine is called).  Its address
+ * is looked up once per device, on the first call made with that device
+ * current; the caller's current device must be the device `stream` belongs to.
+ *
+ * Limit: sizes whose workspace, spec_sample_workspace(B, N, V), exceeds
+ * SPEC_NOALLOC_SCRATCH_BYTES return SPEC_ERR_UNSUPPORTED (nothing launched).
+ * The array's arrival counters are cleared by a small kernel at the start of
+ * every call, so a call never depends on what an earlier call left there.
+ * Every call on one GPU shares that GPU's array: calls that may overlap in
+ * time on the same device (different streams, or several host threads)
+ * race on it and must be serialised by the caller.
+ */
+spec_status_t spec_sample_noalloc(const void* target_logits, const void* draft_logits,
+                                  spec_dtype_t logits_dtype, spec_sibling_rule_t siblings,
+                                  const int32_t* tokens, const int32_t* parent,
+                                  int32_t parent_batch_stride, int32_t B, int32_t N, int32_t V,
+                                  uint64_t seed, uint64_t offset, int32_t* out_tokens,
+                                  int32_t* out_count, int32_t* out_path, uint8_t* out_accept,
+                                  int32_t* dev_err, hipStream_t stream);
 
 /*
  * spec_validate_tree -- host-side check of a parent array (host pointer).

@@ -9,7 +9,8 @@ The computation lives in ``libspecverify.so`` (hand-written HIP, built from
 * ``window_attention`` -- the draft's bounded attention over sink tokens and
   a FIFO ring of the last W tokens, with an optional fused append;
 * ``spec_sample`` -- vocabulary softmax, min(1, target/draft) acceptance and
-  the residual / bonus draw;
+  the residual / bonus draw (``spec_sample_noalloc``: the same without a
+  workspace, for callers that cannot allocate);
 * ``draft_sample`` -- one draft-step token draw from softmax(draft logits);
 * ``kv_commit`` -- after sampling, keep the accepted path's K/V right after
   the prefix, set the new lengths, and rewind the draft ring.
@@ -27,6 +28,7 @@ from .api import (  # noqa: F401
     lib,
     sample_workspace_bytes,
     spec_sample,
+    spec_sample_noalloc,
     status_str,
     validate_tree,
     verify_attention,
@@ -40,7 +42,7 @@ from .api import (  # noqa: F401
 
 __all__ = [
     "SPEC_BF16", "SPEC_F32", "SpecError", "draft_sample", "draft_sample_workspace_bytes",
-    "kv_commit", "lib", "sample_workspace_bytes", "spec_sample",
+    "kv_commit", "lib", "sample_workspace_bytes", "spec_sample", "spec_sample_noalloc",
     "status_str", "validate_tree", "verify_attention", "verify_attention_auto_splits",
     "verify_attention_paged", "verify_attention_paged_workspace_bytes",
     "verify_attention_workspace_bytes", "window_attention", "window_attention_workspace_bytes",

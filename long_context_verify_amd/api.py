@@ -45,6 +45,8 @@ _SIGNATURES = {
     "spec_sample_workspace": (_sz, [_i32] * 3),
     "spec_sample_ex": (_i32, [_vp, _vp, _i32, _i32, _vp, _vp, _i32, _i32, _i32, _i32, _u64, _u64,
                               _vp, _vp, _vp, _vp, _vp, _sz, _vp, _vp]),
+    "spec_sample_noalloc": (_i32, [_vp, _vp, _i32, _i32, _vp, _vp, _i32, _i32, _i32, _i32, _u64,
+                                   _u64, _vp, _vp, _vp, _vp, _vp, _vp]),
     "spec_sample_bf16": (_i32, [_vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _u64, _u64, _vp, _vp,
                                 _vp, _vp, _vp, _sz, _vp, _vp]),
     "spec_draft_sample": (_i32, [_vp, _i32, ctypes.c_int64, _i32, _i32, _u64, _u64, _i32, _vp,
@@ -373,6 +375,49 @@ def spec_sample(target_logits, draft_logits, tokens, parent=None, seed: int = 0,
     else:
         st = lib().spec_sample(_p(target_logits), _p(draft_logits), *args)
     _check(st, "spec_sample")
+    return {"out_tokens": out_tokens, "out_count": out_count, "out_path": out_path,
+            "out_accept": out_accept}
+
+
+def spec_sample_noalloc(target_logits, draft_logits, tokens, parent=None, seed: int = 0,
+                        offset: int = 0, out_tokens=None, out_count=None, out_path=None,
+                        out_accept=None, dev_err=None, want_path: bool = True,
+                        want_accept: bool = True, siblings: str = "first"):
+    """spec_sample_noalloc on torch tensors: spec_sample without a workspace (the
+    library's own per-device scratch array is used; outputs are still the
+    caller's).  Returns dict(out_tokens, out_count, out_path, out_accept)."""
+    if siblings not in ("first", "lossless"):
+        raise ValueError("siblings must be 'first' or 'lossless'")
+    _expect_dims(target_logits, "target_logits", 3)
+    if target_logits.dtype not in _DTYPES or draft_logits.dtype != target_logits.dtype:
+        raise ValueError("logits must be float32 or bfloat16 (both the same)")
+    B, N, V = target_logits.shape
+    _expect(draft_logits, "draft_logits", (B, N, V))
+    _expect(tokens, "tokens", (B, N), torch.int32)
+    _expect(out_tokens, "out_tokens", (B, N), torch.int32)
+    _expect(out_count, "out_count", (B,), torch.int32)
+    _expect(out_path, "out_path", (B, N), torch.int32)
+    _expect(out_accept, "out_accept", (B, N), torch.uint8)
+    _expect_dev_err(dev_err)
+    _check_parent(parent, B, N)
+    _need_gpu(target_logits, draft_logits, tokens, out_tokens, out_count, out_path, out_accept,
+              dev_err)
+    dev = target_logits.device
+    if out_tokens is None:
+        out_tokens = torch.empty(B, N, dtype=torch.int32, device=dev)
+    if out_count is None:
+        out_count = torch.empty(B, dtype=torch.int32, device=dev)
+    if out_path is None and want_path:
+        out_path = torch.empty(B, N, dtype=torch.int32, device=dev)
+    if out_accept is None and want_accept:
+        out_accept = torch.empty(B, N, dtype=torch.uint8, device=dev)
+    par, pstride = _parent_arg(parent, B, N, dev)
+    st = lib().spec_sample_noalloc(
+        _p(target_logits), _p(draft_logits), _DTYPES[target_logits.dtype],
+        1 if siblings == "lossless" else 0, _p(tokens), _p(par), pstride, B, N, V,
+        int(seed) & (2**64 - 1), int(offset), _p(out_tokens), _p(out_count), _p(out_path),
+        _p(out_accept), _p(dev_err), _stream(dev))
+    _check(st, "spec_sample_noalloc")
     return {"out_tokens": out_tokens, "out_count": out_count, "out_path": out_path,
             "out_accept": out_accept}
 

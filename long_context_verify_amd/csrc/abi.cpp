@@ -316,7 +316,7 @@ spec_status_t sample_call(const void* target_logits, const void* draft_logits,
                           uint64_t seed, uint64_t offset, int32_t* out_tokens, int32_t* out_count,
                           int32_t* out_path, uint8_t* out_accept, void* workspace,
                           size_t workspace_bytes, int32_t* dev_err, hipStream_t stream,
-                          bool bf16, bool lossless) {
+                          bool bf16, bool lossless, bool noalloc = false) {
   spec_status_t st = sample_shape(B, N, V);
   if (st != SPEC_OK) return st;
   if (offset >= (1ull << 30)) return SPEC_ERR_INVALID_ARG;
@@ -327,6 +327,14 @@ spec_status_t sample_call(const void* target_logits, const void* draft_logits,
       !aligned_or_null(parent, 4) || !aligned_or_null(dev_err, 4))
     return SPEC_ERR_MISALIGNED;
   const SamplePlan p = plan_sample(B, N, V);
+  if (noalloc) {
+    // The library-owned array replaces the workspace; its arrival counters
+    // (the workspace's first off_m bytes) are cleared before the kernels run.
+    if (p.bytes > SPEC_NOALLOC_SCRATCH_BYTES) return SPEC_ERR_UNSUPPORTED;
+    if (noalloc_scratch(&workspace) != hipSuccess) return SPEC_ERR_HIP;
+    workspace_bytes = SPEC_NOALLOC_SCRATCH_BYTES;
+    if (launch_zero_words(workspace, p.off_m, stream) != hipSuccess) return SPEC_ERR_HIP;
+  }
   if (!aligned(workspace, 256) || workspace_bytes < p.bytes) return SPEC_ERR_WORKSPACE;
 
   SampleArgs a;
@@ -407,6 +415,22 @@ spec_status_t spec_sample_ex(const void* target_logits, const void* draft_logits
                      seed, offset, out_tokens, out_count, out_path, out_accept, workspace,
                      workspace_bytes, dev_err, stream, logits_dtype == SPEC_BF16,
                      siblings == SPEC_SIBLINGS_LOSSLESS);
+}
+
+spec_status_t spec_sample_noalloc(const void* target_logits, const void* draft_logits,
+                                  spec_dtype_t logits_dtype, spec_sibling_rule_t siblings,
+                                  const int32_t* tokens, const int32_t* parent,
+                                  int32_t parent_batch_stride, int32_t B, int32_t N, int32_t V,
+                                  uint64_t seed, uint64_t offset, int32_t* out_tokens,
+                                  int32_t* out_count, int32_t* out_path, uint8_t* out_accept,
+                                  int32_t* dev_err, hipStream_t stream) {
+  if (logits_dtype != SPEC_F32 && logits_dtype != SPEC_BF16) return SPEC_ERR_INVALID_ARG;
+  if (siblings != SPEC_SIBLINGS_FIRST && siblings != SPEC_SIBLINGS_LOSSLESS)
+    return SPEC_ERR_INVALID_ARG;
+  return sample_call(target_logits, draft_logits, tokens, parent, parent_batch_stride, B, N, V,
+                     seed, offset, out_tokens, out_count, out_path, out_accept, nullptr, 0,
+                     dev_err, stream, logits_dtype == SPEC_BF16,
+                     siblings == SPEC_SIBLINGS_LOSSLESS, true);
 }
 
 size_t spec_draft_sample_workspace(int32_t B, int32_t V) {

@@ -40,6 +40,8 @@
 
 #include <hip/hip_runtime.h>
 
+#include <mutex>
+
 #include "spec_common.hpp"
 #include "spec_internal.hpp"
 
@@ -1033,6 +1035,48 @@ static hipError_t launch_sample_t(const SampleArgs& a, hipStream_t stream) {
 
 hipError_t launch_sample(const SampleArgs& a, hipStream_t stream) {
   return a.logits_bf16 ? launch_sample_t<__bf16>(a, stream) : launch_sample_t<float>(a, stream);
+}
+
+// ---------------------------------------------------------------------------
+// Library-owned scratch of spec_sample_noalloc (callers that cannot allocate).
+// One array per device, in the code object's static device memory.  In host
+// code `scratch` names a host-side stand-in, not device memory: kernels and
+// fills only ever get the device address that hipGetSymbolAddress returns,
+// kept per device.
+// ---------------------------------------------------------------------------
+static __device__ __align__(256) uint8_t scratch[SPEC_NOALLOC_SCRATCH_BYTES];
+
+constexpr int kMaxDevices = 64;
+
+hipError_t noalloc_scratch(void** ptr) {
+  static std::mutex mu;
+  static void* per_device[kMaxDevices] = {};
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(mu);
+  if (!per_device[dev]) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    if (!p) return hipErrorInvalidSymbol;
+    per_device[dev] = p;
+  }
+  *ptr = per_device[dev];
+  return hipSuccess;
+}
+
+__global__ __launch_bounds__(256) void zero_words(uint32_t* p, uint32_t n) {
+  for (uint32_t i = blockIdx.x * 256u + threadIdx.x; i < n; i += gridDim.x * 256u) p[i] = 0u;
+}
+
+hipError_t launch_zero_words(void* p, size_t bytes, hipStream_t stream) {
+  const uint32_t n = (uint32_t)(bytes / 4);
+  if (n == 0) return hipSuccess;
+  const uint32_t grid = n / 256u + 1u < 256u ? n / 256u + 1u : 256u;
+  hipLaunchKernelGGL(zero_words, dim3(grid), dim3(256), 0, stream, static_cast<uint32_t*>(p), n);
+  return hipGetLastError();
 }
 
 // ---------------------------------------------------------------------------

@@ -115,6 +115,13 @@ struct SamplePlan {
 SamplePlan plan_sample(int32_t B, int32_t N, int32_t V);
 hipError_t launch_sample(const SampleArgs& a, hipStream_t stream);
 
+// The library-owned scratch array of spec_sample_noalloc on the current
+// device (SPEC_NOALLOC_SCRATCH_BYTES bytes): its device address, looked up
+// once per device.
+hipError_t noalloc_scratch(void** ptr);
+// Zero `bytes` (a multiple of 4) at device pointer p with a fill kernel.
+hipError_t launch_zero_words(void* p, size_t bytes, hipStream_t stream);
+
 // Keeping the accepted path's K/V after a verification round.
 struct CommitArgs {
   void* k;                  // [B, Hkv, L_cap, row_bytes]

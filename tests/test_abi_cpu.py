@@ -333,3 +333,20 @@ def test_binding_refuses_mismatched_shapes(case):
     msg = str(e.value)
     assert "HIP device" not in msg, f"shape mismatch not caught before the device check: {msg}"
     assert word.split("_")[0] in msg or word in msg, msg
+
+
+def test_sample_noalloc_argument_checks():
+    """Host checks of the no-allocation sampling call: sizes whose workspace
+    exceeds the library's scratch array are refused before any HIP call."""
+    def call(B=2, N=5, V=1000, dt=0, rule=0, tgt=P, offset=0):
+        return L.lib().spec_sample_noalloc(tgt, P, dt, rule, P, NULL, 0, B, N, V, 1, offset, P,
+                                           P, NULL, NULL, NULL, NULL)
+    assert call(B=0) == OK
+    assert call(N=0) == INVALID
+    assert call(dt=2) == INVALID
+    assert call(rule=2) == INVALID
+    assert call(offset=1 << 30) == INVALID
+    assert call(tgt=P_ODD) == MISALIGNED
+    assert L.sample_workspace_bytes(4096, 2, 1000) > 4 << 20
+    assert call(B=4096, N=2, V=1000) == UNSUPPORTED
+    assert call(B=64, N=8, V=1 << 27) == UNSUPPORTED

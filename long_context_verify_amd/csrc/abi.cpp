@@ -369,6 +369,9 @@ spec_status_t sample_call(const void* target_logits, const void* draft_logits,
   a.n_groups = p.n_groups;
   a.logits_bf16 = bf16 ? 1 : 0;
   a.lossless = lossless ? 1 : 0;
+  // The lossless walk may stop at any node with its rows cached; the
+  // first-accepted rule reads a leaf's target row only if the walk ends there.
+  a.leaf_rows = lossless ? 1 : 0;
   a.dev_err = dev_err;
   return launch_sample(a, stream) == hipSuccess ? SPEC_OK : SPEC_ERR_HIP;
 }

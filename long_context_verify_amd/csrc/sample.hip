@@ -12,19 +12,25 @@
 // Two kernels, back to back on the caller's stream (no work-group waits on
 // another; the second phase's last work-group of a sequence finishes it):
 //
-//   sample_stats   grid (vocab chunks, 2N rows, B).  Streams the logits once
-//                  (every target row and the draft rows of nodes that have
-//                  children) and writes per-chunk (max, sum of exp(x - max));
-//                  fp32 inside a thread, fp64 across threads.
+//   sample_stats   grid (vocab chunks, 2N rows, B).  Streams, once, the rows
+//                  the decision needs: the target and draft rows of nodes that
+//                  have children (and, for the lossless rule, the target rows
+//                  of leaves too), with non-temporal loads, and writes
+//                  per-chunk (max, sum of exp(x - max)); fp32 inside a thread,
+//                  fp64 across threads.
 //   sample_resid   grid (groups, B).  Every work-group of a sequence derives
 //                  the same decision (fp64 log-normalisers, one Philox uniform
 //                  and acceptance test per node, the walk from the root: a few
 //                  hundred scalars, two memory round trips), then the residual
 //                  (or target) mass of its 1024-id race chunks of the stop
-//                  row.  The group that completes the sequence's masses (an
-//                  arrival counter per sequence in the workspace) runs the
-//                  two-level exponential race in fp64 at the stop row and
-//                  writes the outputs.
+//                  row, all of its chunks' loads in one round.  When the walk
+//                  ends at a leaf whose target row the first kernel skipped,
+//                  the groups gather that row's per-chunk (max, sum) instead,
+//                  so a leaf row is read once, and only when it is drawn from.
+//                  The group that completes the sequence's masses (an arrival
+//                  counter per sequence in the workspace) runs the two-level
+//                  exponential race in fp64 at the stop row and writes the
+//                  outputs.
 // With the lossless sibling rule a decide kernel (one work-group per
 // sequence) runs between the two and stores the decision record that the
 // residual groups read.
@@ -95,13 +101,19 @@ __device__ __forceinline__ float ld1(const T* row, size_t e) {
   return (float)row[e];
 }
 // Ids e .. e+3 (e a multiple of 4, rows aligned to whole vectors): one 16-byte
-// (fp32) or 8-byte (bf16) load.
-template <typename T>
+// (fp32) or 8-byte (bf16) load; NT: non-temporal (data read once).
+template <typename T, bool NT = false>
 __device__ __forceinline__ f32x4 ld4(const T* row, size_t e) {
   if constexpr (sizeof(T) == 4) {
-    return reinterpret_cast<const f32x4*>(row)[e >> 2];
+    const f32x4* p = reinterpret_cast<const f32x4*>(row) + (e >> 2);
+    if constexpr (NT) return __builtin_nontemporal_load(p);
+    else return *p;
   } else {
-    const uint2 w = reinterpret_cast<const uint2*>(row)[e >> 2];
+    const unsigned long long* p = reinterpret_cast<const unsigned long long*>(row) + (e >> 2);
+    unsigned long long v;
+    if constexpr (NT) v = __builtin_nontemporal_load(p);
+    else v = *p;
+    const uint2 w = {(uint32_t)v, (uint32_t)(v >> 32)};
     return f32x4{__uint_as_float(w.x << 16), __uint_as_float(w.x & 0xffff0000u),
                  __uint_as_float(w.y << 16), __uint_as_float(w.y & 0xffff0000u)};
   }
@@ -185,11 +197,19 @@ __global__ __launch_bounds__(kSampleThreads) void sample_stats(SampleArgs a) {
   const int chunk = blockIdx.x, rowsel = blockIdx.y, b = blockIdx.z;
   const int kind = rowsel >= a.N;  // 0: target row, 1: draft row
   const int u = rowsel - kind * a.N;
-  if (kind) {
-    // Draft rows are needed only at nodes that have children.
-    int has = 0;
-    for (int c = 1 + threadIdx.x; c < a.N; c += kSampleThreads) has |= parent_of(a, b, c) == u;
-    if (!__syncthreads_or(has)) return;
+  if (kind || !a.leaf_rows) {
+    // Draft rows are needed only at nodes that have children, and so are
+    // target rows unless the leaves' are streamed here too (the residual
+    // pass reads a leaf's target row if the walk stops there).
+    int has;
+    if (!a.parent) {
+      has = u < a.N - 1;
+    } else {
+      has = 0;
+      for (int c = 1 + threadIdx.x; c < a.N; c += kSampleThreads) has |= parent_of(a, b, c) == u;
+      has = __syncthreads_or(has);
+    }
+    if (!has) return;
   }
   const T* row = static_cast<const T*>(kind ? a.draft : a.target) + ((size_t)b * a.N + u) * a.V;
   const int x0 = chunk * a.vchunk;
@@ -209,7 +229,7 @@ __global__ __launch_bounds__(kSampleThreads) void sample_stats(SampleArgs a) {
     for (int i = 0; i < PER / 4; ++i) {
       const int e = x0 + 4 * (threadIdx.x + kSampleThreads * i);
       f32x4 v = {-INFINITY, -INFINITY, -INFINITY, -INFINITY};
-      if (e < a.V) v = ld4(row, e);   // V % 4 == 0: a vector is wholly in or out
+      if (e < a.V) v = ld4<T, true>(row, e);   // V % 4 == 0: a vector is wholly in or out
 #pragma unroll
       for (int k = 0; k < 4; ++k) x[4 * i + k] = v[k];
     }
@@ -290,7 +310,7 @@ __device__ void lossless_walk(const SampleArgs& a, int b, Decision& d, SiblingTe
 
 // NT: threads of the calling work-group.
 template <typename T, bool LOSSLESS = false, int NT = kSampleThreads, bool CACHE = false>
-__device__ void decide_sequence(const SampleArgs& a, int b, Decision& d,
+__device__ __forceinline__ void decide_sequence(const SampleArgs& a, int b, Decision& d,
                                 SiblingTests* st = nullptr) {
   const int N = a.N, V = a.V;
   const int tid = threadIdx.x;
@@ -339,7 +359,8 @@ __device__ void decide_sequence(const SampleArgs& a, int b, Decision& d,
     const int k0 = tid % GL;
     const int kind = rs >= N;
     const int u = rs - kind * N;
-    const bool need = rs < 2 * N && (!kind || (!bad_tree && d.has_child[u]));
+    const bool need =
+        rs < 2 * N && ((!kind && a.leaf_rows) || (!bad_tree && d.has_child[u]));
     const size_t o = ((size_t)b * 2 * N + rs) * nv;
     float mk = -INFINITY;
     double sk = 0.0;
@@ -620,8 +641,7 @@ __device__ void lossless_walk(const SampleArgs& a, int b, Decision& d, SiblingTe
   __syncthreads();
 }
 
-// Store one sequence's decision record (group 0 of the residual kernel, or
-// the lossless decide kernel).
+// Store one sequence's decision record (the lossless decide kernel).
 __device__ __forceinline__ void store_decision(const SampleArgs& a, int b, const Decision& d) {
   const int N = a.N, tid = threadIdx.x;
   const int r = d.stop;
@@ -677,7 +697,7 @@ __device__ __forceinline__ float race_e32(uint32_t w) {
 // normaliser|, plus 2e-6) on pt and pd, of E (2e-6) and of the quotient, ten
 // times over, and 1e-30 for fp32 underflow, so no id left out can win or tie
 // in fp64.  Usually one id per block is scored in fp64.
-__device__ void race_ids(const float (&lt)[4], const float (&ld)[4], const uint32_t (&words)[4],
+__device__ __forceinline__ void race_ids(const float (&lt)[4], const float (&ld)[4], const uint32_t (&words)[4],
                          int e0, int V, double lzt, double lzd, double shift, bool resid,
                          double& best, int& bidx, double* redd, int* redi) {
   __shared__ float redf[4];
@@ -747,33 +767,28 @@ struct StopView {
   const Decision* d;        // the LDS decision when dec is NULL
 };
 
-template <typename T>
-__device__ void race_emit(const SampleArgs& a, int b, const StopView& sv) {
+// Outputs of a sequence whose device data is invalid (bad parent array or token).
+__device__ __forceinline__ void emit_bad(const SampleArgs& a, int b, int bad) {
+  const int N = a.N, tid = threadIdx.x;
+  for (int c = tid; c < N; c += (int)blockDim.x) {
+    a.out_tokens[(size_t)b * N + c] = -1;
+    if (a.out_path) a.out_path[(size_t)b * N + c] = -1;
+    if (a.out_accept) a.out_accept[(size_t)b * N + c] = 0;
+  }
+  if (tid == 0) {
+    a.out_count[b] = 0;
+    report_error(a.dev_err, bad == 2 ? SPEC_DEVERR_TOKEN : SPEC_DEVERR_PARENT);
+  }
+}
+
+// Level 1 of the draw at stop row r: chunks race with score W_c / E1_c.
+// After a rejection the weights are the residual masses; if they all vanish,
+// the target's (use_resid tells which).  The masses were stored by other
+// work-groups of this launch.  Returns the winning chunk.
+__device__ __forceinline__ int race_level1(const SampleArgs& a, int b, int r, bool residual, bool& use_resid) {
   __shared__ double redd[4];
   __shared__ int redi[4];
-  const int N = a.N, V = a.V;
   const int tid = threadIdx.x;
-  const int len = sv.len;
-  const int bad = sv.bad;
-  const bool residual = sv.residual;
-  int* out_tok = a.out_tokens + (size_t)b * N;
-  if (bad) {
-    for (int c = tid; c < N; c += kSampleThreads) {
-      out_tok[c] = -1;
-      if (a.out_path) a.out_path[(size_t)b * N + c] = -1;
-      if (a.out_accept) a.out_accept[(size_t)b * N + c] = 0;
-    }
-    if (tid == 0) {
-      a.out_count[b] = 0;
-      report_error(a.dev_err, bad == 2 ? SPEC_DEVERR_TOKEN : SPEC_DEVERR_PARENT);
-    }
-    return;
-  }
-  const int r = sv.r;
-
-  // Level 1: chunks race with score W_c / E1_c.  After a rejection the
-  // weights are the residual masses; if they all vanish, the target's.
-  // (The masses were stored by other work-groups of this launch.)
   const double* rw = a.race_w + (size_t)b * a.n_race * 2;
   double w_res = 0.0, w_tgt = 0.0;     // this thread's first chunk, q = tid
   if (tid < a.n_race) {
@@ -785,7 +800,7 @@ __device__ void race_emit(const SampleArgs& a, int b, const StopView& sv) {
     tot += load_coherent(rw + 2 * q);
   tot = block_sum(tot, redd);
   const bool fallback = residual && !(tot > 0.0);
-  const bool use_resid = residual && !fallback;
+  use_resid = residual && !fallback;
   double best = -1.0;
   int bidx = 0x7fffffff;
   for (int q = tid; q < a.n_race; q += kSampleThreads) {
@@ -798,16 +813,44 @@ __device__ void race_emit(const SampleArgs& a, int b, const StopView& sv) {
     }
   }
   block_argmax(best, bidx, redd, redi);
-  const int cstar = bidx < a.n_race ? bidx : 0;
+  return bidx < a.n_race ? bidx : 0;
+}
 
-  // Level 2: ids of the winning chunk race with score w_x / E2_x (fp64 weights).
-  const double lzt = sv.lzt, lzd = sv.lzd, shift = sv.shift;
-  const T* trow = static_cast<const T*>(a.target) + ((size_t)b * N + r) * V;
-  const T* drow = static_cast<const T*>(a.draft) + ((size_t)b * N + r) * V;
-  const int e0 = cstar * kRaceChunk + 4 * tid;
+// The level-2 race among this thread's four ids of one race chunk, with the
+// logits already in registers (lt, ld; ids past V hold -inf).  Returns the
+// winning id of the chunk (block-wide), or a value >= V if no id has positive
+// weight.  After a residual race that finds no id with a positive fp64
+// residual (the fp32 chunk mass was positive from a cancellation at the 1e-7
+// level) the chunk is raced on the target's weights instead.
+__device__ __forceinline__ int race_chunk(const SampleArgs& a, int b, int r, int q, const float (&lt)[4],
+                          const float (&ld)[4], bool use_resid, double lzt, double lzd,
+                          double shift) {
+  __shared__ double redd[4];
+  __shared__ int redi[4];
+  const int e0 = q * kRaceChunk + 4 * (int)threadIdx.x;
   uint32_t w0 = (uint32_t)(e0 >> 2), w1 = (uint32_t)r, w2 = (uint32_t)b, w3 = a.ctr3_base + 3u;
   philox4x32_10(w0, w1, w2, w3, a.key0, a.key1);
   const uint32_t words[4] = {w0, w1, w2, w3};
+  double best = -1.0;
+  int bidx = 0x7fffffff;
+  race_ids(lt, ld, words, e0, a.V, lzt, lzd, use_resid ? shift : 0.0, use_resid, best, bidx,
+           redd, redi);
+  if (bidx >= a.V && use_resid) {
+    best = -1.0;
+    bidx = 0x7fffffff;
+    race_ids(lt, ld, words, e0, a.V, lzt, lzd, 0.0, false, best, bidx, redd, redi);
+  }
+  return bidx;
+}
+
+// Level 2 of the draw with the winning chunk's logits loaded from memory.
+template <typename T>
+__device__ __forceinline__ int race_level2(const SampleArgs& a, int b, int r, int cstar, bool use_resid,
+                           double lzt, double lzd, double shift) {
+  const int N = a.N, V = a.V;
+  const T* trow = static_cast<const T*>(a.target) + ((size_t)b * N + r) * V;
+  const T* drow = static_cast<const T*>(a.draft) + ((size_t)b * N + r) * V;
+  const int e0 = cstar * kRaceChunk + 4 * (int)threadIdx.x;
   float lt[4], ld[4];
 #pragma unroll
   for (int k = 0; k < 4; ++k) {
@@ -815,24 +858,20 @@ __device__ void race_emit(const SampleArgs& a, int b, const StopView& sv) {
     lt[k] = e < V ? ld1(trow, e) : -INFINITY;
     ld[k] = (e < V && use_resid) ? ld1(drow, e) : -INFINITY;
   }
-  double best2 = -1.0;
-  int bidx2 = 0x7fffffff;
-  race_ids(lt, ld, words, e0, V, lzt, lzd, use_resid ? shift : 0.0, use_resid, best2, bidx2,
-           redd, redi);
-  if (bidx2 >= V && use_resid) {
-    // The fp32 chunk mass was positive but no id of the chunk has a positive
-    // fp64 residual (a cancellation at the 1e-7 level): draw from the target.
-    best2 = -1.0;
-    bidx2 = 0x7fffffff;
-    race_ids(lt, ld, words, e0, V, lzt, lzd, 0.0, false, best2, bidx2, redd, redi);
-  }
-  const int y = bidx2 < V ? bidx2 : 0;
+  const int y = race_chunk(a, b, r, cstar, lt, ld, use_resid, lzt, lzd, shift);
+  return y < V ? y : 0;
+}
 
+// The outputs of a sequence: the accepted path's drafted tokens, then y.
+__device__ __forceinline__ void emit_outputs(const SampleArgs& a, int b, const StopView& sv, int y) {
+  const int N = a.N, tid = threadIdx.x;
+  const int len = sv.len;
+  int* out_tok = a.out_tokens + (size_t)b * N;
   auto path_at = [&](int c) -> int {
     if (sv.dec) return sv.dec[4 + c];
     return c < sv.d->len ? sv.d->path[c] : -1;
   };
-  for (int c = tid; c < N; c += kSampleThreads) {
+  for (int c = tid; c < N; c += (int)blockDim.x) {
     int tokv = -1;
     const int pv = path_at(c);
     if (c < len - 1)
@@ -845,6 +884,18 @@ __device__ void race_emit(const SampleArgs& a, int b, const StopView& sv) {
       a.out_accept[(size_t)b * N + c] = (uint8_t)(sv.dec ? sv.dec[4 + N + c] : sv.d->acc[c]);
   }
   if (tid == 0) a.out_count[b] = len;
+}
+
+template <typename T>
+__device__ void race_emit(const SampleArgs& a, int b, const StopView& sv) {
+  if (sv.bad) {
+    emit_bad(a, b, sv.bad);
+    return;
+  }
+  bool use_resid = false;
+  const int cstar = race_level1(a, b, sv.r, sv.residual, use_resid);
+  const int y = race_level2<T>(a, b, sv.r, cstar, use_resid, sv.lzt, sv.lzd, sv.shift);
+  emit_outputs(a, b, sv, y);
 }
 
 // Residual (or target) mass of the stop row's 1024-id race chunks q0 .. q1-1
@@ -890,6 +941,10 @@ __global__ __launch_bounds__(kSampleThreads) void sample_resid(SampleArgs a) {
     dm = residual ? d.m[1][r] : 0.f;
     dinv = residual ? (float)(1.0 / d.s[1][r]) : 0.f;
   }
+  // A leaf's target row whose statistics the first kernel did not gather
+  // (the walk accepted every draft on its path): this pass gathers them too,
+  // per race chunk (max, sum of exp), and the draw derives the normaliser.
+  const bool row_stats = residual || a.leaf_rows;
   const T* trow = static_cast<const T*>(a.target) + ((size_t)b * N + r) * V;
   const T* drow = static_cast<const T*>(a.draft) + ((size_t)b * N + r) * V;
   const int q0 = (int)((long long)a.n_race * grp / a.n_groups);
@@ -898,7 +953,7 @@ __global__ __launch_bounds__(kSampleThreads) void sample_resid(SampleArgs a) {
   // partial sums in LDS; one block pass per batch of chunks adds the waves.
   // The loads of kU chunks are issued together (a group may own several).
   constexpr int kBatch = 64;
-  constexpr int kU = 4;
+  constexpr int kU = 8;
   __shared__ double part[kSampleThreads / kWave][kBatch][2];
   const int wave = tid >> 6, lane = tid & 63;
   for (int qb = q0; qb < q1; qb += kBatch) {
@@ -929,42 +984,100 @@ __global__ __launch_bounds__(kSampleThreads) void sample_resid(SampleArgs a) {
           }
         }
       }
+      if (row_stats) {
 #pragma unroll
-      for (int u = 0; u < kU; ++u) {
-        if (i0 + u >= nq) break;
-        float sw = 0.f, spt = 0.f;
+        for (int u = 0; u < kU; ++u) {
+          if (i0 + u >= nq) break;
+          float sw = 0.f, spt = 0.f;
 #pragma unroll
-        for (int k = 0; k < 4; ++k) {
-          const float pt = fast_exp2((tv[u][k] - tm) * kLog2e) * tinv;
-          const float pd = residual ? fast_exp2((dv[u][k] - dm) * kLog2e) * dinv : 0.f;
-          spt += pt;
-          sw += fmaxf(pt - shift * pd, 0.f);
+          for (int k = 0; k < 4; ++k) {
+            const float pt = fast_exp2((tv[u][k] - tm) * kLog2e) * tinv;
+            const float pd = residual ? fast_exp2((dv[u][k] - dm) * kLog2e) * dinv : 0.f;
+            spt += pt;
+            sw += fmaxf(pt - shift * pd, 0.f);
+          }
+          const double tw = wave_sum((double)sw);
+          const double tp = wave_sum((double)spt);
+          if (lane == 0) {
+            part[wave][i0 + u][0] = tw;
+            part[wave][i0 + u][1] = tp;
+          }
         }
-        const double tw = wave_sum((double)sw);
-        const double tp = wave_sum((double)spt);
-        if (lane == 0) {
-          part[wave][i0 + u][0] = tw;
-          part[wave][i0 + u][1] = tp;
+      } else {
+        // (max, sum of exp(x - max)) of the chunk's target logits, per wave.
+#pragma unroll
+        for (int u = 0; u < kU; ++u) {
+          if (i0 + u >= nq) break;
+          const float mw =
+              wave_max(fmaxf(fmaxf(tv[u][0], tv[u][1]), fmaxf(tv[u][2], tv[u][3])));
+          float sx = 0.f;
+          if (mw != -INFINITY) {
+#pragma unroll
+            for (int k = 0; k < 4; ++k) sx += fast_exp2((tv[u][k] - mw) * kLog2e);
+          }
+          const double sw = wave_sum((double)sx);
+          if (lane == 0) {
+            part[wave][i0 + u][0] = (double)mw;
+            part[wave][i0 + u][1] = sw;
+          }
         }
       }
     }
     __syncthreads();
     if (tid < nq) {
-      double tw = 0.0, tp = 0.0;
+      double x0 = 0.0, x1 = 0.0;
+      if (row_stats) {
 #pragma unroll
-      for (int w = 0; w < kSampleThreads / kWave; ++w) {
-        tw += part[w][tid][0];
-        tp += part[w][tid][1];
+        for (int w = 0; w < kSampleThreads / kWave; ++w) {
+          x0 += part[w][tid][0];
+          x1 += part[w][tid][1];
+        }
+      } else {
+        x0 = -INFINITY;
+#pragma unroll
+        for (int w = 0; w < kSampleThreads / kWave; ++w) x0 = fmax(x0, part[w][tid][0]);
+        if (x0 != -INFINITY) {
+#pragma unroll
+          for (int w = 0; w < kSampleThreads / kWave; ++w)
+            if (part[w][tid][0] != -INFINITY)
+              x1 += part[w][tid][1] * exp2((part[w][tid][0] - x0) * (double)kLog2e);
+        }
       }
       double* o = a.race_w + ((size_t)b * a.n_race + qb + tid) * 2;
-      store_coherent(o, tw);
-      store_coherent(o + 1, tp);
+      store_coherent(o, x0);
+      store_coherent(o + 1, x1);
     }
     __syncthreads();
   }
 
   // The group that completes the sequence's masses runs the draw.
   if (!last_of_group(a.arrive + (size_t)b * kArriveStride, grp, a.n_groups, a.dev_err)) return;
+  if (!row_stats && !bad) {
+    // The stop row's log-normaliser from its race chunks' (max, sum), then
+    // each chunk's target mass sum exp(x - lz) in place of the pair.
+    __shared__ double redn[4];
+    __shared__ float redm[4];
+    double* rw = a.race_w + (size_t)b * a.n_race * 2;
+    float mx = -INFINITY;
+    for (int q = tid; q < a.n_race; q += kSampleThreads) mx = fmaxf(mx, (float)load_coherent(rw + 2 * q));
+    mx = block_max(mx, redm);
+    double sum = 0.0;
+    if (mx != -INFINITY)
+      for (int q = tid; q < a.n_race; q += kSampleThreads) {
+        const double mq = load_coherent(rw + 2 * q);
+        if (mq != -INFINITY) sum += load_coherent(rw + 2 * q + 1) * exp(mq - (double)mx);
+      }
+    sum = block_sum(sum, redn);
+    lzt = (double)mx + log(sum);
+    for (int q = tid; q < a.n_race; q += kSampleThreads) {
+      const double mq = load_coherent(rw + 2 * q);
+      const double w = mq == -INFINITY ? 0.0 : load_coherent(rw + 2 * q + 1) * exp(mq - lzt);
+      store_coherent(rw + 2 * q, 0.0);
+      store_coherent(rw + 2 * q + 1, w);
+    }
+    __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0): the masses are stored
+    __syncthreads();
+  }
   StopView sv;
   if constexpr (FROM_RECORD) {
     const int32_t* dec = a.decision + (size_t)b * a.dec_stride;

@@ -102,6 +102,9 @@ struct SampleArgs {
   int32_t n_groups;        // resample work-groups per sequence
   int32_t logits_bf16;
   int32_t lossless;        // siblings tested against successively updated residuals
+  int32_t leaf_rows;       // 1: the statistics kernel also streams the target rows of
+                           // leaves; 0: a leaf's target row is read only when the walk
+                           // stops there (its statistics then come from the residual pass)
   int32_t* dev_err;
 };
 
@@ -109,7 +112,9 @@ constexpr int kDecisionDoubles = 8;
 
 struct SamplePlan {
   int32_t n_vchunks, vchunk, n_race, n_groups, dec_stride;
-  size_t off_m, off_s, off_g, off_w, off_dec, off_lz, bytes;   // arrival counters at offset 0
+  // The arrival counters fill [0, off_m); then the row partials, gathered
+  // token logits, race-chunk masses and the decision records.
+  size_t off_m, off_s, off_g, off_w, off_dec, off_lz, bytes;
 };
 
 SamplePlan plan_sample(int32_t B, int32_t N, int32_t V);

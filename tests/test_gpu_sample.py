@@ -60,6 +60,14 @@ CASES = [
     ("chain_sharp", 64, 5, 30000, False, 40.0, 2.0, None),
     # a vocabulary one id past a multiple of four at full size: the scalar paths
     ("b8_chain_v128257_scalar", 8, 5, 128257, False, 3.0, 1.0, None),
+    # long chains and a wide tree over mid-size vocabularies: residual
+    # groups owning several race chunks, bonus draws whose leaf row is read
+    # only by the residual pass
+    ("b4_chain40_v65536", 4, 40, 65536, False, 3.0, 1.0, None),
+    ("b3_tree64_v32768", 3, 64, 32768, True, 3.0, 1.0, None),
+    # draft = target: every draft accepted, every draw a bonus from a leaf
+    # row whose statistics the residual pass gathers
+    ("b32_chain_all_accepted_v50000", 32, 5, 50000, False, 3.0, 0.0, None),
 ]
 
 

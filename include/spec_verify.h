@@ -59,6 +59,10 @@
 extern "C" {
 #endif
 
+/* Every enum below also lists a least and a greatest int32 value (not
+ * meaningful codes): the enum's range is then all of int32, so any integer a
+ * caller passes is a valid value of the type, and the library can refuse the
+ * unlisted ones with SPEC_ERR_INVALID_ARG. */
 typedef enum {
   SPEC_OK = 0,
   SPEC_ERR_INVALID_ARG = 1, /* a size, count or enum is out of range */
@@ -66,15 +70,24 @@ typedef enum {
   SPEC_ERR_BAD_TREE = 3,    /* host-side parent array is not a valid tree */
   SPEC_ERR_MISALIGNED = 4,  /* a required pointer is NULL or misaligned */
   SPEC_ERR_WORKSPACE = 5,   /* workspace missing or smaller than required */
-  SPEC_ERR_HIP = 6          /* a HIP launch failed (hipGetLastError) */
+  SPEC_ERR_HIP = 6,         /* a HIP launch failed (hipGetLastError) */
+  SPEC_STATUS_RANGE_MIN = -2147483647 - 1,
+  SPEC_STATUS_RANGE_MAX = 2147483647
 } spec_status_t;
 
-typedef enum { SPEC_F32 = 0, SPEC_BF16 = 1 } spec_dtype_t;
+typedef enum {
+  SPEC_F32 = 0,
+  SPEC_BF16 = 1,
+  SPEC_DTYPE_RANGE_MIN = -2147483647 - 1,
+  SPEC_DTYPE_RANGE_MAX = 2147483647
+} spec_dtype_t;
 
 /* How siblings of a candidate tree are tested (spec_sample_ex). */
 typedef enum {
-  SPEC_SIBLINGS_FIRST = 0,   /* every node against the target row; first passing child */
-  SPEC_SIBLINGS_LOSSLESS = 1 /* in order, against residuals updated after each rejection */
+  SPEC_SIBLINGS_FIRST = 0,    /* every node against the target row; first passing child */
+  SPEC_SIBLINGS_LOSSLESS = 1, /* in order, against residuals updated after each rejection */
+  SPEC_SIBLINGS_RANGE_MIN = -2147483647 - 1,
+  SPEC_SIBLINGS_RANGE_MAX = 2147483647
 } spec_sibling_rule_t;
 
 /* Bits OR-ed into *dev_err by the kernels. */

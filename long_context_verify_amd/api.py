@@ -19,7 +19,8 @@ import numpy as np
 import torch
 
 HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(HERE, "libspecverify.so")
+# SPECVERIFY_LIB selects another build of the same library (the sanitized one).
+LIB_PATH = os.environ.get("SPECVERIFY_LIB") or os.path.join(HERE, "libspecverify.so")
 HEADER = os.path.join(os.path.dirname(HERE), "include", "spec_verify.h")
 
 SPEC_F32, SPEC_BF16 = 0, 1

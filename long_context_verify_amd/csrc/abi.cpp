@@ -78,6 +78,7 @@ const char* spec_status_str(spec_status_t status) {
     case SPEC_ERR_MISALIGNED: return "SPEC_ERR_MISALIGNED";
     case SPEC_ERR_WORKSPACE: return "SPEC_ERR_WORKSPACE";
     case SPEC_ERR_HIP: return "SPEC_ERR_HIP";
+    default: break;
   }
   return "SPEC_ERR_UNKNOWN";
 }

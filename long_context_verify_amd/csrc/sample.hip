@@ -1315,9 +1315,8 @@ __global__ __launch_bounds__(kSampleThreads) void draft_partial(DraftArgs a) {
     const uint32_t w[4] = {c0, c1, c2, c3};
 #pragma unroll
     for (int k = 0; k < 4; ++k) {
-      // (2 (w >> 9) + 1) 2^-24 is exact in fp32 and lies in (0, 1).
-      const float u = (float)(2u * (w[k] >> 9) + 1u) * 5.9604644775390625e-08f;
-      const float e = -__builtin_amdgcn_logf(u) * 0.6931471805599453f;   // -ln U
+      // E = -ln U within 2e-6 relative, also for U near 1 (a series there).
+      const float e = race_e32(w[k]);
       word[4 * i + k] = w[k];
       s32[4 * i + k] = lraw[4 * i + k] - __builtin_amdgcn_logf(e) * 0.6931471805599453f;
       m32 = fmaxf(m32, s32[4 * i + k]);   // ids past V carry -inf

@@ -23,6 +23,15 @@ def tol_for(dtype):
     return (1e-5, 1e-5) if dtype == torch.float32 else (2e-2, 1e-2)
 
 
+# bf16 outputs are also held, per (sequence, query head), to a bound scaled by
+# that head's largest reference output: max |o_gpu - o_ref| <= TAU_BF16 *
+# max |o_ref|.  The kernel rounds P to bf16 for the PV product and O to bf16
+# on output, each a relative 2^-9; TAU_BF16 = 2^-5 leaves a factor 16 for
+# their sum over a row.  With N(0, 1) inputs |o| shrinks like 1/sqrt(L), so
+# at long contexts this bound is tens of times tighter than 2e-2 absolute.
+TAU_BF16 = 2.0 ** -5
+
+
 def assert_attention_close(o_gpu, lse_gpu, o_ref, lse_ref, dtype, what=""):
     ta, tl = tol_for(dtype)
     og = cpu64(o_gpu)
@@ -31,6 +40,15 @@ def assert_attention_close(o_gpu, lse_gpu, o_ref, lse_ref, dtype, what=""):
     if dtype == torch.bfloat16:
         rel = np.linalg.norm(og - o_ref) / max(np.linalg.norm(o_ref), 1e-30)
         assert rel <= 1e-2, f"{what}: relative Frobenius error {rel:.3e} > 1e-2"
+        d = np.abs(og - o_ref).reshape(og.shape[0] * og.shape[1], -1).max(axis=1)
+        ref = np.abs(o_ref).reshape(og.shape[0] * og.shape[1], -1).max(axis=1)
+        scaled = d / np.maximum(ref, 1e-30)
+        worst = int(np.argmax(scaled))
+        print(f"[err] {what}: max abs {err:.3e}, max per-head abs / max|ref| {scaled[worst]:.3e} "
+              f"(bound {TAU_BF16:.3e})", flush=True)
+        assert np.all(d <= TAU_BF16 * ref + 1e-7), (
+            f"{what}: head {worst}: max abs error {d[worst]:.3e} > {TAU_BF16:.3e} x max|ref| "
+            f"{ref[worst]:.3e}")
     if lse_gpu is not None:
         le = np.max(np.abs(cpu64(lse_gpu) - lse_ref))
         assert le <= tl, f"{what}: max abs lse error {le:.3e} > {tl}"

@@ -108,3 +108,33 @@ def test_draft_sample_degenerate_rows():
     l = lp.cpu().numpy()
     assert l[0] == 0.0 and l[1] == 0.0 and np.isnan(l[2])
     assert abs(l[3] - np.log(0.1)) <= LOGPROB_TOL
+
+
+def test_draft_winner_with_uniform_near_one():
+    """Rows whose winning id has U > 1 - 2^-20, so E = -ln U < 2^-20: the
+    kernel's fp32 screen (which keeps each thread's candidates within a small
+    margin of its best fp32 score) must evaluate that E accurately.  With equal
+    logits the winner is the id with the largest U; the seed is chosen on the
+    CPU with the oracle's generator so that several rows have such an id."""
+    import long_context_verify_amd as L
+    from oracle.sample import uniforms
+    say("draft_sample U near 1")
+    B, V, node, offset, seed = 64, 128256, 1, 3, 0x5EED2026
+    ids = np.arange(V)
+    near = []
+    for b in range(B):
+        u = uniforms(seed, ids // 4, node, b, 4 * offset + 1, ids % 4)
+        if u.max() > 1.0 - 2.0 ** -20:
+            near.append((b, int(np.argmax(u))))
+    assert len(near) >= 3, f"seed gives only {len(near)} rows with U > 1 - 2^-20"
+    for name, logits in (("equal", torch.zeros(B, V)),
+                         ("near-equal", torch.randn(B, V, generator=torch.Generator().manual_seed(5))
+                          * 1e-3)):
+        lg = logits.float().to(DEV)
+        tok, lp = L.draft_sample(lg, node, seed=seed, offset=offset)
+        torch.cuda.synchronize()
+        ref = oracle_draft(lg, seed, offset, node)
+        _check(tok.cpu().numpy(), lp.cpu().numpy(), ref, f"U near 1, {name} logits")
+        if name == "equal":
+            for b, x in near:
+                assert int(tok[b].item()) == x == int(ref["token"][b]), f"row {b}"

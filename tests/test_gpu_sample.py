@@ -2,10 +2,13 @@
 
 Bar: with the same Philox uniforms, accept decisions, counts, paths and drawn
 tokens are bit-exact, except in sequences where the oracle marks a
-floating-point near-tie (|ratio - u| <= 1e-6 on a decisive node, a race
-top-2 score ratio <= 1 + 1e-5, or a residual mass <= 1e-6).  Per-node
-accept flags are compared on every node whose |ratio - u| > 1e-6.  At most
-1% of sequences may be exempt.
+floating-point near-tie.  The stated tolerance exempts only an acceptance
+ratio within 1e-6 of its uniform on a decisive node; the oracle also marks a
+race whose two best scores are within a factor 1 + 1e-5 and a residual mass
+at or below 1e-6 (a deviation from the stated tolerance, kept because fp32
+chunk sums decide there).  Every fixed-seed case here prints its exempt
+sequences by cause and requires none: all of them are compared bit for bit.
+Per-node accept flags are compared on every node whose |ratio - u| > 1e-6.
 """
 
 import numpy as np
@@ -13,7 +16,7 @@ import pytest
 import torch
 from scipy import stats
 
-from oracle.sample import softmax, spec_sample as oracle_sample
+from oracle.sample import RACE_MARGIN, WSUM_FLOOR, softmax, spec_sample as oracle_sample
 from tests.gpu_util import say
 from workloads import CONFIGS, make_sample_inputs, random_tree
 
@@ -29,9 +32,26 @@ def _gpu(x, parent, seed, offset, siblings="first"):
     return {k: v.cpu().numpy() for k, v in r.items()}
 
 
-def _compare(g, o, what):
+def _exempt_kinds(o):
+    """Split the oracle's exempt sequences by cause: an acceptance ratio within
+    1e-6 of its uniform (the stated tolerance), a race whose two best scores
+    are within a factor 1 + 1e-5, or a residual mass at or below 1e-6."""
+    race = (o["margin1"] <= 1.0 + RACE_MARGIN) | (o["margin2"] <= 1.0 + RACE_MARGIN)
+    mass = o["residual"] & (o["wsum"] <= WSUM_FLOOR)
+    tie = o["exempt"] & ~race & ~mass
+    return tie, race & o["exempt"], mass & o["exempt"]
+
+
+def _compare(g, o, what, max_exempt=0):
+    """Bit-exact comparison of every non-exempt sequence.  The inputs are
+    fixed-seed, so the exempt count is fixed too: it is printed by cause and
+    must not exceed max_exempt (0 everywhere: no case here sits near a tie)."""
     ex = o["exempt"]
-    assert ex.mean() <= 0.01 + 1e-12 or ex.sum() <= 1, f"{what}: {ex.sum()} exempt sequences"
+    tie, race, mass = _exempt_kinds(o)
+    print(f"[exempt] {what}: {int(ex.sum())} of {ex.size} sequences (ratio near-tie "
+          f"{int(tie.sum())}, race margin {int(race.sum())}, small residual mass "
+          f"{int(mass.sum())})", flush=True)
+    assert ex.sum() <= max_exempt, f"{what}: {ex.sum()} exempt sequences"
     ok = ~ex
     for key in ("out_tokens", "out_count", "out_path"):
         bad = np.nonzero(np.any(np.atleast_2d(g[key][ok] != o[key][ok]).reshape(ok.sum(), -1),

@@ -23,7 +23,7 @@
 //                  and acceptance test per node, the walk from the root: a few
 //                  hundred scalars, two memory round trips), then the residual
 //                  (or target) mass of its 1024-id race chunks of the stop
-//                  row, all of its chunks' loads in one round.  When the walk
+//                  row (the loads of four chunks in flight at once).  When the walk
 //                  ends at a leaf whose target row the first kernel skipped,
 //                  the groups gather that row's per-chunk (max, sum) instead,
 //                  so a leaf row is read once, and only when it is drawn from.
@@ -953,7 +953,7 @@ __global__ __launch_bounds__(kSampleThreads) void sample_resid(SampleArgs a) {
   // partial sums in LDS; one block pass per batch of chunks adds the waves.
   // The loads of kU chunks are issued together (a group may own several).
   constexpr int kBatch = 64;
-  constexpr int kU = 8;
+  constexpr int kU = 4;
   __shared__ double part[kSampleThreads / kWave][kBatch][2];
   const int wave = tid >> 6, lane = tid & 63;
   for (int qb = q0; qb < q1; qb += kBatch) {

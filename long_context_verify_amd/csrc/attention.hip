@@ -629,21 +629,38 @@ __global__ __launch_bounds__(NW * kWave, 8 / NW) void attn_split_mfma(AttnArgs a
 //
 // Each wave owns 32 query rows (two MFMA blocks, Q in registers); the
 // work-group covers WAVES*32 rows of one (sequence, kv head) unit, so one
-// pass over the keys serves them all.  Chunks of 64 keys (32 KB) are copied
-// HBM -> LDS with direct-to-LDS loads (global_load_lds_dwordx4: lane l's 16
-// bytes land at base + 16 l), two chunks ahead of the one being computed,
-// into a ring of three tiles; one barrier per chunk.  A tile holds
-//   K: 64 rows x 256 B, 16-byte pieces XOR-swizzled by row (loaded as 1 KB
-//      contiguous runs; the A operand of lane (h,r), K[16 kb + r][32 s + 8 h
-//      .. +8], is one conflict-free 16-byte read);
-//   V: 64 rows x 256 B, 32-byte granules XOR-swizzled by row -- each wave
-//      builds its MFMA operands with gfx950's transposing LDS reads
+// pass over the keys serves them all.  Chunks of 64 keys are copied HBM ->
+// LDS with direct-to-LDS loads (global_load_lds_dwordx4: lane l's 16 bytes
+// land at base + 16 l), the K rows into one ring of 16 KB tiles and the V
+// rows into another:
+//   K tile: 64 rows x 256 B, 16-byte pieces XOR-swizzled by row (loaded as
+//      1 KB contiguous runs; the A operand of lane (h,r), K[16 kb + r][32 s +
+//      8 h .. +8], is one conflict-free 16-byte read);
+//   V tile: 64 rows x 256 B, 32-byte granules XOR-swizzled by row -- each
+//      wave builds its MFMA operands with gfx950's transposing LDS reads
 //      (ds_read_b64_tr_b16), so no register transpose is needed.
-// A chunk is two 32-key halves; the softmax of a row runs once per chunk over
-// its 16 scores per lane.  The running max is only moved (and O rescaled)
-// when a chunk exceeds it by more than 2^8 (log2 domain); otherwise the
-// exponentials are taken against the old max and stay below 256, which keeps
-// the rescale off the VALU in the common case.
+//
+// Per chunk c a wave runs an MFMA block M_c = {O += V_{c-1}^T P_{c-1}^T,
+// S_c = K_c Q^T} and a VALU block X_c = {softmax of S_c -> P_c}; the PV
+// product of a chunk is deferred into the next chunk's MFMA block.  The
+// work-group has one barrier per chunk, B_c (chunk c is in LDS; the tile of
+// chunk c-2 is free for the load of chunk c+2).  Waves 0-3 pass B_c right
+// before M_c; waves 4-7 right before X_{c-1}, i.e. half a chunk earlier in
+// their own program.  Waves are placed on the four SIMDs in turn, so each
+// SIMD holds one wave of each group, and the barrier keeps them in opposite
+// phases: while one runs its MFMA block the other runs its softmax.  Either
+// way every wave reads only K tile c and V tile c-1 between B_c and B_{c+1},
+// so each ring needs one tile being read and the rest can be in flight: with
+// five tiles per ring (160 KB) the K of chunks c+1..c+4 and the V of chunks
+// c..c+3 are in flight, 128 KB per CU, twice what one ring of whole chunks
+// leaves room for.
+//
+// The softmax of a row runs once per chunk over its 16 scores per lane.  The
+// running max is only moved (and O rescaled) when a chunk exceeds it by more
+// than 2^8 (log2 domain); otherwise the exponentials are taken against the
+// old max and stay below 256, which keeps the rescale off the VALU in the
+// common case.  Row sums of P come from one more MFMA per 32 keys with an
+// all-ones A operand, so they sum exactly the bf16 weights that multiply V.
 // ---------------------------------------------------------------------------
 typedef short v4i16 __attribute__((ext_vector_type(4)));
 typedef short v8i16 __attribute__((ext_vector_type(8)));
@@ -655,7 +672,8 @@ __device__ __forceinline__ int v_swizzle(int row) { return (row & 7) << 1; }
 __device__ __forceinline__ int k_swizzle(int row) { return row & 15; }
 
 constexpr int kTreeChunk = 64;        // keys per chunk
-constexpr int kTreeNBuf = 3;          // LDS tiles in the ring
+constexpr int kTreeNK = 5;            // K tiles in the ring
+constexpr int kTreeNV = 5;            // V tiles in the ring (4 with a page table in LDS)
 constexpr float kRescaleTau = 8.0f;   // log2 units
 
 __device__ __forceinline__ void lds_dma16(const void* src, void* lds_base) {
@@ -670,27 +688,41 @@ __device__ __forceinline__ void wait_vmcnt(int n) {
     case 0: __builtin_amdgcn_s_waitcnt(0x0F70); break;
     case 4: __builtin_amdgcn_s_waitcnt(0x0F74); break;
     case 8: __builtin_amdgcn_s_waitcnt(0x0F78); break;
+    case 12: __builtin_amdgcn_s_waitcnt(0x0F7C); break;
     default: __builtin_amdgcn_s_waitcnt(0x0F70); break;
   }
 }
 
+template <bool B>
+struct MaskTag {
+  static constexpr bool value = B;
+};
+
 template <int WAVES, bool PAGED = false>
 __global__ __launch_bounds__(WAVES * kWave, 1) void attn_tree_mfma(AttnArgs a) {
+  static_assert(WAVES == 8, "two groups of four waves: one wave of each group per SIMD");
   constexpr int D = 128, DS = 4, QB = 2;
   constexpr int SR = WAVES * 32;              // query rows per work-group
-  constexpr int TILE = 32768;                 // bytes per chunk (K 16 KB + V 16 KB)
   constexpr int UPW = 32 / WAVES;             // 1 KB load units per wave per chunk
-  __shared__ __attribute__((aligned(16))) char tiles[kTreeNBuf][TILE];
+  constexpr int NK = kTreeNK;
+  constexpr int NV = PAGED ? kTreeNV - 1 : kTreeNV;
+  __shared__ __attribute__((aligned(16))) char ktiles[NK][16384];
+  __shared__ __attribute__((aligned(16))) char vtiles[NV][16384];
   __shared__ int32_t lds_pages[PAGED ? kPageCap : 1];
 
   int unit, split, qs;
   if (!decode_tile(a, unit, split, qs)) return;
   const int lane = threadIdx.x & 63;
-  const int wave = threadIdx.x >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  // Waves 4-7 take each barrier before their softmax block instead of their
+  // MFMA block.  They also copy the V rows of every chunk, waves 0-3 the K rows.
+  const bool late = wave >= WAVES / 2;
   const int r = lane & 15;
   const int h = lane >> 4;
   const size_t row_bytes = (size_t)D * 2;
   const UnitGeom u = unit_geom<false>(a, unit, split == 0 && qs == 0 && threadIdx.x == 0);
+  const int n_keys = __builtin_amdgcn_readfirstlane(u.n_keys);
+  const int p0 = __builtin_amdgcn_readfirstlane(u.p0);
 
   const char* qbase = static_cast<const char*>(a.q) +
                       ((size_t)(u.b * a.Hq + u.hk * a.g) * a.n_q) * row_bytes;
@@ -711,84 +743,84 @@ __global__ __launch_bounds__(WAVES * kWave, 1) void attn_tree_mfma(AttnArgs a) {
   }
 
   // This split's range of 64-key chunks.
-  const long long nch = (u.n_keys + kTreeChunk - 1) / kTreeChunk;
+  const long long nch = (n_keys + kTreeChunk - 1) / kTreeChunk;
   const int c0 = (int)(nch * split / a.n_splits);
   int c1 = (int)(nch * (split + 1) / a.n_splits);
-  const int last = u.n_keys - 1;
+  const int last = n_keys - 1;
   int pfirst = 0;
   if constexpr (PAGED) {
-    if (!stage_pages<PAGED>(a, u, c0 * kTreeChunk, min(c1 * kTreeChunk, u.n_keys), lds_pages,
+    if (!stage_pages<PAGED>(a, u, c0 * kTreeChunk, min(c1 * kTreeChunk, n_keys), lds_pages,
                             pfirst))
       c1 = c0;
   }
 
-  // This wave's share of one chunk: UPW 1 KB units out of 32 (16 K + 16 V).
-  const char* kbase_p = static_cast<const char*>(a.k) + (size_t)u.unit * a.L_cap * row_bytes;
-  const char* vbase_p = static_cast<const char*>(a.v) + (size_t)u.unit * a.L_cap * row_bytes;
-  auto issue = [&](int c, int buf) {
-    const int kbase = c * kTreeChunk;
-    char* tile = tiles[buf];
-    // Keys key0 .. of this chunk are consecutive rows from kc / vc: the unit's
-    // stream in a contiguous cache, or the chunk's page (one lookup per chunk).
-    const char* kc = kbase_p;
-    const char* vc = vbase_p;
-    int key0 = 0;
-    if constexpr (PAGED) {
-      kc = cache_row<PAGED>(a, u, kbase, 0, row_bytes, lds_pages, pfirst);
-      vc = cache_row<PAGED>(a, u, kbase, 1, row_bytes, lds_pages, pfirst);
-      key0 = kbase;
-    }
+  // This wave's share of a chunk: UPW 1 KB units (4 rows each) of the K rows
+  // (waves 0-3) or the V rows (waves 4-7).  Slot (lane & 15) of a row takes the
+  // 16-byte piece (lane & 15) ^ swizzle(row), so the operand reads below (16
+  // rows, same column) hit distinct banks.  The offsets are loop-invariant.
+  const bool dma_v = late;
+  int drow[UPW];
+  uint32_t doff[UPW];
 #pragma unroll
-    for (int i = 0; i < UPW; ++i) {
-      const int unit_id = wave * UPW + i;
-      if (unit_id < 16) {     // K rows 4 unit_id .. +3: 1 KB contiguous per instruction
-        const int krow = 4 * unit_id + (lane >> 4);
-        int key = kbase + krow;
-        key = key < last ? key : last;
-        // Slot (lane & 15) of the row takes the 16-byte piece (lane & 15) ^ (row % 16),
-        // so the operand reads below (16 rows, same column) hit distinct banks.
-        const int piece = (lane & 15) ^ k_swizzle(krow);
-        lds_dma16(kc + (size_t)(key - key0) * row_bytes + piece * 16, tile + unit_id * 1024);
-      } else {                // V rows 4 (unit_id - 16) .. +3, 16 lanes per row
-        const int vrow = 4 * (unit_id - 16) + (lane >> 4);
-        int key = kbase + vrow;
-        key = key < last ? key : last;
-        // Slot (lane & 15) of the row takes the 16-byte piece whose 32-byte
-        // granule is XOR-swizzled by the row, so transposed reads of 16 rows
-        // spread over all banks.
-        const int piece = (lane & 15) ^ v_swizzle(vrow);
-        lds_dma16(vc + (size_t)(key - key0) * row_bytes + piece * 16, tile + unit_id * 1024);
+  for (int i = 0; i < UPW; ++i) {
+    const int row = 4 * ((wave * UPW + i) & 15) + (lane >> 4);
+    const int piece = (lane & 15) ^ (dma_v ? v_swizzle(row) : k_swizzle(row));
+    drow[i] = row;
+    doff[i] = (uint32_t)(row * 256 + piece * 16);
+  }
+  const char* dsrc =
+      static_cast<const char*>(dma_v ? a.v : a.k) + (size_t)u.unit * a.L_cap * row_bytes;
+  auto issue = [&](int c) {
+    const int kbase = c * kTreeChunk;
+    char* dst = (dma_v ? vtiles[c % NV] : ktiles[c % NK]) + ((wave * UPW) & 15) * 1024;
+    // Keys kbase .. kbase+63 are consecutive rows from src: the unit's stream
+    // in a contiguous cache, or the chunk's page (one lookup per chunk).
+    const char* src = PAGED ? cache_row<PAGED>(a, u, kbase, dma_v ? 1 : 0, row_bytes, lds_pages,
+                                               pfirst)
+                            : dsrc + (size_t)kbase * row_bytes;
+    if (kbase + kTreeChunk <= n_keys) {
+#pragma unroll
+      for (int i = 0; i < UPW; ++i) lds_dma16(src + doff[i], dst + i * 1024);
+    } else {
+      // Last, partial chunk: rows past the end repeat the last key (masked below).
+#pragma unroll
+      for (int i = 0; i < UPW; ++i) {
+        const int key = min(kbase + drow[i], last);
+        lds_dma16(src + (size_t)(key - kbase) * row_bytes + (doff[i] & 255u), dst + i * 1024);
       }
     }
   };
+  // Barrier B_k.  Before it, this wave's copies of the tile read next have
+  // landed: K of chunk k (waves 0-3; up to NK-2 later K tiles may still be in
+  // flight) or V of chunk k-1 (waves 4-7; up to NV-2 later V tiles).  After
+  // it, the copy of K chunk k+NK-1 goes into the tile K chunk k-1 used, or of
+  // V chunk k+NV-2 into the tile V chunk k-2 used.
+  auto sync = [&](int k) {
+    const int after = dma_v ? min(NV - 2, c1 - k) : min(NK - 2, c1 - 1 - k);
+    wait_vmcnt(UPW * max(after, 0));
+    __syncthreads();
+    const int next = dma_v ? k + NV - 2 : k + NK - 1;
+    if (next < c1) issue(next);
+  };
 
-  float m[QB], lsum[QB];
+  float m[QB];
+  f32x4 lacc[QB];
   f32x4 oacc[QB][8];
+  f32x4 sacc[QB][4];
+  bf16x8 pop[QB][2];
 #pragma unroll
   for (int qb = 0; qb < QB; ++qb) {
     m[qb] = -INFINITY;
-    lsum[qb] = 0.f;
+    lacc[qb] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int j = 0; j < 8; ++j) oacc[qb][j] = f32x4{0.f, 0.f, 0.f, 0.f};
   }
+  const bf16x8 ones = __builtin_bit_cast(
+      bf16x8, u32x4{0x3F803F80u, 0x3F803F80u, 0x3F803F80u, 0x3F803F80u});
 
-#pragma unroll
-  for (int i = 0; i < kTreeNBuf - 1; ++i)
-    if (c0 + i < c1) issue(c0 + i, (c0 + i) % kTreeNBuf);
-
-  for (int c = c0; c < c1; ++c) {
-    // Chunks issued after c by this wave so far: min(NBUF-2, c1-1-c), UPW loads each.
-    const int ahead = min(kTreeNBuf - 2, c1 - 1 - c);
-    wait_vmcnt(ahead * UPW);
-    __syncthreads();   // chunk c is in LDS for every wave; all waves are past chunk c-1
-    if (c + kTreeNBuf - 1 < c1) issue(c + kTreeNBuf - 1, (c + kTreeNBuf - 1) % kTreeNBuf);
-    if (!wave_live) continue;
-
-    const char* tile = tiles[c % kTreeNBuf];
-    const int kbase = c * kTreeChunk;
-
-    // S^T for both 32-key halves: sacc[qb][kb][e] = score(key 16 kb + 4 h + e, row qb*16 + r).
-    f32x4 sacc[QB][4];
+  // S^T for both 32-key halves of a chunk: sacc[qb][kb][e] = score(key 16 kb + 4 h + e,
+  // row qb*16 + r).
+  auto qk = [&](const char* tile) {
 #pragma unroll
     for (int half = 0; half < 2; ++half) {
       bf16x8 kop[2][DS];
@@ -810,65 +842,20 @@ __global__ __launch_bounds__(WAVES * kWave, 1) void attn_tree_mfma(AttnArgs a) {
         sacc[qb][2 * half + 1] = acc1;
       }
     }
+  };
 
-    const bool need_mask = kbase + kTreeChunk > u.p0;
-    bf16x8 pop[QB][2];
-#pragma unroll
-    for (int qb = 0; qb < QB; ++qb) {
-      // Raw scores; the softmax scale (> 0, in log2 units) is applied to the
-      // max and folded into the exponent's FMA.
-      float sv[16];
-#pragma unroll
-      for (int t = 0; t < 16; ++t) sv[t] = sacc[qb][t >> 2][t & 3];
-      if (need_mask) {
-#pragma unroll
-        for (int t = 0; t < 16; ++t) {
-          const int key = kbase + 16 * (t >> 2) + 4 * h + (t & 3);
-          const int rel = key - u.p0;
-          const bool anc_ok = ((anc[qb] >> (rel & 63)) & 1ull) != 0;
-          const bool ok = key < u.n_keys && (rel < 0 || anc_ok);
-          sv[t] = ok ? sv[t] : -INFINITY;
-        }
-      }
-      float cm = sv[0];
-#pragma unroll
-      for (int t = 1; t < 16; ++t) cm = fmaxf(cm, sv[t]);
-      cm = xgroup_max(cm) * a.scale_log2;
-      const bool grow = cm > m[qb] + kRescaleTau;
-      if (__any(grow)) {
-        const float mn = grow ? cm : m[qb];
-        const float alpha = grow ? fast_exp2(m[qb] - mn) : 1.f;
-        m[qb] = mn;
-        lsum[qb] *= alpha;
-#pragma unroll
-        for (int j = 0; j < 8; ++j) oacc[qb][j] *= alpha;
-      }
-      const float mu = (m[qb] == -INFINITY) ? 0.f : m[qb];
-      float p[16];
-      float ps = 0.f;
-#pragma unroll
-      for (int t = 0; t < 16; ++t) {
-        p[t] = fast_exp2(fmaf(sv[t], a.scale_log2, -mu));
-        ps += p[t];
-      }
-      lsum[qb] += ps;
-#pragma unroll
-      for (int half = 0; half < 2; ++half) {
-        const float* ph = p + 8 * half;
-        u32x4 pk = {pack_bf16x2(ph[0], ph[1]), pack_bf16x2(ph[2], ph[3]),
-                    pack_bf16x2(ph[4], ph[5]), pack_bf16x2(ph[6], ph[7])};
-        pop[qb][half] = __builtin_bit_cast(bf16x8, pk);
-      }
-    }
-
-    // O^T += V^T P^T.  The A operand of dim block blk is, in lane (h, r),
-    // V[key(h, t)][16 blk + r] for t = 0..7 (key(h, t) = 16 (t / 4) + 4 h + t % 4
-    // within the half): two transposing LDS reads, each of four keys.  In a
-    // read, lane (h, r) points at 4 dims (16 blk + 4 (r % 4) ..) of key
-    // 4 h + r / 4 (+16 for the second), and the hardware hands lane r the
-    // dim 16 blk + r of all four keys.
+  // O^T += V^T P^T and l += 1^T P^T.  The A operand of dim block blk is, in
+  // lane (h, r), V[key(h, t)][16 blk + r] for t = 0..7 (key(h, t) = 16 (t / 4)
+  // + 4 h + t % 4 within the half): two transposing LDS reads, each of four
+  // keys.  In a read, lane (h, r) points at 4 dims (16 blk + 4 (r % 4) ..) of
+  // key 4 h + r / 4 (+16 for the second), and the hardware hands lane r the
+  // dim 16 blk + r of all four keys.
+  auto pv = [&](const char* tile) {
 #pragma unroll
     for (int half = 0; half < 2; ++half) {
+#pragma unroll
+      for (int qb = 0; qb < QB; ++qb)
+        lacc[qb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ones, pop[qb][half], lacc[qb], 0, 0, 0);
 #pragma unroll
       for (int blk = 0; blk < 8; ++blk) {
         v4i16 part[2];
@@ -876,7 +863,7 @@ __global__ __launch_bounds__(WAVES * kWave, 1) void attn_tree_mfma(AttnArgs a) {
         for (int sec = 0; sec < 2; ++sec) {
           const int vrow = 32 * half + 16 * sec + 4 * h + (r >> 2);
           const int gp = 2 * blk + ((r & 3) >> 1);          // global 16-byte piece
-          const char* src = tile + 16384 + vrow * 256 + ((gp ^ v_swizzle(vrow)) << 4) +
+          const char* src = tile + vrow * 256 + ((gp ^ v_swizzle(vrow)) << 4) +
                             ((r & 1) << 3);
           part[sec] = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
               (__attribute__((address_space(3))) v4i16*)(src));
@@ -890,7 +877,81 @@ __global__ __launch_bounds__(WAVES * kWave, 1) void attn_tree_mfma(AttnArgs a) {
               __builtin_amdgcn_mfma_f32_16x16x32_bf16(vop, pop[qb][half], oacc[qb][blk], 0, 0, 0);
       }
     }
-  }
+  };
+
+  // Scores of chunk c -> bf16 weights P_c (and the running max / rescale).
+  // Chunks that reach the block's own keys (or the end) apply the tree mask;
+  // the loop below runs the other chunks through a mask-free copy.
+  auto softmax = [&](int c, auto masked) {
+    const int kbase = c * kTreeChunk;
+    constexpr bool need_mask = decltype(masked)::value;
+#pragma unroll
+    for (int qb = 0; qb < QB; ++qb) {
+      // Raw scores; the softmax scale (> 0, in log2 units) is applied to the
+      // max and folded into the exponent's FMA.
+      float sv[16];
+#pragma unroll
+      for (int t = 0; t < 16; ++t) sv[t] = sacc[qb][t >> 2][t & 3];
+      if constexpr (need_mask) {
+#pragma unroll
+        for (int t = 0; t < 16; ++t) {
+          const int key = kbase + 16 * (t >> 2) + 4 * h + (t & 3);
+          const int rel = key - p0;
+          const bool anc_ok = ((anc[qb] >> (rel & 63)) & 1ull) != 0;
+          const bool ok = key < n_keys && (rel < 0 || anc_ok);
+          sv[t] = ok ? sv[t] : -INFINITY;
+        }
+      }
+      // The row max only matters when it passes m + tau, so each lane first
+      // tests its own 16 scores; the exact max across the row's four lanes
+      // (two cross-lane rounds) is taken only when some lane passes.
+      float lm = sv[0];
+#pragma unroll
+      for (int t = 1; t < 16; ++t) lm = fmaxf(lm, sv[t]);
+      if (__any(lm * a.scale_log2 > m[qb] + kRescaleTau)) {
+        const float cm = xgroup_max(lm) * a.scale_log2;
+        const bool grow = cm > m[qb] + kRescaleTau;
+        const float mn = grow ? cm : m[qb];
+        const float alpha = grow ? fast_exp2(m[qb] - mn) : 1.f;
+        m[qb] = mn;
+        lacc[qb] *= alpha;
+#pragma unroll
+        for (int j = 0; j < 8; ++j) oacc[qb][j] *= alpha;
+      }
+      const float mu = (m[qb] == -INFINITY) ? 0.f : m[qb];
+      float p[16];
+#pragma unroll
+      for (int t = 0; t < 16; ++t) p[t] = fast_exp2(fmaf(sv[t], a.scale_log2, -mu));
+#pragma unroll
+      for (int half = 0; half < 2; ++half) {
+        const float* ph = p + 8 * half;
+        u32x4 pk = {pack_bf16x2(ph[0], ph[1]), pack_bf16x2(ph[2], ph[3]),
+                    pack_bf16x2(ph[4], ph[5]), pack_bf16x2(ph[6], ph[7])};
+        pop[qb][half] = __builtin_bit_cast(bf16x8, pk);
+      }
+    }
+  };
+
+  // Iteration c: [B_c] M_c [B_{c+1} for waves 4-7] X_c.  The last iteration
+  // (c = c1) only adds the deferred PV product of chunk c1-1.
+  auto step = [&](int c, auto masked) {
+    if (!late) sync(c);
+    if (wave_live) {
+      if (c > c0) pv(vtiles[(c - 1) % NV]);
+      if (c < c1) qk(ktiles[c % NK]);
+    }
+    if (late && c < c1) sync(c + 1);
+    if (wave_live && c < c1) softmax(c, masked);
+  };
+  // Prologue: K chunks c0 .. c0+NK-2, V chunks c0 .. c0+NV-3.
+  const int pre = dma_v ? NV - 2 : NK - 1;
+  for (int i = 0; i < pre; ++i)
+    if (c0 + i < c1) issue(c0 + i);
+  if (late) sync(c0);
+  // Chunks below cm hold prefix keys only (every key < p0 <= n_keys).
+  const int cm = min(max(p0 / kTreeChunk, c0), c1);
+  for (int c = c0; c < cm; ++c) step(c, MaskTag<false>{});
+  for (int c = cm; c <= c1; ++c) step(c, MaskTag<true>{});
 
   if (!wave_live) return;
   // Each wave owns its rows: write them straight to the output (one split) or
@@ -900,7 +961,7 @@ __global__ __launch_bounds__(WAVES * kWave, 1) void attn_tree_mfma(AttnArgs a) {
   const size_t part = ((size_t)unit * a.n_qs + qs) * a.n_splits + split;
 #pragma unroll
   for (int qb = 0; qb < QB; ++qb) {
-    const float l = xgroup_sum(lsum[qb]);
+    const float l = lacc[qb][0];                   // every lane of a column holds the row sum
     const int srow = wave * 32 + qb * 16 + r;      // row within the slice
     const int row = qs * SR + srow;
     if (row >= a.M) continue;

@@ -967,8 +967,8 @@ __global__ __launch_bounds__(kSampleThreads) void sample_resid(SampleArgs a) {
         if (VEC4) {
           f32x4 t4 = {-INFINITY, -INFINITY, -INFINITY, -INFINITY}, d4 = t4;
           if (live && e0 < V) {
-            t4 = ld4(trow, e0);
-            if (residual) d4 = ld4(drow, e0);
+            t4 = ld4<T, true>(trow, e0);   // non-temporal: the row is read once here
+            if (residual) d4 = ld4<T, true>(drow, e0);
           }
 #pragma unroll
           for (int k = 0; k < 4; ++k) {

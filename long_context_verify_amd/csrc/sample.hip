@@ -290,6 +290,7 @@ struct Decision {
   uint8_t acc[SPEC_MAX_SAMPLE_NODES];
   int path[SPEC_MAX_SAMPLE_NODES];
   int tok[SPEC_MAX_SAMPLE_NODES];         // drafted token of each node
+  int16_t par[SPEC_MAX_SAMPLE_NODES];     // parent of each node (loaded once)
   int len, bad, stop;
   bool residual;
   double shift;                           // residual weights max(pt - shift * pd, 0)
@@ -339,10 +340,13 @@ __device__ __forceinline__ void decide_sequence(const SampleArgs& a, int b, Deci
   }
   if (tid == 0) d.bad = 0;
   for (int u = tid; u < N; u += NT) d.has_child[u] = 0;
-  if (c_tok < N) d.tok[c_tok] = x;
+  if (c_tok < N) {
+    d.tok[c_tok] = x;
+    d.par[c_tok] = (int16_t)p;
+  }
   __syncthreads();
   for (int c = 1 + tid; c < N; c += NT) {
-    const int pc = parent_of(a, b, c);
+    const int pc = c == c_tok ? p : parent_of(a, b, c);
     if (pc < 0 || pc >= c)
       d.bad = 1;
     else
@@ -441,7 +445,7 @@ __device__ __forceinline__ void decide_sequence(const SampleArgs& a, int b, Deci
         int nxt = -1;
         for (int base = cur + 1; base < N && nxt < 0; base += kWave) {
           const int c = base + tid;
-          const bool hit = c < N && d.acc[c] && parent_of(a, b, c) == cur;
+          const bool hit = c < N && d.acc[c] && d.par[c] == cur;
           const unsigned long long ball = __ballot(hit);
           if (ball) nxt = base + __ffsll((long long)ball) - 1;
         }

@@ -676,9 +676,21 @@ constexpr int kTreeNK = 5;            // K tiles in the ring
 constexpr int kTreeNV = 5;            // V tiles in the ring (4 with a page table in LDS)
 constexpr float kRescaleTau = 8.0f;   // log2 units
 
+// The copy is issued as inline assembly on purpose: the compiler treats a
+// direct-to-LDS load as a pending write to every LDS location, and before the
+// next LDS read it would wait for all loads in flight (vmcnt(0)), chunks
+// copied ahead included, which serialises the copies with the compute.  The
+// kernel orders its tiles itself: an explicit vmcnt wait on this wave's own
+// copies, then a work-group barrier, before any wave reads a tile.  M0 holds
+// the (wave-uniform) LDS destination; one wait state separates its write from
+// the load that reads it.
 __device__ __forceinline__ void lds_dma16(const void* src, void* lds_base) {
-  __builtin_amdgcn_global_load_lds(src, (__attribute__((address_space(3))) void*)lds_base, 16, 0,
-                                   0);
+  const uint32_t lds = __builtin_amdgcn_readfirstlane(
+      (uint32_t)(uintptr_t)(__attribute__((address_space(3))) char*)lds_base);
+  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off"
+               :
+               : "v"(src), "s"(lds)
+               : "memory", "m0");
 }
 
 // Wait until at most n of this wave's vector-memory operations are pending

@@ -955,7 +955,11 @@ __global__ __launch_bounds__(WAVES * kWave, 1) void attn_tree_mfma(AttnArgs a) {
     if (late && c < c1) sync(c + 1);
     if (wave_live && c < c1) softmax(c, masked);
   };
-  // Prologue: K chunks c0 .. c0+NK-2, V chunks c0 .. c0+NV-3.
+  // Prologue: K chunks c0 .. c0+NK-2, V chunks c0 .. c0+NV-3.  The Q,
+  // ancestor and page-table loads are waited for first: the compiler does
+  // not see the copies (inline assembly), so otherwise it would wait for
+  // every load in flight, copies included, at the first use of Q per chunk.
+  __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0)
   const int pre = dma_v ? NV - 2 : NK - 1;
   for (int i = 0; i < pre; ++i)
     if (c0 + i < c1) issue(c0 + i);

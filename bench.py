@@ -176,7 +176,15 @@ class Timer:
                 prep()
         t_all = self._bracket(with_call, n)
         t_base = self._bracket(without, n)
-        return max(t_all - t_base, 0.0)
+        if t_all - t_base > 0.0:
+            return t_all - t_base
+        # The difference can vanish under a profiler that serialises kernels
+        # (counter collection); then report back-to-back calls, never zero.
+        def call(i):
+            if prep:
+                prep()
+            fn(i)
+        return self._bracket(call, n)
 
 
 def stream_rates(dev, timer, mib=2048, reps=10):

@@ -28,8 +28,12 @@
 //     work-group that completes a unit's last split (an arrival counter per
 //     unit in the workspace) combines them in a fixed order.
 //
+// Wide query blocks (candidate trees with g * n_q > 32 rows) go to a second
+// bf16 kernel, attn_tree_mfma below, in which all waves of a work-group share
+// each K/V chunk through LDS instead of streaming it once per 32-row slice.
+//
 // The fp32 path is a plain VALU kernel (one wave per query row, lanes over
-// the head dimension) with the same partial format, merged by the second kernel.
+// the head dimension) with the same partial format, merged by the merge kernel.
 
 #include <hip/hip_runtime.h>
 
@@ -643,8 +647,11 @@ __global__ __launch_bounds__(NW * kWave, 8 / NW) void attn_split_mfma(AttnArgs a
 // Per chunk c a wave runs an MFMA block M_c = {O += V_{c-1}^T P_{c-1}^T,
 // S_c = K_c Q^T} and a VALU block X_c = {softmax of S_c -> P_c}; the PV
 // product of a chunk is deferred into the next chunk's MFMA block.  The
-// work-group has one barrier per chunk, B_c (chunk c is in LDS; the tile of
-// chunk c-2 is free for the load of chunk c+2).  Waves 0-3 pass B_c right
+// work-group has one barrier per chunk, B_c: before it each wave waits for
+// its own copies of the tile it reads next (explicit vmcnt waits; the copies
+// are inline assembly, see lds_dma16), after it the copy of K chunk c+4 goes
+// into the tile K chunk c-1 used and the copy of V chunk c+3 into the tile V
+// chunk c-2 used.  Waves 0-3 pass B_c right
 // before M_c; waves 4-7 right before X_{c-1}, i.e. half a chunk earlier in
 // their own program.  Waves are placed on the four SIMDs in turn, so each
 // SIMD holds one wave of each group, and the barrier keeps them in opposite

@@ -20,10 +20,11 @@
 //                  fp64 across threads.
 //   sample_resid   grid (groups, B).  Every work-group of a sequence derives
 //                  the same decision (fp64 log-normalisers, one Philox uniform
-//                  and acceptance test per node, the walk from the root: a few
-//                  hundred scalars, two memory round trips), then the residual
-//                  (or target) mass of its 1024-id race chunks of the stop
-//                  row (the loads of four chunks in flight at once).  When the walk
+//                  and acceptance test per node, the walk from the root over
+//                  parents held in LDS: a few hundred scalars after one round
+//                  of loads), then the residual (or target) mass of its
+//                  1024-id race chunks of the stop row (non-temporal loads,
+//                  four chunks in flight at once).  When the walk
 //                  ends at a leaf whose target row the first kernel skipped,
 //                  the groups gather that row's per-chunk (max, sum) instead,
 //                  so a leaf row is read once, and only when it is drawn from.

@@ -690,14 +690,18 @@ constexpr float kRescaleTau = 8.0f;   // log2 units
 // kernel orders its tiles itself: an explicit vmcnt wait on this wave's own
 // copies, then a work-group barrier, before any wave reads a tile.  M0 holds
 // the (wave-uniform) LDS destination; one wait state separates its write from
-// the load that reads it.
+// the load that reads it.  M0 is a register the compiler reserves, so the
+// statement saves it and puts it back instead of declaring it clobbered.
 __device__ __forceinline__ void lds_dma16(const void* src, void* lds_base) {
   const uint32_t lds = __builtin_amdgcn_readfirstlane(
       (uint32_t)(uintptr_t)(__attribute__((address_space(3))) char*)lds_base);
-  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off"
-               :
-               : "v"(src), "s"(lds)
-               : "memory", "m0");
+  uint32_t saved;
+  asm volatile(
+      "s_mov_b32 %0, m0\n\ts_mov_b32 m0, %2\n\ts_nop 0\n\t"
+      "global_load_lds_dwordx4 %1, off\n\ts_mov_b32 m0, %0"
+      : "=&s"(saved)
+      : "v"(src), "s"(lds)
+      : "memory");
 }
 
 // Wait until at most n of this wave's vector-memory operations are pending

@@ -790,13 +790,18 @@ __device__ __forceinline__ void emit_bad(const SampleArgs& a, int b, int bad) {
 // After a rejection the weights are the residual masses; if they all vanish,
 // the target's (use_resid tells which).  The masses were stored by other
 // work-groups of this launch.  Returns the winning chunk.
-__device__ __forceinline__ int race_level1(const SampleArgs& a, int b, int r, bool residual, bool& use_resid) {
+__device__ __forceinline__ int race_level1(const SampleArgs& a, int b, int r, bool residual,
+                                           bool& use_resid, bool held = false,
+                                           double w_held = 0.0) {
   __shared__ double redd[4];
   __shared__ int redi[4];
   const int tid = threadIdx.x;
   const double* rw = a.race_w + (size_t)b * a.n_race * 2;
   double w_res = 0.0, w_tgt = 0.0;     // this thread's first chunk, q = tid
-  if (tid < a.n_race) {
+  if (held) {
+    // Target weights already in registers (one chunk per thread, no residual).
+    w_tgt = w_held;
+  } else if (tid < a.n_race) {
     w_res = load_coherent(rw + 2 * tid);
     w_tgt = load_coherent(rw + 2 * tid + 1);
   }
@@ -892,13 +897,14 @@ __device__ __forceinline__ void emit_outputs(const SampleArgs& a, int b, const S
 }
 
 template <typename T>
-__device__ void race_emit(const SampleArgs& a, int b, const StopView& sv) {
+__device__ void race_emit(const SampleArgs& a, int b, const StopView& sv, bool held = false,
+                          double w_held = 0.0) {
   if (sv.bad) {
     emit_bad(a, b, sv.bad);
     return;
   }
   bool use_resid = false;
-  const int cstar = race_level1(a, b, sv.r, sv.residual, use_resid);
+  const int cstar = race_level1(a, b, sv.r, sv.residual, use_resid, held, w_held);
   const int y = race_level2<T>(a, b, sv.r, cstar, use_resid, sv.lzt, sv.lzd, sv.shift);
   emit_outputs(a, b, sv, y);
 }
@@ -1057,31 +1063,45 @@ __global__ __launch_bounds__(kSampleThreads) void sample_resid(SampleArgs a) {
 
   // The group that completes the sequence's masses runs the draw.
   if (!last_of_group(a.arrive + (size_t)b * kArriveStride, grp, a.n_groups, a.dev_err)) return;
+  // With one race chunk per thread the leaf row's target masses stay in
+  // registers and go straight to the level-1 race.
+  const bool held = !row_stats && !bad && a.n_race <= kSampleThreads;
+  double w_held = 0.0;
   if (!row_stats && !bad) {
     // The stop row's log-normaliser from its race chunks' (max, sum), then
     // each chunk's target mass sum exp(x - lz) in place of the pair.
     __shared__ double redn[4];
     __shared__ float redm[4];
     double* rw = a.race_w + (size_t)b * a.n_race * 2;
-    float mx = -INFINITY;
-    for (int q = tid; q < a.n_race; q += kSampleThreads) mx = fmaxf(mx, (float)load_coherent(rw + 2 * q));
+    double m0 = -INFINITY, s0 = 0.0;   // this thread's first chunk, q = tid
+    if (tid < a.n_race) {
+      m0 = load_coherent(rw + 2 * tid);
+      s0 = load_coherent(rw + 2 * tid + 1);
+    }
+    float mx = (float)m0;
+    for (int q = tid + kSampleThreads; q < a.n_race; q += kSampleThreads)
+      mx = fmaxf(mx, (float)load_coherent(rw + 2 * q));
     mx = block_max(mx, redm);
     double sum = 0.0;
     if (mx != -INFINITY)
       for (int q = tid; q < a.n_race; q += kSampleThreads) {
-        const double mq = load_coherent(rw + 2 * q);
-        if (mq != -INFINITY) sum += load_coherent(rw + 2 * q + 1) * exp(mq - (double)mx);
+        const double mq = q == tid ? m0 : load_coherent(rw + 2 * q);
+        if (mq != -INFINITY) sum += (q == tid ? s0 : load_coherent(rw + 2 * q + 1)) * exp(mq - (double)mx);
       }
     sum = block_sum(sum, redn);
     lzt = (double)mx + log(sum);
-    for (int q = tid; q < a.n_race; q += kSampleThreads) {
-      const double mq = load_coherent(rw + 2 * q);
-      const double w = mq == -INFINITY ? 0.0 : load_coherent(rw + 2 * q + 1) * exp(mq - lzt);
-      store_coherent(rw + 2 * q, 0.0);
-      store_coherent(rw + 2 * q + 1, w);
+    if (held) {
+      w_held = m0 == -INFINITY ? 0.0 : s0 * exp(m0 - lzt);
+    } else {
+      for (int q = tid; q < a.n_race; q += kSampleThreads) {
+        const double mq = load_coherent(rw + 2 * q);
+        const double w = mq == -INFINITY ? 0.0 : load_coherent(rw + 2 * q + 1) * exp(mq - lzt);
+        store_coherent(rw + 2 * q, 0.0);
+        store_coherent(rw + 2 * q + 1, w);
+      }
+      __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0): the masses are stored
+      __syncthreads();
     }
-    __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0): the masses are stored
-    __syncthreads();
   }
   StopView sv;
   if constexpr (FROM_RECORD) {
@@ -1090,7 +1110,7 @@ __global__ __launch_bounds__(kSampleThreads) void sample_resid(SampleArgs a) {
   } else {
     sv = StopView{d.len, d.bad, r, residual, lzt, lzd, shiftd, nullptr, &d};
   }
-  race_emit<T>(a, b, sv);
+  race_emit<T>(a, b, sv, held, w_held);
 }
 
 

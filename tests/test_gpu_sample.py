@@ -88,6 +88,10 @@ CASES = [
     # draft = target: every draft accepted, every draw a bonus from a leaf
     # row whose statistics the residual pass gathers
     ("b32_chain_all_accepted_v50000", 32, 5, 50000, False, 3.0, 0.0, None),
+    # more race chunks than threads in a work-group (293): the draw reads the
+    # chunk masses back from memory instead of holding one per thread
+    ("b4_chain_all_accepted_v300000", 4, 3, 300000, False, 3.0, 0.0, None),
+    ("b4_chain_v300000", 4, 4, 300000, False, 3.0, 1.0, None),
 ]
 
 

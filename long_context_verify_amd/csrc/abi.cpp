@@ -481,6 +481,7 @@ spec_status_t spec_draft_sample(const void* draft_logits, spec_dtype_t dtype, in
   a.part_m = reinterpret_cast<float*>(ws + p.off_m);
   a.part_s = reinterpret_cast<double*>(ws + p.off_s);
   a.n_chunks = p.n_chunks;
+  a.chunk = p.chunk;
   a.logits_bf16 = dtype == SPEC_BF16 ? 1 : 0;
   a.dev_err = dev_err;
   // Vector loads (4 ids) when every row starts aligned and holds whole vectors.

@@ -58,7 +58,8 @@ constexpr int kSampleThreads = 256;
 constexpr int kDecideThreads = 512;    // lossless decide: one work-group streams the rows
 constexpr int kRaceChunk = 1024;
 constexpr int kStatsChunk = 8192;   // ids per stats work-group (32 per thread)
-constexpr int kDraftChunk = 2048;   // ids per draft-draw work-group (8 per thread)
+constexpr int kDraftChunkSmall = 2048;   // ids per draft-draw work-group (8 per thread)
+constexpr int kDraftChunkLarge = 4096;   // the same at large batch (16 per thread)
 constexpr int kArriveFan = 16;      // residual groups per first-level arrival counter
 constexpr int kArrivePad = 16;      // counters 64 bytes apart
 constexpr int kArriveStride = kArrivePad * (kArriveFan + 1);   // counters per sequence
@@ -1296,19 +1297,22 @@ __device__ void draft_finish_row(const DraftArgs& a, int b, float* redf, double*
   }
 }
 
-// grid (chunks of 2048 ids, B).  Thread t holds the id groups
-// g = chunk*512 + t + 256*i (i < 2), four consecutive ids per group, so one
-// Philox call serves one 16-byte load.  Small chunks give many work-groups:
-// the Philox rounds, not the bytes, set the time of a 0.5 MB row.
-template <bool VEC4, typename T>
+// grid (chunks of CH ids, B).  Thread t holds the id groups
+// g = chunk*CH/4 + t + 256*i (i < CH/1024), four consecutive ids per group,
+// so one Philox call serves one 16-byte load.  Small chunks give many
+// work-groups: the Philox rounds, not the bytes, set the time of a 0.5 MB
+// row.  At large batch there are work-groups enough either way, and chunks
+// twice as long spread each work-group's three block reductions over twice
+// the ids.
+template <bool VEC4, typename T, int CH>
 __global__ __launch_bounds__(kSampleThreads) void draft_partial(DraftArgs a) {
   __shared__ float redf[4];
   __shared__ double redd[4];
   __shared__ RaceBest redr[4];
   const int chunk = blockIdx.x, b = blockIdx.y;
   const T* row = static_cast<const T*>(a.logits) + (size_t)b * a.row_stride;
-  constexpr int GROUPS = kDraftChunk / 4 / kSampleThreads;  // 2
-  const int g0 = chunk * (kDraftChunk / 4) + threadIdx.x;
+  constexpr int GROUPS = CH / 4 / kSampleThreads;  // 2 or 4
+  const int g0 = chunk * (CH / 4) + threadIdx.x;
   float x[4 * GROUPS], lraw[4 * GROUPS];   // logit * log2(e), and the logit
 #pragma unroll
   for (int i = 0; i < GROUPS; ++i) {
@@ -1399,7 +1403,12 @@ __global__ __launch_bounds__(kSampleThreads) void draft_partial(DraftArgs a) {
 
 DraftPlan plan_draft(int32_t B, int32_t V) {
   DraftPlan p{};
-  p.n_chunks = (V + kDraftChunk - 1) / kDraftChunk;
+  // Long chunks once short ones would give more than eight work-groups per
+  // CU (at 64 x 128256: 23-25 against 28 us; at 8 x 128256 short chunks
+  // stay faster, 9.4-10.5 against 10.5-11 us).
+  const long long small = (long long)B * ((V + kDraftChunkSmall - 1) / kDraftChunkSmall);
+  p.chunk = small > 8 * 256 ? kDraftChunkLarge : kDraftChunkSmall;
+  p.n_chunks = (V + p.chunk - 1) / p.chunk;
   const size_t n = (size_t)B * p.n_chunks;
   p.off_best = align256((size_t)B * kArriveStride * sizeof(uint32_t));   // arrival counters first
   p.off_idx = align256(p.off_best + n * sizeof(double));
@@ -1410,19 +1419,29 @@ DraftPlan plan_draft(int32_t B, int32_t V) {
   return p;
 }
 
-hipError_t launch_draft(const DraftArgs& a, bool vec4, hipStream_t stream) {
+template <int CH>
+static void launch_draft_chunks(const DraftArgs& a, bool vec4, hipStream_t stream) {
   dim3 g1(a.n_chunks, a.B), blk(kSampleThreads);
   if (a.logits_bf16) {
     if (vec4)
-      hipLaunchKernelGGL((draft_partial<true, __bf16>), g1, blk, 0, stream, a);
+      hipLaunchKernelGGL((draft_partial<true, __bf16, CH>), g1, blk, 0, stream, a);
     else
-      hipLaunchKernelGGL((draft_partial<false, __bf16>), g1, blk, 0, stream, a);
+      hipLaunchKernelGGL((draft_partial<false, __bf16, CH>), g1, blk, 0, stream, a);
   } else {
     if (vec4)
-      hipLaunchKernelGGL((draft_partial<true, float>), g1, blk, 0, stream, a);
+      hipLaunchKernelGGL((draft_partial<true, float, CH>), g1, blk, 0, stream, a);
     else
-      hipLaunchKernelGGL((draft_partial<false, float>), g1, blk, 0, stream, a);
+      hipLaunchKernelGGL((draft_partial<false, float, CH>), g1, blk, 0, stream, a);
   }
+}
+
+hipError_t launch_draft(const DraftArgs& a, bool vec4, hipStream_t stream) {
+  if (a.chunk == kDraftChunkLarge)
+    launch_draft_chunks<kDraftChunkLarge>(a, vec4, stream);
+  else if (a.chunk == kDraftChunkSmall)
+    launch_draft_chunks<kDraftChunkSmall>(a, vec4, stream);
+  else
+    return hipErrorInvalidValue;
   return hipGetLastError();
 }
 

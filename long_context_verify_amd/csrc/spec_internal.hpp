@@ -160,12 +160,13 @@ struct DraftArgs {
   float* part_m;            // [B][n_chunks] max of logit * log2(e)
   double* part_s;           // [B][n_chunks] sum of exp2(x - max)
   int32_t n_chunks;
+  int32_t chunk;            // ids per work-group: 2048, or 4096 at large batch
   int32_t logits_bf16;
   int32_t* dev_err;
 };
 
 struct DraftPlan {
-  int32_t n_chunks;
+  int32_t n_chunks, chunk;
   size_t off_best, off_idx, off_x, off_m, off_s, bytes;
 };
 

@@ -45,12 +45,15 @@ CASES = [
     ("v128256_b64_sharp", 64, 128256, 8.0),
     ("v1_b4", 4, 1, 1.0),
     ("v8191_b32_ragged", 32, 8191, 2.0),
+    # large batch: 4096-id work-groups, a ragged last chunk, scalar loads
+    ("v100001_b48_scalar", 48, 100001, 3.0),
 ]
 
 
 @pytest.mark.parametrize("case", CASES + [
-    ("bf16_v128256_b8", 8, 128256, 3.0), ("bf16_v5001_scalar", 64, 5001, 3.0)],
-    ids=[c[0] for c in CASES] + ["bf16_v128256_b8", "bf16_v5001_scalar"])
+    ("bf16_v128256_b8", 8, 128256, 3.0), ("bf16_v5001_scalar", 64, 5001, 3.0),
+    ("bf16_v128256_b64", 64, 128256, 3.0)],
+    ids=[c[0] for c in CASES] + ["bf16_v128256_b8", "bf16_v5001_scalar", "bf16_v128256_b64"])
 def test_draft_sample_parity(case):
     import long_context_verify_amd as L
     name, B, V, std = case

@@ -47,6 +47,7 @@ CASES = [
     ("v8191_b32_ragged", 32, 8191, 2.0),
     # large batch: 4096-id work-groups, a ragged last chunk, scalar loads
     ("v100001_b48_scalar", 48, 100001, 3.0),
+    ("v32768_b160_whole_chunks", 160, 32768, 3.0),
 ]
 
 
